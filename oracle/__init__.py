@@ -1,0 +1,192 @@
+"""ctypes wrapper of the C oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE: only the tests, the package smoke check and the
+benchmark's CPU-baseline leg import this module.  The HIP library never does,
+and this module never imports the library.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "oracle.c")
+
+F16 = 0
+BF16 = 1
+
+GCC_FLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+             "-fPIC", "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+
+def build(verbose=False):
+    """Compile the oracle with gcc (no GPU code involved)."""
+    cmd = ["gcc", *GCC_FLAGS, _SRC, "-o", LIB_PATH + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    global _lib
+    _lib = None
+
+
+_lib = None
+
+_p = C.c_void_p
+_i64 = C.c_int64
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = C.CDLL(LIB_PATH)
+        sig = {
+            "oracle_num_threads": ([], C.c_int),
+            "oracle_f16_to_double": ([C.c_uint16], C.c_double),
+            "oracle_bf16_to_double": ([C.c_uint16], C.c_double),
+            "oracle_double_to_f16": ([C.c_double], C.c_uint16),
+            "oracle_double_to_bf16": ([C.c_double], C.c_uint16),
+            "oracle_round_array": ([_p, _p, _i64, C.c_int], None),
+            "oracle_w4a16": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p, _p], None),
+            "oracle_w4a16_points": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p, _p, _i64, _p], None),
+            "oracle_grouped": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, C.c_int, _p, _p], None),
+            "oracle_msd_amax": ([_p, _i64, _i64, _i64, _p], None),
+            "oracle_msd_layers": ([_p, _p, _i64, _i64, _i64, _p], None),
+            "oracle_msd_decompose_one": ([C.c_float, C.c_float, _p, _p], None),
+            "oracle_msd_yint": ([_p, _p, _i64, _i64, _i64, _i64, _p], None),
+            "oracle_msd": ([_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p], None),
+            "oracle_prepack": ([_p, _p, _i64, _i64, _i64, C.c_int], None),
+            "oracle_unpack": ([_p, _p, _i64, _i64, _i64, C.c_int], None),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be contiguous"
+    return a.ctypes.data
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def f16_to_double(bits: int) -> float:
+    return lib().oracle_f16_to_double(int(bits))
+
+
+def bf16_to_double(bits: int) -> float:
+    return lib().oracle_bf16_to_double(int(bits))
+
+
+def round_array(v: np.ndarray, dtype: int) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().oracle_round_array(_ptr(v), _ptr(out), v.size, dtype)
+    return out
+
+
+def w4a16(x, w, scale, zero, M, K, N, dtype, group=128):
+    """Return (y64 [M,N] float64, y [M,N] uint16 bits)."""
+    y64 = np.empty((M, N), dtype=np.float64)
+    y = np.empty((M, N), dtype=np.uint16)
+    lib().oracle_w4a16(_ptr(x), _ptr(w), _ptr(scale), _ptr(zero), M, K, N, group, dtype,
+                       _ptr(y64), _ptr(y))
+    return y64, y
+
+
+def w4a16_points(x, w, scale, zero, M, K, N, dtype, rows, cols, group=128):
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    out = np.empty(rows.shape[0], dtype=np.float64)
+    lib().oracle_w4a16_points(_ptr(x), _ptr(w), _ptr(scale), _ptr(zero), M, K, N, group, dtype,
+                              _ptr(rows), _ptr(cols), rows.shape[0], _ptr(out))
+    return out
+
+
+def grouped(x, offsets, w, scale, zero, E, R, K, N, dtype, group=128):
+    y64 = np.zeros((R, N), dtype=np.float64)
+    y = np.zeros((R, N), dtype=np.uint16)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    lib().oracle_grouped(_ptr(x), _ptr(offsets), _ptr(w), _ptr(scale), _ptr(zero), E, R, K, N,
+                         group, dtype, _ptr(y64), _ptr(y))
+    return y64, y
+
+
+def msd_amax(x, M, K, group=128):
+    out = np.empty((M, K // group), dtype=np.float32)
+    lib().oracle_msd_amax(_ptr(x), M, K, group, _ptr(out))
+    return out
+
+
+def msd_layers(x, amax, M, K, group=128):
+    out = np.empty((3, M, K), dtype=np.int8)
+    lib().oracle_msd_layers(_ptr(x), _ptr(np.ascontiguousarray(amax, np.float32)), M, K, group, _ptr(out))
+    return out
+
+
+def msd_decompose_one(a: float, amax: float):
+    out = np.zeros(3, dtype=np.int8)
+    t = np.zeros(3, dtype=np.float32)
+    lib().oracle_msd_decompose_one(float(np.float32(a)), float(np.float32(amax)), _ptr(out), _ptr(t))
+    return out, t
+
+
+def msd_yint(layers, w, M, K, N, group=128):
+    out = np.empty((K // group, 3, M, N), dtype=np.int32)
+    lib().oracle_msd_yint(_ptr(np.ascontiguousarray(layers, np.int8)), _ptr(w), M, K, N, group, _ptr(out))
+    return out
+
+
+def msd(x, w, scale, M, K, N, group=128, intermediates=False):
+    y64 = np.empty((M, N), dtype=np.float64)
+    y = np.empty((M, N), dtype=np.uint16)
+    amax = np.empty((M, K // group), dtype=np.float32) if intermediates else None
+    layers = np.empty((3, M, K), dtype=np.int8) if intermediates else None
+    lib().oracle_msd(_ptr(x), _ptr(w), _ptr(scale), M, K, N, group, _ptr(y64), _ptr(y),
+                     _ptr(amax), _ptr(layers))
+    if intermediates:
+        return y64, y, amax, layers
+    return y64, y
+
+
+def prepack(w, E, K, N, is_signed):
+    out = np.empty(E * K * N // 2, dtype=np.uint8)
+    lib().oracle_prepack(_ptr(np.ascontiguousarray(w, np.uint8)), _ptr(out), E, K, N, int(is_signed))
+    return out
+
+
+def unpack(packed, E, K, N, is_signed):
+    out = np.empty(E * K * N // 2, dtype=np.uint8)
+    lib().oracle_unpack(_ptr(np.ascontiguousarray(packed, np.uint8)), _ptr(out), E, K, N, int(is_signed))
+    return out
+
+
+def compare(y_bits, y_ref_bits, dtype):
+    """Tolerance check used across the suite: returns (max_ratio, rel_l1), where
+    max_ratio = max|y - y_ref| / max|y_ref| (bar 1e-2) and rel_l1 =
+    sum|y - y_ref| / sum|y_ref| (bar 2e-3); y_ref is the once-rounded oracle."""
+    if dtype == BF16:
+        conv = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        conv = lambda b: np.asarray(b, np.uint16).view(np.float16).astype(np.float64)
+    y = conv(y_bits)
+    r = conv(y_ref_bits)
+    d = np.abs(y - r)
+    mref = np.max(np.abs(r)) if r.size else 0.0
+    sref = np.sum(np.abs(r))
+    max_ratio = float(np.max(d) / mref) if r.size and mref > 0 else float(np.max(d) if d.size else 0.0)
+    rel_l1 = float(np.sum(d) / sref) if sref > 0 else float(np.sum(d))
+    return max_ratio, rel_l1

@@ -1,0 +1,393 @@
+/*
+ * oracle.c — CPU oracle for W4A16 (group 128) and MSD A16W4 PerGroup.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h).  Plain loops, fp64 for the dense
+ * definition, IEEE binary32 exactly as written for the MSD decomposition.
+ * Build with -O2 -ffp-contract=off and without -ffast-math so that every
+ * float operation rounds once, in program order (x86-64 SSE arithmetic).
+ *
+ * The dense/grouped result has a plain definition,
+ *     Y = X . dequant(W),   dequant(W)[k][n] = (q[k][n] - z[g][n]) * s[g][n],
+ * g = k / 128 (Humming article: group INT4 weights with a scale and optional
+ * zero point per group; the operator spec of the MSD page §4.2 / §4.3 fixes
+ * a (K/128, N) scale).  The oracle writes that definition out.
+ *
+ * MSD is an encoding, so its oracle follows the eleven steps of the
+ * WeightQuantBatchMatmulExperiment page, §4.1, in that page's order:
+ *   eq.1  A_max = rowMax(|A_group|)
+ *   eq.2-7 tmp1 = 7.49*A/A_max, A1 = round(tmp1), tmp2 = (tmp1-A1)*14.98,
+ *          A2 = round(tmp2), tmp3 = (tmp2-A2)*14.98, A3 = round(tmp3)
+ *   eq.8-9 Y_int = [A1;A2;A3] . Weight_group   (integer matmul)
+ *   eq.10  Y_group = ((Y1/7.49 + Y2/(7.49*14.98) + Y3/(7.49*14.98*14.98))*A_max)*scale_group
+ *   eq.11  Y = sum over groups of Y_group
+ * with the factors {7.49f, 14.98f, 14.98f} stored as fp32 constants (§4.1).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#include <assert.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------- */
+/* 16-bit float decoding (exact) and RNE encoding from fp64.                  */
+/* ------------------------------------------------------------------------- */
+
+double oracle_f16_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int exp = (h >> 10) & 0x1F;
+    int man = h & 0x3FF;
+    double v;
+    if (exp == 0)
+        v = ldexp((double)man, -24);                 /* subnormal: man * 2^-24 */
+    else if (exp == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + man), exp - 25);   /* (1.man) * 2^(exp-15) */
+    return sign ? -v : v;
+}
+
+double oracle_bf16_to_double(uint16_t b) {
+    int sign = (b >> 15) & 1;
+    int exp = (b >> 7) & 0xFF;
+    int man = b & 0x7F;
+    double v;
+    if (exp == 0)
+        v = ldexp((double)man, -133);                /* subnormal: man * 2^-133 */
+    else if (exp == 255)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + man), exp - 134);   /* (1.man) * 2^(exp-127) */
+    return sign ? -v : v;
+}
+
+/* Round |v| to a binary float with `mbits` explicit mantissa bits, exponent
+ * bias `bias`, `ebits` exponent bits, round-to-nearest-even (rint in the
+ * default rounding mode is RNE; the scalings by powers of two are exact). */
+static uint16_t encode_rne(double v, int mbits, int ebits, int bias) {
+    uint16_t sign = signbit(v) ? (uint16_t)(1u << (mbits + ebits)) : 0;
+    double a = fabs(v);
+    int emax_field = (1 << ebits) - 1;
+    uint16_t inf = (uint16_t)(sign | (emax_field << mbits));
+    if (isnan(v)) return (uint16_t)(inf | (1u << (mbits - 1)));
+    if (isinf(a)) return inf;
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);          /* a = f * 2^e, f in [0.5, 1): unbiased exponent e-1 */
+    int unb = e - 1;
+    int emin = 1 - bias;
+    if (unb < emin) {
+        /* subnormal range: quantum 2^(emin - mbits) */
+        double n = rint(ldexp(a, mbits - emin));
+        /* n == 2^mbits rounds up into the smallest normal: same bit pattern */
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    double n = rint(ldexp(a, mbits - unb));          /* in [2^mbits, 2^(mbits+1)] */
+    if (n >= ldexp(1.0, mbits + 1)) { n = ldexp(1.0, mbits); unb += 1; }
+    int field = unb + bias;
+    if (field >= emax_field) return inf;
+    return (uint16_t)(sign | (field << mbits) | ((uint16_t)n - (1u << mbits)));
+}
+
+uint16_t oracle_double_to_f16(double v) { return encode_rne(v, 10, 5, 15); }
+uint16_t oracle_double_to_bf16(double v) { return encode_rne(v, 7, 8, 127); }
+
+void oracle_round_array(const double *v, uint16_t *out, int64_t n, int dtype) {
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = dtype == ORACLE_BF16 ? oracle_double_to_bf16(v[i]) : oracle_double_to_f16(v[i]);
+}
+
+static double to_double(uint16_t bits, int dtype) {
+    return dtype == ORACLE_BF16 ? oracle_bf16_to_double(bits) : oracle_f16_to_double(bits);
+}
+
+/* ------------------------------------------------------------------------- */
+/* int4 decoding of the plain layout                                          */
+/* ------------------------------------------------------------------------- */
+
+/* 4-bit code of element (row, col) of a [rows][cols/2]-byte packed matrix. */
+static int nibble(const uint8_t *p, int64_t cols, int64_t row, int64_t col) {
+    uint8_t byte = p[row * (cols / 2) + col / 2];
+    return (col & 1) ? (byte >> 4) : (byte & 0xF);
+}
+
+/* Integer weight value: two's complement int4 when signed, else 0..15. */
+static int weight_int(const uint8_t *w, int64_t N, int64_t k, int64_t n, int is_signed) {
+    int c = nibble(w, N, k, n);
+    return is_signed ? (c >= 8 ? c - 16 : c) : c;
+}
+
+/* dequant(W)[k][n] = (q - z) * s, exact in fp64 (|q - z| < 2^5, s has at most
+ * 11 significant bits, so the product has at most 16 bits). */
+static double dequant(const uint8_t *w, const uint16_t *scale, const uint8_t *zero,
+                      int64_t N, int64_t group, int dtype, int64_t k, int64_t n) {
+    int64_t g = k / group;
+    int is_signed = zero == NULL;
+    int q = weight_int(w, N, k, n, is_signed);
+    int z = zero ? nibble(zero, N, g, n) : 0;
+    return (double)(q - z) * to_double(scale[g * N + n], dtype);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Dense W4A16                                                                */
+/* ------------------------------------------------------------------------- */
+
+void oracle_w4a16(const uint16_t *x, const uint8_t *w, const uint16_t *scale,
+                  const uint8_t *zero, int64_t M, int64_t K, int64_t N,
+                  int64_t group, int dtype, double *y64, uint16_t *y) {
+    if (M <= 0) return;
+    /* Step 1: dequant(W) materialised in fp64 (exact). */
+    double *wd = (double *)malloc(sizeof(double) * (size_t)K * (size_t)N);
+    assert(wd);
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            wd[k * N + n] = dequant(w, scale, zero, N, group, dtype, k, n);
+
+    double *acc = y64 ? y64 : (double *)malloc(sizeof(double) * (size_t)M * (size_t)N);
+    assert(acc);
+    /* Step 2: acc[m][n] = sum_k x[m][k] * wd[k][n], each sum taken in
+     * ascending k (the loops over n only run independent sums side by side). */
+    const int64_t NC = 512;
+    int64_t nchunks = (N + NC - 1) / NC;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t c = 0; c < nchunks; ++c) {
+            int64_t n0 = c * NC, n1 = n0 + NC < N ? n0 + NC : N;
+            double *row = acc + m * N;
+            for (int64_t n = n0; n < n1; ++n) row[n] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double xv = to_double(x[m * K + k], dtype);
+                const double *wr = wd + k * N;
+                for (int64_t n = n0; n < n1; ++n) row[n] += xv * wr[n];
+            }
+        }
+    }
+    /* Step 3: one rounding to the output dtype. */
+    if (y) oracle_round_array(acc, y, M * N, dtype);
+    if (!y64) free(acc);
+    free(wd);
+}
+
+void oracle_w4a16_points(const uint16_t *x, const uint8_t *w, const uint16_t *scale,
+                         const uint8_t *zero, int64_t M, int64_t K, int64_t N,
+                         int64_t group, int dtype, const int64_t *rows,
+                         const int64_t *cols, int64_t P, double *out) {
+    (void)M;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t m = rows[p], n = cols[p];
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += to_double(x[m * K + k], dtype) * dequant(w, scale, zero, N, group, dtype, k, n);
+        out[p] = s;
+    }
+}
+
+void oracle_grouped(const uint16_t *x, const int32_t *offsets, const uint8_t *w,
+                    const uint16_t *scale, const uint8_t *zero, int64_t E, int64_t R,
+                    int64_t K, int64_t N, int64_t group, int dtype,
+                    double *y64, uint16_t *y) {
+    int64_t G = K / group;
+    (void)R;
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t r0 = offsets[e], r1 = offsets[e + 1];
+        if (r1 <= r0) continue;   /* expert without rows: nothing to compute */
+        oracle_w4a16(x + r0 * K, w + e * K * (N / 2), scale + e * G * N,
+                     zero ? zero + e * G * (N / 2) : NULL, r1 - r0, K, N, group, dtype,
+                     y64 ? y64 + r0 * N : NULL, y ? y + r0 * N : NULL);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* MSD (multi-step decomposition), step by step                               */
+/* ------------------------------------------------------------------------- */
+
+static const float MSD_F1 = 7.49f;    /* first factor  (fp32 constant) */
+static const float MSD_F2 = 14.98f;   /* second/third factor            */
+
+void oracle_msd_amax(const uint16_t *x, int64_t M, int64_t K, int64_t group, float *amax) {
+    int64_t G = K / group;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t g = 0; g < G; ++g) {
+            float mx = 0.0f;
+            for (int64_t k = g * group; k < (g + 1) * group; ++k) {
+                float a = fabsf((float)oracle_f16_to_double(x[m * K + k]));  /* exact */
+                if (a > mx) mx = a;
+            }
+            amax[m * G + g] = mx;   /* eq.1: rowMax(|A_group|), per row and group */
+        }
+}
+
+/* eqs.2-7 for one element.  Each line is one binary32 operation, rounded to
+ * nearest even; round() is round-half-to-even (rintf).  An all-zero group
+ * (amax == 0) has all three layers 0. */
+void oracle_msd_decompose_one(float a, float amax, int8_t out[3], float t_out[3]) {
+    if (amax == 0.0f) {
+        out[0] = out[1] = out[2] = 0;
+        if (t_out) t_out[0] = t_out[1] = t_out[2] = 0.0f;
+        return;
+    }
+    float p = MSD_F1 * a;          /* 7.49 * A            */
+    float t1 = p / amax;           /* tmp1 = 7.49*A/A_max  (eq.2) */
+    float a1 = rintf(t1);          /* A1 = round(tmp1)     (eq.3) */
+    float d1 = t1 - a1;
+    float t2 = d1 * MSD_F2;        /* tmp2 = (tmp1-A1)*14.98 (eq.4) */
+    float a2 = rintf(t2);          /* A2 = round(tmp2)     (eq.5) */
+    float d2 = t2 - a2;
+    float t3 = d2 * MSD_F2;        /* tmp3 = (tmp2-A2)*14.98 (eq.6) */
+    float a3 = rintf(t3);          /* A3 = round(tmp3)     (eq.7) */
+    out[0] = (int8_t)a1;
+    out[1] = (int8_t)a2;
+    out[2] = (int8_t)a3;
+    if (t_out) { t_out[0] = t1; t_out[1] = t2; t_out[2] = t3; }
+}
+
+void oracle_msd_layers(const uint16_t *x, const float *amax, int64_t M, int64_t K,
+                       int64_t group, int8_t *layers) {
+    int64_t G = K / group;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            int8_t l[3];
+            float a = (float)oracle_f16_to_double(x[m * K + k]);
+            oracle_msd_decompose_one(a, amax[m * G + k / group], l, NULL);
+            for (int j = 0; j < 3; ++j) layers[(j * M + m) * K + k] = l[j];  /* eq.8: [A1;A2;A3] */
+        }
+}
+
+void oracle_msd_yint(const int8_t *layers, const uint8_t *w, int64_t M, int64_t K,
+                     int64_t N, int64_t group, int32_t *yint) {
+    int64_t G = K / group;
+    /* eq.9: Y_int = A_int . Weight_group, one integer product per group. */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t g = 0; g < G; ++g)
+        for (int64_t m = 0; m < M; ++m)
+            for (int j = 0; j < 3; ++j)
+                for (int64_t n = 0; n < N; ++n) {
+                    int64_t s = 0;
+                    for (int64_t k = g * group; k < (g + 1) * group; ++k)
+                        s += (int64_t)layers[(j * M + m) * K + k] * weight_int(w, N, k, n, 1);
+                    assert(s >= INT32_MIN && s <= INT32_MAX);
+                    yint[((g * 3 + j) * M + m) * N + n] = (int32_t)s;
+                }
+}
+
+void oracle_msd(const uint16_t *x, const uint8_t *w, const uint16_t *scale, int64_t M,
+                int64_t K, int64_t N, int64_t group, double *y64, uint16_t *y,
+                float *amax_out, int8_t *layers_out) {
+    if (M <= 0) return;
+    int64_t G = K / group;
+    float *amax = (float *)malloc(sizeof(float) * (size_t)(M * G));
+    int8_t *layers = (int8_t *)malloc((size_t)(3 * M * K));
+    int8_t *q = (int8_t *)malloc((size_t)(K * N));
+    double *acc = y64 ? y64 : (double *)malloc(sizeof(double) * (size_t)(M * N));
+    assert(amax && layers && q && acc);
+
+    oracle_msd_amax(x, M, K, group, amax);            /* eq.1   */
+    oracle_msd_layers(x, amax, M, K, group, layers);  /* eqs.2-8 */
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) q[k * N + n] = (int8_t)weight_int(w, N, k, n, 1);
+
+    const double c1 = (double)MSD_F1, c2 = (double)MSD_F2;
+#pragma omp parallel
+    {
+        int64_t *Y = (int64_t *)malloc(sizeof(int64_t) * (size_t)(3 * N));
+#pragma omp for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            double *row = acc + m * N;
+            for (int64_t n = 0; n < N; ++n) row[n] = 0.0;
+            for (int64_t g = 0; g < G; ++g) {
+                /* eq.9 for this (row, group): three integer dot products per column */
+                memset(Y, 0, sizeof(int64_t) * (size_t)(3 * N));
+                for (int j = 0; j < 3; ++j)
+                    for (int64_t k = g * group; k < (g + 1) * group; ++k) {
+                        int64_t a = layers[(j * M + m) * K + k];
+                        if (a == 0) continue;
+                        const int8_t *qr = q + k * N;
+                        int64_t *Yj = Y + j * N;
+                        for (int64_t n = 0; n < N; ++n) Yj[n] += a * (int64_t)qr[n];
+                    }
+                /* eq.10 (merge, fp64) and eq.11 (accumulate over groups) */
+                double am = (double)amax[m * G + g];
+                for (int64_t n = 0; n < N; ++n) {
+                    double yg = ((double)Y[n] / c1 + (double)Y[N + n] / (c1 * c2) +
+                                 (double)Y[2 * N + n] / (c1 * c2 * c2)) * am;
+                    row[n] += yg * oracle_f16_to_double(scale[g * N + n]);
+                }
+            }
+        }
+        free(Y);
+    }
+    if (y) oracle_round_array(acc, y, M * N, ORACLE_F16);
+    if (amax_out) memcpy(amax_out, amax, sizeof(float) * (size_t)(M * G));
+    if (layers_out) memcpy(layers_out, layers, (size_t)(3 * M * K));
+    if (!y64) free(acc);
+    free(q);
+    free(layers);
+    free(amax);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Prepacked layout (the library's own format)                                */
+/* ------------------------------------------------------------------------- */
+/*
+ * The packed buffer is a sequence of 1024-byte tiles, one per (expert e,
+ * column block nb of 16 columns, K-group g of 128 rows), ordered e, nb, g.
+ * Inside a tile, 16-byte slot L (0..63) holds column n = 16*nb + (L % 16) for
+ * the 32 rows k = 128*g + 32*(L / 16) + r, r = 0..31.  Slot word t (0..3,
+ * little-endian uint32 at byte 4t of the slot) holds r = 8t + i, i = 0..7, with
+ * the 4-bit code of row r at bit 4*(i / 2) + 16*(i % 2).  The code is the
+ * unsigned value u (unsigned weights) or q + 8 (signed weights q in [-8, 7]).
+ */
+static int64_t packed_bit_index(int64_t K, int64_t N, int64_t e, int64_t k, int64_t n) {
+    int64_t G = K / 128, NB = N / 16;
+    int64_t nb = n / 16, j = n % 16, g = k / 128, kk = k % 128;
+    int64_t c = kk / 32, r = kk % 32, t = r / 8, i = r % 8;
+    int64_t tile = (e * NB + nb) * G + g;
+    int64_t slot = c * 16 + j;
+    int64_t byte = tile * 1024 + slot * 16 + t * 4;
+    int64_t bit = 4 * (i / 2) + 16 * (i % 2);
+    return byte * 8 + bit;      /* bit offset inside a little-endian word */
+}
+
+void oracle_prepack(const uint8_t *w, uint8_t *packed, int64_t E, int64_t K, int64_t N, int is_signed) {
+    memset(packed, 0, (size_t)(E * K * N / 2));
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t k = 0; k < K; ++k)
+            for (int64_t n = 0; n < N; ++n) {
+                int code = nibble(w + e * K * (N / 2), N, k, n);
+                if (is_signed) code ^= 0x8;   /* (q + 8) mod 16 for two's complement q */
+                int64_t b = packed_bit_index(K, N, e, k, n);
+                /* word-relative bit b%32 of the word at byte (b/32)*4: little endian */
+                int64_t word_byte = (b / 32) * 4;
+                int64_t wb = b % 32;
+                packed[word_byte + wb / 8] |= (uint8_t)(code << (wb % 8));
+            }
+}
+
+void oracle_unpack(const uint8_t *packed, uint8_t *w, int64_t E, int64_t K, int64_t N, int is_signed) {
+    memset(w, 0, (size_t)(E * K * N / 2));
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t k = 0; k < K; ++k)
+            for (int64_t n = 0; n < N; ++n) {
+                int64_t b = packed_bit_index(K, N, e, k, n);
+                int64_t word_byte = (b / 32) * 4;
+                int64_t wb = b % 32;
+                int code = (packed[word_byte + wb / 8] >> (wb % 8)) & 0xF;
+                if (is_signed) code ^= 0x8;
+                uint8_t *dst = w + e * K * (N / 2) + k * (N / 2) + n / 2;
+                *dst |= (uint8_t)((n & 1) ? (code << 4) : code);
+            }
+}

@@ -1,0 +1,87 @@
+/*
+ * oracle.h — CPU oracle for the weight-only quantized matmul (W4A16, group
+ * 128) and its MSD (multi-step decomposition) variant.
+ *
+ * TEST INFRASTRUCTURE.  This is a plain, slow, obviously-correct host
+ * implementation used only to check the HIP library.  Only the test suite,
+ * the package smoke check and the benchmark's CPU-baseline leg may load or
+ * call it.  It shares no code, header, table or helper with the HIP library:
+ * both sides only consume the same seeded input bytes.
+ *
+ * All pointers are HOST pointers.  Layouts are the plain user layouts:
+ *   x      [M][K]      16-bit patterns (fp16 or bf16), row-major
+ *   w      [K][N/2]    int4, two per byte along N, low nibble = even n;
+ *                       signed two's complement when zero == NULL,
+ *                       unsigned 0..15 otherwise
+ *   scale  [G][N]      16-bit patterns, same dtype as x, G = K/group
+ *   zero   [G][N/2]    unsigned int4 packed like w (nullable)
+ *   y      [M][N]      16-bit patterns, same dtype as x
+ *
+ * Sources (cited by page title and section):
+ *  - "WeightQuantBatchMatmulExperiment operator deep-dive: MSD algorithm for
+ *    A16W4 PerGroup pseudo-quant MatMul" (CANN ops-nn sample), §4.1 eqs. 1-11
+ *    (MSD), §4.2 (operator spec: fp16 x / int4 weight / fp16 antiquant_scale ->
+ *    fp16 y), §4.3 (two int4 per byte, scale shape (K/128, N)).
+ *  - "Humming: open-source library for quantized inference" (vLLM / Ant
+ *    Group article), section on the standard quantization descriptor
+ *    (group INT4 weights, scale granularity, zero points).
+ */
+#ifndef W4A16_ORACLE_H
+#define W4A16_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORACLE_F16 = 0, ORACLE_BF16 = 1 };
+
+int oracle_num_threads(void);
+
+/* Exact decoding of 16-bit float patterns and round-to-nearest-even encoding. */
+double   oracle_f16_to_double(uint16_t h);
+double   oracle_bf16_to_double(uint16_t b);
+uint16_t oracle_double_to_f16(double v);
+uint16_t oracle_double_to_bf16(double v);
+void     oracle_round_array(const double *v, uint16_t *out, int64_t n, int dtype);
+
+/* Dense: y64[m][n] = sum_k x[m][k] * (q[k][n] - z[g(k)][n]) * s[g(k)][n]  (fp64),
+ * y = RNE(y64) in the dtype of x.  y64 or y may be NULL. */
+void oracle_w4a16(const uint16_t *x, const uint8_t *w, const uint16_t *scale,
+                  const uint8_t *zero, int64_t M, int64_t K, int64_t N,
+                  int64_t group, int dtype, double *y64, uint16_t *y);
+
+/* Same definition evaluated only at P points (rows[p], cols[p]); fp64 out. */
+void oracle_w4a16_points(const uint16_t *x, const uint8_t *w, const uint16_t *scale,
+                         const uint8_t *zero, int64_t M, int64_t K, int64_t N,
+                         int64_t group, int dtype, const int64_t *rows,
+                         const int64_t *cols, int64_t P, double *out);
+
+/* Grouped (MoE): rows offsets[e]..offsets[e+1] of x use expert e's weights
+ * w + e*K*N/2, scale + e*G*N, zero + e*G*N/2. */
+void oracle_grouped(const uint16_t *x, const int32_t *offsets, const uint8_t *w,
+                    const uint16_t *scale, const uint8_t *zero, int64_t E, int64_t R,
+                    int64_t K, int64_t N, int64_t group, int dtype,
+                    double *y64, uint16_t *y);
+
+/* MSD, step by step.  x, scale are fp16; weights signed int4. */
+void oracle_msd_amax(const uint16_t *x, int64_t M, int64_t K, int64_t group, float *amax /*[M][G]*/);
+void oracle_msd_layers(const uint16_t *x, const float *amax, int64_t M, int64_t K,
+                       int64_t group, int8_t *layers /*[3][M][K]*/);
+void oracle_msd_decompose_one(float a, float amax, int8_t out[3], float t_out[3]);
+void oracle_msd_yint(const int8_t *layers, const uint8_t *w, int64_t M, int64_t K,
+                     int64_t N, int64_t group, int32_t *yint /*[G][3][M][N]*/);
+void oracle_msd(const uint16_t *x, const uint8_t *w, const uint16_t *scale, int64_t M,
+                int64_t K, int64_t N, int64_t group, double *y64, uint16_t *y,
+                float *amax_out /*nullable [M][G]*/, int8_t *layers_out /*nullable [3][M][K]*/);
+
+/* Reference of the prepacked weight layout (the library's own format, stated
+ * in words in the design notes) and its inverse.  w/out sizes E*K*N/2. */
+void oracle_prepack(const uint8_t *w, uint8_t *packed, int64_t E, int64_t K, int64_t N, int is_signed);
+void oracle_unpack(const uint8_t *packed, uint8_t *w, int64_t E, int64_t K, int64_t N, int is_signed);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

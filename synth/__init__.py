@@ -1,0 +1,243 @@
+"""Seeded synthetic inputs for the weight-only quantized matmul workloads.
+
+This module only *produces* input tensors (activations, packed int4 weights,
+scales, zero points, MoE routing).  It contains none of the method's
+arithmetic: no dequantisation, no matmul, no MSD decomposition.  Both the CPU
+oracle (``oracle/``) and the HIP path (``weight_only_quantized_amd``) consume
+exactly the bytes produced here, so the two sides never share computation.
+
+Storage conventions (the plain, user-facing layout; the pages only say "two
+int4 per byte", see the WeightQuantBatchMatmulExperiment operator deep-dive,
+§4.3):
+
+* activations ``x``: ``[M][K]`` raw 16-bit patterns (``np.uint16``) of fp16 or
+  bf16 values, row-major;
+* weights ``w``: ``[K][N/2]`` bytes (``[E][K][N/2]`` for grouped), element
+  ``(k, n)`` in byte ``k*N/2 + n//2``, low nibble for even ``n``;
+  signed weights are 4-bit two's complement in [-8, 7], unsigned ones are
+  plain [0, 15];
+* scales: ``[G][N]`` (``[E][G][N]``) raw 16-bit patterns, same dtype as ``x``;
+* zero points: ``[G][N/2]`` bytes packed like ``w`` (unsigned 4-bit).
+
+Random streams: one ``numpy`` PCG64 generator per (seed, tensor tag), so each
+tensor is reproducible on its own.  Normal draws are made in fp64, rounded once
+to fp32 and then once, round-to-nearest-even, to the 16-bit type.
+"""
+from __future__ import annotations
+
+import dataclasses
+import zlib
+from typing import Optional
+
+import numpy as np
+
+F16 = 0
+BF16 = 1
+GROUP = 128
+
+_TAGS = ("x", "w", "s", "z", "mask", "route", "tokens")
+
+
+def stream(seed: int, tag: str) -> np.random.Generator:
+    """Independent generator for one tensor tag."""
+    return np.random.Generator(np.random.PCG64([int(seed), zlib.crc32(tag.encode())]))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (round-to-nearest-even), return raw bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b = a.view(np.uint32).astype(np.uint64)
+    r = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def f32_to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to fp16 (numpy's conversion is round-to-nearest-even)."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def to_bits(a: np.ndarray, dtype: int) -> np.ndarray:
+    return f32_to_bf16_bits(a) if dtype == BF16 else f32_to_f16_bits(a)
+
+
+def bits_to_f32(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """Exact widening of 16-bit patterns to fp32 (for test diagnostics)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    if dtype == BF16:
+        return (bits.astype(np.uint32) << 16).view(np.float32)
+    return bits.view(np.float16).astype(np.float32)
+
+
+def pack_nibbles(vals: np.ndarray) -> np.ndarray:
+    """Pack a [..., N] array of 4-bit codes (0..15) two per byte along the last
+    axis, low nibble = even index."""
+    v = np.ascontiguousarray(vals, dtype=np.uint8) & 0xF
+    assert v.shape[-1] % 2 == 0
+    return (v[..., 0::2] | (v[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`pack_nibbles` (4-bit codes, unsigned)."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+@dataclasses.dataclass
+class Problem:
+    """One W4A16 (or MSD) problem instance in the plain storage layout."""
+    x: np.ndarray                 # uint16 [M][K] (or [R][K] for grouped)
+    w: np.ndarray                 # uint8 [K][N/2] or [E][K][N/2]
+    scale: np.ndarray             # uint16 [G][N] or [E][G][N]
+    zero: Optional[np.ndarray]    # uint8 [G][N/2] or [E][G][N/2], or None
+    q: np.ndarray                 # int8 integer weight values, [K][N] / [E][K][N]
+    M: int
+    K: int
+    N: int
+    dtype: int
+    E: int = 1
+    offsets: Optional[np.ndarray] = None   # int32 [E+1] for grouped
+    name: str = ""
+
+    @property
+    def signed(self) -> bool:
+        return self.zero is None
+
+    @property
+    def G(self) -> int:
+        return self.K // GROUP
+
+
+def _normal(g: np.random.Generator, shape) -> np.ndarray:
+    return g.standard_normal(shape, dtype=np.float64).astype(np.float32)
+
+
+def _weights(seed, shape_kn, signed, tag="w"):
+    g = stream(seed, tag)
+    if signed:
+        q = g.integers(-8, 8, size=shape_kn, dtype=np.int8)
+    else:
+        q = g.integers(0, 16, size=shape_kn, dtype=np.int8)
+    return q, pack_nibbles(q.view(np.uint8) & 0xF)
+
+
+def _scales(seed, shape, lo, hi, dtype, tag="s"):
+    g = stream(seed, tag)
+    s = (lo + (hi - lo) * g.random(shape, dtype=np.float64)).astype(np.float32)
+    return to_bits(s, dtype)
+
+
+def make_dense(M, K, N, dtype, signed=True, scale_range=(0.002, 0.01),
+               zero_range=(6, 9), seed=0, outlier_frac=0.0, outlier_mult=20.0,
+               x_scale=1.0, name="") -> Problem:
+    """Dense W4A16 problem: x ~ N(0,1) (optionally with outliers), W int4,
+    scale uniform, zero points uniform integers (unsigned weights only)."""
+    assert K % GROUP == 0 and N % 2 == 0
+    G = K // GROUP
+    x = _normal(stream(seed, "x"), (M, K)) * np.float32(x_scale)
+    if outlier_frac > 0:
+        mask = stream(seed, "mask").random((M, K)) < outlier_frac
+        x = np.where(mask, x * np.float32(outlier_mult), x).astype(np.float32)
+    xb = to_bits(x, dtype)
+    q, w = _weights(seed, (K, N), signed)
+    s = _scales(seed, (G, N), scale_range[0], scale_range[1], dtype)
+    z = None
+    if not signed:
+        zq = stream(seed, "z").integers(zero_range[0], zero_range[1] + 1, size=(G, N), dtype=np.int8)
+        z = pack_nibbles(zq.view(np.uint8))
+    return Problem(x=xb, w=w, scale=s, zero=z, q=q, M=M, K=K, N=N, dtype=dtype, name=name)
+
+
+def zipf_routing(tokens, experts, topk, alpha, seed):
+    """Per-token top-k expert choice: ``topk`` distinct experts drawn without
+    replacement from a Zipf(alpha) law truncated to ``experts`` ranks,
+    P(e) proportional to (e+1)^-alpha.  Returns int array [tokens, topk]."""
+    p = (np.arange(1, experts + 1, dtype=np.float64)) ** (-alpha)
+    p /= p.sum()
+    g = stream(seed, "route")
+    out = np.empty((tokens, topk), dtype=np.int64)
+    for t in range(tokens):
+        out[t] = g.choice(experts, size=topk, replace=False, p=p)
+    return out
+
+
+def make_grouped(E, tokens, topk, K, N, dtype, alpha=1.1, signed=True,
+                 scale_range=(0.002, 0.01), seed=0, name="",
+                 counts: Optional[np.ndarray] = None) -> Problem:
+    """MoE grouped problem.  Rows of ``x`` are token activations gathered and
+    sorted by (expert, token); ``offsets[e]..offsets[e+1]`` are expert e's rows.
+    If ``counts`` is given it overrides the routing draw (rows per expert)."""
+    G = K // GROUP
+    if counts is None:
+        route = zipf_routing(tokens, E, topk, alpha, seed)
+        pairs = sorted((int(e), t) for t in range(tokens) for e in route[t])
+        tok_of_row = np.array([t for _, t in pairs], dtype=np.int64)
+        counts = np.bincount(np.array([e for e, _ in pairs]), minlength=E)
+    else:
+        counts = np.asarray(counts, dtype=np.int64)
+        tok_of_row = np.concatenate([np.arange(c) % max(tokens, 1) for c in counts]).astype(np.int64) \
+            if counts.sum() else np.zeros(0, np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    R = int(offsets[-1])
+    xt = _normal(stream(seed, "tokens"), (max(tokens, 1), K))
+    x = xt[tok_of_row] if R else np.zeros((0, K), np.float32)
+    xb = to_bits(x, dtype)
+    q, w = _weights(seed, (E, K, N), signed)
+    s = _scales(seed, (E, G, N), scale_range[0], scale_range[1], dtype)
+    z = None
+    if not signed:
+        zq = stream(seed, "z").integers(6, 10, size=(E, G, N), dtype=np.int8)
+        z = pack_nibbles(zq.view(np.uint8))
+    return Problem(x=xb, w=w, scale=s, zero=z, q=q, M=R, K=K, N=N, dtype=dtype,
+                   E=E, offsets=offsets, name=name)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads (shapes and distributions of the benchmark configurations)
+# ---------------------------------------------------------------------------
+
+def tiny(seed=0) -> Problem:
+    """M=4, K=256, N=256; x fp16 N(0,1); signed int4; scale fp16 U[0.005,0.02]."""
+    return make_dense(4, 256, 256, F16, signed=True, scale_range=(0.005, 0.02), seed=seed, name="tiny")
+
+
+def decode(M, seed=0, N=14336, K=4096) -> Problem:
+    """Decode: K=4096, N=14336; x bf16 N(0,1); unsigned int4 with per-group
+    uint4 zero points U{6..9}; scale bf16 U[0.002,0.01]."""
+    return make_dense(M, K, N, BF16, signed=False, scale_range=(0.002, 0.01),
+                      zero_range=(6, 9), seed=seed, name=f"decode_m{M}")
+
+
+def prefill(seed=0, M=4096, K=4096, N=4096) -> Problem:
+    """Prefill: M=N=K=4096; x bf16 N(0,1); signed int4; scale bf16 U[0.002,0.01]."""
+    return make_dense(M, K, N, BF16, signed=True, scale_range=(0.002, 0.01), seed=seed, name="prefill")
+
+
+def msd(seed=0, M=64, K=8192, N=8192) -> Problem:
+    """MSD A16W4: M=64, K=N=8192; x fp16 N(0,1) with 1% of entries x20;
+    signed int4; antiquant_scale fp16 U[0.005,0.02]."""
+    return make_dense(M, K, N, F16, signed=True, scale_range=(0.005, 0.02), seed=seed,
+                      outlier_frac=0.01, outlier_mult=20.0, name="msd")
+
+
+def msd_page_example(seed=0) -> Problem:
+    """The MSD page's own example shape (M=1, N=12288, K=8192): x U[-3,3],
+    weights in [-7,7], scale U[-3,3] (WeightQuantBatchMatmulExperiment
+    operator deep-dive, §4.3)."""
+    M, K, N = 1, 8192, 12288
+    G = K // GROUP
+    x = (-3 + 6 * stream(seed, "x").random((M, K))).astype(np.float32)
+    q = stream(seed, "w").integers(-7, 8, size=(K, N), dtype=np.int8)
+    s = (-3 + 6 * stream(seed, "s").random((G, N))).astype(np.float32)
+    return Problem(x=to_bits(x, F16), w=pack_nibbles(q.view(np.uint8) & 0xF),
+                   scale=to_bits(s, F16), zero=None, q=q, M=M, K=K, N=N, dtype=F16,
+                   name="msd_page")
+
+
+def moe(seed=0) -> Problem:
+    """MoE grouped: 64 experts, 512 tokens, top-8 Zipf(1.1) routing,
+    K=2048, N=1408; x bf16 N(0,1); signed int4; scale bf16 U[0.002,0.01]."""
+    return make_grouped(64, 512, 8, 2048, 1408, BF16, alpha=1.1, signed=True, seed=seed, name="moe")

@@ -1,0 +1,148 @@
+/*
+ * w4a16.h — libw4a16: weight-only quantized matrix multiply on AMD Instinct
+ * MI355X (gfx950, CDNA4).  Plain C ABI: device pointers, sizes, a stream.
+ *
+ * Computes Y = X . dequant(W) with
+ *   X     fp16 or bf16 activations,
+ *   W     int4 weights, one scale (same dtype as X) and optionally one uint4
+ *         zero point per group of 128 consecutive K rows and per column,
+ *   dequant(W)[k][n] = (q[k][n] - z[k/128][n]) * s[k/128][n],
+ *   fp32 accumulation, Y rounded to the dtype of X.
+ * Sources: "Humming: open-source library for quantized inference" (vLLM /
+ * Ant Group article), section on the standard quantization descriptor (group
+ * INT4 weights with BF16 activations, scale granularity, zero points);
+ * "WeightQuantBatchMatmulExperiment operator deep-dive: MSD algorithm for
+ * A16W4 PerGroup pseudo-quant MatMul" (CANN ops-nn sample), §4.2 operator
+ * spec and §4.3 data layout (two int4 per byte, scale shape (K/128, N)).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller, row-major,
+ *    on the current HIP device.  `stream` is a hipStream_t (NULL = the
+ *    default stream).  Work is enqueued asynchronously; no call synchronizes
+ *    or allocates device memory.
+ *  - Plain weight layout: w[E][K][N/2] bytes; element (k, n) is nibble
+ *    (n & 1) of byte k*N/2 + n/2 (low nibble = even n).
+ *  - Signedness: when `zero` is NULL the weights are signed two's-complement
+ *    int4 in [-8, 7] and MUST have been prepacked with is_signed = 1; when
+ *    `zero` is given the weights are unsigned in [0, 15] (prepacked with
+ *    is_signed = 0) and zero[G][N/2] holds uint4 zero points packed like w.
+ *  - Shape rules: K > 0, K % 128 == 0, N > 0, N % 64 == 0, M (or R) >= 0,
+ *    E >= 1, group_size == 128.  M == 0 (or an expert without rows) is a
+ *    no-op that returns W4A16_OK.
+ *  - Alignment: x, w_packed, workspace 16 bytes; scale, y 2 bytes.
+ *  - Errors: every argument is checked on the host before anything is
+ *    enqueued; on error nothing is launched and y is untouched.  A launch
+ *    failure reported by the runtime maps to W4A16_ERR_DEVICE, as does a
+ *    current device that is not gfx950.  Faults inside a kernel surface, as
+ *    usual in HIP, at the caller's next synchronization.
+ *  - Thread safety: calls are stateless apart from a per-device property
+ *    cache filled once; concurrent calls on different streams are safe.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_NULL = 1,         /* a required pointer is NULL               */
+    W4A16_ERR_SHAPE = 2,        /* a size violates the shape rules          */
+    W4A16_ERR_UNSUPPORTED = 3,  /* group_size or dtype not supported        */
+    W4A16_ERR_ALIGN = 4,        /* a pointer is not aligned as required     */
+    W4A16_ERR_WORKSPACE = 5,    /* MSD workspace missing or too small       */
+    W4A16_ERR_DEVICE = 6        /* not a gfx950 device, or a launch failed  */
+} w4a16_status;
+
+typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1 } w4a16_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *w4a16_status_str(int status);
+
+/* Bytes of the prepacked buffer for E experts of K x N weights: E*K*N/2. */
+size_t w4a16_prepacked_bytes(int64_t E, int64_t K, int64_t N);
+
+/*
+ * Offline weight repack (run once per model load).  Reorders the nibbles of
+ * w[E][K][N/2] into the library's tile layout so the GEMM kernels read 32
+ * nibbles of one column with one 128-bit load and dequantize them in
+ * registers straight into the matrix-core operand, with no LDS round trip.
+ * Layout: 1024-byte tiles ordered (expert, 16-column block, 128-row group);
+ * slot L (16 bytes) of a tile holds column 16*nb + L%16, rows
+ * 128*g + 32*(L/16) + r (r = 0..31); word t of the slot holds r = 8t + i with
+ * row r's code at bit 4*(i/2) + 16*(i%2); the code is u (is_signed == 0) or
+ * q + 8 (is_signed == 1).  Motivation: "Marlin layout" (pwwt.cn notes,
+ * §6.2: weights reordered for memory access, kernels matched to the layout);
+ * QUICK abstract (offline interleave that skips the shared-memory write-back
+ * after dequantization); Humming article (weights reordered for the target
+ * kernel).  w and w_packed: device, E*K*N/2 bytes each, must not overlap.
+ */
+w4a16_status w4a16_prepack(const void *w, void *w_packed, int64_t E, int64_t K, int64_t N,
+                           int is_signed, void *stream);
+
+/*
+ * Dense W4A16 GEMM: y[M][N] = x[M][K] . dequant(W).
+ *   x        [M][K] fp16/bf16 (dtype dt)
+ *   w_packed prepacked weights (E = 1)
+ *   scale    [K/128][N], dtype dt
+ *   zero     [K/128][N/2] uint4 or NULL (see Signedness)
+ *   y        [M][N], dtype dt
+ * Small M runs a split-K matrix-core kernel whose waves reduce through LDS;
+ * large M runs an LDS-staged tile kernel (see the design notes).
+ */
+w4a16_status w4a16_gemm(const void *x, const void *w_packed, const void *scale,
+                        const void *zero, void *y, int64_t M, int64_t K, int64_t N,
+                        int64_t group_size, int dt, void *stream);
+
+/*
+ * MSD A16W4 PerGroup GEMM (WeightQuantBatchMatmulExperiment operator
+ * deep-dive, §4.1 eqs. 1-11): per row and 128-group, A_max = max|x|; the
+ * group is split into three int4 residual layers with the fp32 factors
+ * 7.49, 14.98, 14.98 (round half to even); the layers are multiplied with the
+ * int4 weights by int8 matrix-core instructions with int32 accumulation, then
+ * merged as ((Y1/7.49 + Y2/(7.49*14.98) + Y3/(7.49*14.98^2)) * A_max) * scale
+ * and accumulated over groups in fp32.
+ *   x                [M][K] fp16
+ *   w_packed         prepacked signed weights (is_signed = 1)
+ *   antiquant_scale  [K/128][N] fp16
+ *   y                [M][N] fp16
+ *   workspace        device scratch of at least w4a16_msd_workspace_bytes()
+ *                    bytes, 16-byte aligned, owned by the caller; its contents
+ *                    on entry are ignored and on return are unspecified.
+ * Two-stage use as in the page's aclnn API (§5.4): query the size, allocate,
+ * then call.  Calls sharing one workspace must be ordered on one stream.
+ */
+size_t w4a16_msd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
+
+w4a16_status w4a16_msd_gemm(const void *x, const void *w_packed, const void *antiquant_scale,
+                            void *y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Grouped (MoE) W4A16 GEMM: for each expert e, rows
+ * expert_offsets[e] .. expert_offsets[e+1]-1 of x are multiplied by expert
+ * e's weights.  Rows must already be gathered and sorted by expert.
+ *   x               [R][K], dtype dt
+ *   expert_offsets  DEVICE int32[E+1], offsets[0] = 0, non-decreasing,
+ *                   offsets[E] = R (read on the device only: no host sync)
+ *   w_packed        prepacked weights of all E experts (E*K*N/2 bytes)
+ *   scale           [E][K/128][N], dtype dt
+ *   zero            [E][K/128][N/2] or NULL
+ *   y               [R][N], dtype dt; rows of experts without rows: none
+ * Experts with no rows cost nothing beyond a skipped tile slot (Humming
+ * article: dense and MoE workloads share the kernel components).
+ */
+w4a16_status w4a16_grouped_gemm(const void *x, const int32_t *expert_offsets, const void *w_packed,
+                                const void *scale, const void *zero, void *y, int64_t E,
+                                int64_t R, int64_t K, int64_t N, int64_t group_size, int dt,
+                                void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A16_H */

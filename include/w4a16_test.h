@@ -1,0 +1,44 @@
+/*
+ * w4a16_test.h — test hooks of libw4a16.  Not part of the product API: they
+ * expose intermediate results of the same kernels for bit-exact checks on
+ * small shapes, and let tests force a kernel variant.
+ */
+#ifndef W4A16_TEST_H
+#define W4A16_TEST_H
+
+#include "w4a16.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Inverse of w4a16_prepack: w_packed -> plain w[E][K][N/2] (device pointers). */
+w4a16_status w4a16_test_unpack(const void *w_packed, void *w, int64_t E, int64_t K, int64_t N,
+                               int is_signed, void *stream);
+
+/*
+ * MSD intermediates from the production kernels (small shapes only):
+ *   amax    [M][K/128]      fp32  (eq.1)
+ *   layers  [3][M][K]       int8  (eqs.2-8), plain k order
+ *   yint    [K/128][3][M][N] int32 (eq.9), one product per group
+ * workspace as for w4a16_msd_gemm.  All pointers are device pointers.
+ */
+w4a16_status w4a16_test_msd_intermediates(const void *x, const void *w_packed, int64_t M,
+                                          int64_t K, int64_t N, int64_t group_size,
+                                          float *amax, int8_t *layers, int32_t *yint,
+                                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Force the dense GEMM kernel family for subsequent calls in this process:
+ * 0 = automatic (default), 1 = small-M split-K kernel, 2 = tile kernel.
+ * Not thread-safe; tests and benchmarks only.  Returns the previous value.
+ */
+int w4a16_test_force_variant(int variant);
+
+/* Name of the kernel variant the dispatcher picks for a dense call. */
+const char *w4a16_test_variant_name(int64_t M, int64_t K, int64_t N, int dt, int has_zero);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

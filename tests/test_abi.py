@@ -1,0 +1,120 @@
+"""The C-ABI library loads and exports every declared entry point; host-side
+validation rejects bad arguments before touching the device.  No compute
+calls are made here (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import weight_only_quantized_amd as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for h in ("w4a16.h", "w4a16_test.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = w4.lib()
+    declared = _declared()
+    assert {"w4a16_prepack", "w4a16_gemm", "w4a16_msd_gemm", "w4a16_grouped_gemm",
+            "w4a16_msd_workspace_bytes", "w4a16_prepacked_bytes", "w4a16_status_str"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == set(w4.EXPORTED)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert w4.w4a16_status_str(s).startswith(w4.STATUS_NAMES[s])
+    assert "UNKNOWN" in w4.w4a16_status_str(99)
+
+
+def test_size_queries():
+    assert w4.w4a16_prepacked_bytes(1, 4096, 14336) == 4096 * 14336 // 2
+    assert w4.w4a16_prepacked_bytes(64, 2048, 1408) == 64 * 2048 * 1408 // 2
+    assert w4.w4a16_prepacked_bytes(0, 128, 64) == 0
+    ws = w4.w4a16_msd_workspace_bytes(64, 8192, 8192)
+    # at least A_max/coefficients + three int8 layers
+    assert ws >= 3 * 64 * 8192 and ws % 256 == 0
+    assert w4.w4a16_msd_workspace_bytes(64, 8192, 8192, 64) == 0     # unsupported group
+    assert w4.w4a16_msd_workspace_bytes(0, 8192, 8192) == 0
+    assert w4.w4a16_msd_workspace_bytes(1, 100, 8192) == 0            # K % 128 != 0
+
+
+FAKE = 1 << 40          # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(group_size=64), 3),
+    (dict(dt=7), 3),
+    (dict(K=100), 2),
+    (dict(K=0), 2),
+    (dict(N=96), 2),
+    (dict(M=-1), 2),
+])
+def test_gemm_validation(kw, status):
+    args = dict(M=4, K=256, N=256, group_size=128, dt=0)
+    args.update(kw)
+    st = w4.lib().w4a16_gemm(FAKE, FAKE, FAKE, None, FAKE, args["M"], args["K"], args["N"],
+                            args["group_size"], args["dt"], None)
+    assert st == status
+
+
+def test_gemm_null_and_align():
+    L = w4.lib()
+    assert L.w4a16_gemm(None, FAKE, FAKE, None, FAKE, 4, 256, 256, 128, 0, None) == 1
+    assert L.w4a16_gemm(FAKE, FAKE, None, None, FAKE, 4, 256, 256, 128, 0, None) == 1
+    assert L.w4a16_gemm(FAKE + 8, FAKE, FAKE, None, FAKE, 4, 256, 256, 128, 0, None) == 4
+    assert L.w4a16_gemm(FAKE, FAKE + 4, FAKE, None, FAKE, 4, 256, 256, 128, 0, None) == 4
+    assert L.w4a16_gemm(FAKE, FAKE, FAKE + 1, None, FAKE, 4, 256, 256, 128, 0, None) == 4
+
+
+def test_m_zero_is_noop():
+    L = w4.lib()
+    assert L.w4a16_gemm(None, None, None, None, None, 0, 256, 256, 128, 1, None) == 0
+    assert L.w4a16_msd_gemm(None, None, None, None, 0, 256, 256, 128, None, 0, None) == 0
+    assert L.w4a16_grouped_gemm(None, None, None, None, None, None, 4, 0, 256, 256, 128, 1, None) == 0
+
+
+def test_msd_validation():
+    L = w4.lib()
+    ws = w4.w4a16_msd_workspace_bytes(4, 256, 256)
+    assert L.w4a16_msd_gemm(FAKE, FAKE, FAKE, FAKE, 4, 256, 256, 64, FAKE, ws, None) == 3
+    assert L.w4a16_msd_gemm(FAKE, FAKE, FAKE, FAKE, 4, 250, 256, 128, FAKE, ws, None) == 2
+    assert L.w4a16_msd_gemm(FAKE, FAKE, FAKE, FAKE, 4, 256, 256, 128, None, ws, None) == 5
+    assert L.w4a16_msd_gemm(FAKE, FAKE, FAKE, FAKE, 4, 256, 256, 128, FAKE, ws - 1, None) == 5
+    assert L.w4a16_msd_gemm(FAKE, FAKE, None, FAKE, 4, 256, 256, 128, FAKE, ws, None) == 1
+    assert L.w4a16_msd_gemm(FAKE, FAKE, FAKE, FAKE, 4, 256, 256, 128, FAKE + 8, ws, None) == 4
+
+
+def test_grouped_and_prepack_validation():
+    L = w4.lib()
+    assert L.w4a16_grouped_gemm(FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, 16, 256, 256, 128, 1, None) == 2
+    assert L.w4a16_grouped_gemm(FAKE, None, FAKE, FAKE, None, FAKE, 4, 16, 256, 256, 128, 1, None) == 1
+    assert L.w4a16_grouped_gemm(FAKE, FAKE + 2, FAKE, FAKE, None, FAKE, 4, 16, 256, 256, 128, 1, None) == 4
+    assert L.w4a16_grouped_gemm(FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 16, 256, 256, 128, 5, None) == 3
+    assert L.w4a16_prepack(FAKE, FAKE, 0, 256, 256, 1, None) == 2
+    assert L.w4a16_prepack(FAKE, FAKE, 1, 200, 256, 1, None) == 2
+    assert L.w4a16_prepack(None, FAKE, 1, 256, 256, 1, None) == 1
+    assert L.w4a16_prepack(FAKE + 1, FAKE, 1, 256, 256, 1, None) == 4
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(w4.W4A16Error) as ei:
+        w4.w4a16_gemm(FAKE, FAKE, FAKE, None, FAKE, 4, 256, 256, group_size=32, dt=0, stream=0)
+    assert ei.value.status == 3
+
+
+def test_variant_table():
+    assert "small" in w4.w4a16_test_variant_name(1, 4096, 14336, 1, 1)
+    assert "small" in w4.w4a16_test_variant_name(16, 4096, 14336, 1, 1)
+    assert "tile" in w4.w4a16_test_variant_name(17, 4096, 4096, 1, 0)
+    assert "tile" in w4.w4a16_test_variant_name(4096, 4096, 4096, 1, 0)

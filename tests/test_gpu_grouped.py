@@ -1,0 +1,45 @@
+"""Grouped (MoE) W4A16 parity against the oracle: the MoE workload with
+Zipf(1.1) top-8 routing, and skewed / empty expert edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(orc, p, label):
+    from gpu_helpers import Dev, check_tol, to_host_u16
+    print(f"[case] {label} E={p.E} R={p.M} K={p.K} N={p.N} counts={np.diff(p.offsets).tolist()[:16]}", flush=True)
+    d = Dev(p)
+    y = d.grouped(d.new_y(fill=0))
+    torch.cuda.synchronize()
+    _, y_ref = orc.grouped(p.x, p.offsets, p.w, p.scale, p.zero, p.E, p.M, p.K, p.N, p.dtype)
+    return check_tol(to_host_u16(y), y_ref, p.dtype, label=label)
+
+
+def test_moe_full(orc):
+    _check(orc, synth.moe(), "moe")
+
+
+@pytest.mark.parametrize("counts,dt,signed", [
+    ([5, 0, 17, 1, 0, 9], synth.BF16, True),
+    ([0, 0, 0, 40], synth.BF16, False),
+    ([300], synth.F16, True),
+    ([129, 0, 128, 1, 0], synth.F16, False),
+    ([0] * 10 + [3] + [0] * 50 + [200], synth.BF16, True),
+])
+def test_edge_counts(orc, counts, dt, signed):
+    p = synth.make_grouped(len(counts), max(sum(counts), 1), 1, 256, 320, dt, signed=signed,
+                           counts=counts, seed=len(counts))
+    _check(orc, p, f"grouped_{counts[:6]}")
+
+
+def test_many_experts_over_workgroup_scan(orc):
+    """E larger than one workgroup's scan width (512) exercises the carry."""
+    rng = np.random.default_rng(4)
+    counts = rng.integers(0, 3, size=700)
+    counts[rng.integers(0, 700, 5)] = 70
+    p = synth.make_grouped(700, int(counts.sum()), 1, 128, 64, synth.BF16, counts=counts, seed=2)
+    _check(orc, p, "many_experts")

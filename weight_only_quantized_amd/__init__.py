@@ -1,0 +1,142 @@
+"""Python binding of libw4a16 (weight-only quantized matmul on MI355X).
+
+Argument marshalling only: every function has the name of the C entry point
+it calls (include/w4a16.h, include/w4a16_test.h), takes device tensors (torch
+tensors on a ROCm device, or raw integer device addresses) plus sizes, and
+enqueues on the given stream (default: torch's current stream).  Every step of
+the computation runs in the HIP kernels of libw4a16.so; there is no fallback.
+A non-OK status raises :class:`W4A16Error`.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+
+W4A16_F16 = 0
+W4A16_BF16 = 1
+GROUP_SIZE = 128
+
+W4A16_OK = 0
+STATUS_NAMES = {0: "W4A16_OK", 1: "W4A16_ERR_NULL", 2: "W4A16_ERR_SHAPE", 3: "W4A16_ERR_UNSUPPORTED",
+                4: "W4A16_ERR_ALIGN", 5: "W4A16_ERR_WORKSPACE", 6: "W4A16_ERR_DEVICE"}
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {w4a16_status_str(status)} (status {status})")
+
+
+_lib = None
+_p = C.c_void_p
+_i64 = C.c_int64
+_SIGS = {
+    "w4a16_status_str": ([C.c_int], C.c_char_p),
+    "w4a16_prepacked_bytes": ([_i64, _i64, _i64], C.c_size_t),
+    "w4a16_prepack": ([_p, _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
+    "w4a16_gemm": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p], C.c_int),
+    "w4a16_msd_workspace_bytes": ([_i64, _i64, _i64, _i64], C.c_size_t),
+    "w4a16_msd_gemm": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, C.c_size_t, _p], C.c_int),
+    "w4a16_grouped_gemm": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, C.c_int, _p], C.c_int),
+    "w4a16_test_unpack": ([_p, _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
+    "w4a16_test_msd_intermediates": ([_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, C.c_size_t, _p], C.c_int),
+    "w4a16_test_force_variant": ([C.c_int], C.c_int),
+    "w4a16_test_variant_name": ([_i64, _i64, _i64, C.c_int, C.c_int], C.c_char_p),
+}
+EXPORTED = tuple(_SIGS)
+
+
+def lib():
+    """Load libw4a16.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+        L = C.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, where):
+    if status != W4A16_OK:
+        raise W4A16Error(status, where)
+
+
+def w4a16_status_str(status: int) -> str:
+    return lib().w4a16_status_str(int(status)).decode()
+
+
+def w4a16_prepacked_bytes(E: int, K: int, N: int) -> int:
+    return lib().w4a16_prepacked_bytes(E, K, N)
+
+
+def w4a16_prepack(w, w_packed, E, K, N, is_signed, stream=None):
+    _check(lib().w4a16_prepack(_ptr(w), _ptr(w_packed), E, K, N, int(is_signed), _stream(stream)), "w4a16_prepack")
+
+
+def w4a16_gemm(x, w_packed, scale, zero, y, M, K, N, group_size=GROUP_SIZE, dt=W4A16_BF16, stream=None):
+    _check(lib().w4a16_gemm(_ptr(x), _ptr(w_packed), _ptr(scale), _ptr(zero), _ptr(y), M, K, N, group_size,
+                            int(dt), _stream(stream)), "w4a16_gemm")
+
+
+def w4a16_msd_workspace_bytes(M, K, N, group_size=GROUP_SIZE) -> int:
+    return lib().w4a16_msd_workspace_bytes(M, K, N, group_size)
+
+
+def w4a16_msd_gemm(x, w_packed, antiquant_scale, y, M, K, N, group_size=GROUP_SIZE, workspace=None,
+                   workspace_bytes=0, stream=None):
+    _check(lib().w4a16_msd_gemm(_ptr(x), _ptr(w_packed), _ptr(antiquant_scale), _ptr(y), M, K, N, group_size,
+                                _ptr(workspace), int(workspace_bytes), _stream(stream)), "w4a16_msd_gemm")
+
+
+def w4a16_grouped_gemm(x, expert_offsets, w_packed, scale, zero, y, E, R, K, N, group_size=GROUP_SIZE,
+                       dt=W4A16_BF16, stream=None):
+    _check(lib().w4a16_grouped_gemm(_ptr(x), _ptr(expert_offsets), _ptr(w_packed), _ptr(scale), _ptr(zero),
+                                    _ptr(y), E, R, K, N, group_size, int(dt), _stream(stream)),
+           "w4a16_grouped_gemm")
+
+
+# ---- test hooks (include/w4a16_test.h) ----------------------------------------
+
+def w4a16_test_unpack(w_packed, w, E, K, N, is_signed, stream=None):
+    _check(lib().w4a16_test_unpack(_ptr(w_packed), _ptr(w), E, K, N, int(is_signed), _stream(stream)),
+           "w4a16_test_unpack")
+
+
+def w4a16_test_msd_intermediates(x, w_packed, M, K, N, amax, layers, yint, workspace, workspace_bytes,
+                                 group_size=GROUP_SIZE, stream=None):
+    _check(lib().w4a16_test_msd_intermediates(_ptr(x), _ptr(w_packed), M, K, N, group_size, _ptr(amax),
+                                              _ptr(layers), _ptr(yint), _ptr(workspace), int(workspace_bytes),
+                                              _stream(stream)), "w4a16_test_msd_intermediates")
+
+
+def w4a16_test_force_variant(variant: int) -> int:
+    return lib().w4a16_test_force_variant(int(variant))
+
+
+def w4a16_test_variant_name(M, K, N, dt, has_zero) -> str:
+    return lib().w4a16_test_variant_name(M, K, N, int(dt), int(has_zero)).decode()

@@ -1,0 +1,185 @@
+// api.cpp — C ABI of libw4a16: argument validation, device check, dispatch.
+// Every check runs on the host before any launch (nothing is enqueued on an
+// error).  No exception crosses the ABI; the library never allocates device
+// memory and never synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/w4a16.h"
+#include "../../include/w4a16_test.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    std::once_flag once;
+    bool gfx950 = false;
+    int cus = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::atomic<int> g_force_variant{0};
+
+// 1 if the current device is gfx950, 0 if not, -1 on a runtime error.
+int current_device_ok() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    DeviceInfo &d = g_dev[dev];
+    std::call_once(d.once, [&] {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+            d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+            d.cus = prop.multiProcessorCount;
+        }
+    });
+    return d.gfx950 ? 1 : 0;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+w4a16_status map_err(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_DEVICE; }
+
+w4a16_status check_kn(int64_t K, int64_t N, int64_t group_size) {
+    if (group_size != 128) return W4A16_ERR_UNSUPPORTED;
+    if (K <= 0 || N <= 0 || K % 128 != 0 || N % 64 != 0) return W4A16_ERR_SHAPE;
+    // the kernels index tiles and rows with 32-bit grid coordinates
+    if (K > (int64_t(1) << 30) || N > (int64_t(1) << 30)) return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+// Dense dispatch table: decode-sized M goes to the split-K kernel, the rest to
+// the LDS-staged tile kernel.
+int pick_variant(int64_t M) {
+    const int forced = g_force_variant.load(std::memory_order_relaxed);
+    if (forced == 1 && M <= 16) return 1;
+    if (forced == 2) return 2;
+    return M <= 16 ? 1 : 2;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *w4a16_status_str(int status) {
+    switch (status) {
+        case W4A16_OK: return "W4A16_OK";
+        case W4A16_ERR_NULL: return "W4A16_ERR_NULL: a required pointer is NULL";
+        case W4A16_ERR_SHAPE: return "W4A16_ERR_SHAPE: sizes violate K>0, K%128==0, N>0, N%64==0, M>=0, E>=1";
+        case W4A16_ERR_UNSUPPORTED: return "W4A16_ERR_UNSUPPORTED: group_size must be 128, dtype F16 or BF16 (MSD: F16)";
+        case W4A16_ERR_ALIGN: return "W4A16_ERR_ALIGN: x, w_packed, workspace need 16-byte, scale and y 2-byte alignment";
+        case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE: MSD workspace is NULL or smaller than w4a16_msd_workspace_bytes()";
+        case W4A16_ERR_DEVICE: return "W4A16_ERR_DEVICE: current device is not gfx950 or a launch failed";
+        default: return "W4A16_ERR_UNKNOWN";
+    }
+}
+
+size_t w4a16_prepacked_bytes(int64_t E, int64_t K, int64_t N) {
+    if (E < 1 || K <= 0 || N <= 0) return 0;
+    return (size_t)E * (size_t)K * (size_t)N / 2;
+}
+
+w4a16_status w4a16_prepack(const void *w, void *w_packed, int64_t E, int64_t K, int64_t N, int is_signed,
+                           void *stream) {
+    if (!w || !w_packed) return W4A16_ERR_NULL;
+    if (E < 1) return W4A16_ERR_SHAPE;
+    w4a16_status st = check_kn(K, N, 128);
+    if (st != W4A16_OK) return st;
+    if (!aligned(w, 16) || !aligned(w_packed, 16)) return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_prepack(w, w_packed, E, K, N, is_signed ? 1 : 0, (hipStream_t)stream));
+}
+
+w4a16_status w4a16_gemm(const void *x, const void *w_packed, const void *scale, const void *zero, void *y,
+                        int64_t M, int64_t K, int64_t N, int64_t group_size, int dt, void *stream) {
+    if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
+    w4a16_status st = check_kn(K, N, group_size);
+    if (st != W4A16_OK) return st;
+    if (M < 0 || M > (int64_t(1) << 31) - 1) return W4A16_ERR_SHAPE;
+    if (M == 0) return W4A16_OK;
+    if (!x || !w_packed || !scale || !y) return W4A16_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(scale, 2) || !aligned(y, 2))
+        return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    hipStream_t s = (hipStream_t)stream;
+    if (pick_variant(M) == 1) return map_err(w4::launch_gemm_small(x, w_packed, scale, zero, y, M, K, N, dt, s));
+    return map_err(w4::launch_gemm_tile(x, nullptr, w_packed, scale, zero, y, M, K, N, 1, dt, s));
+}
+
+size_t w4a16_msd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+    if (check_kn(K, N, group_size) != W4A16_OK || M < 0) return 0;
+    if (M == 0) return 0;
+    return w4::msd_plan(M, K, N).total;
+}
+
+w4a16_status w4a16_msd_gemm(const void *x, const void *w_packed, const void *antiquant_scale, void *y,
+                            int64_t M, int64_t K, int64_t N, int64_t group_size, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    w4a16_status st = check_kn(K, N, group_size);
+    if (st != W4A16_OK) return st;
+    if (M < 0 || M > (int64_t(1) << 24)) return W4A16_ERR_SHAPE;
+    if (M == 0) return W4A16_OK;
+    if (!x || !w_packed || !antiquant_scale || !y) return W4A16_ERR_NULL;
+    if (!workspace || workspace_bytes < w4::msd_plan(M, K, N).total) return W4A16_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(antiquant_scale, 2) || !aligned(y, 16) ||
+        !aligned(workspace, 16))
+        return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_msd(x, w_packed, antiquant_scale, y, M, K, N, workspace, (hipStream_t)stream));
+}
+
+w4a16_status w4a16_grouped_gemm(const void *x, const int32_t *expert_offsets, const void *w_packed,
+                                const void *scale, const void *zero, void *y, int64_t E, int64_t R, int64_t K,
+                                int64_t N, int64_t group_size, int dt, void *stream) {
+    if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
+    w4a16_status st = check_kn(K, N, group_size);
+    if (st != W4A16_OK) return st;
+    if (E < 1 || E > (int64_t(1) << 20) || R < 0 || R > (int64_t(1) << 31) - 1) return W4A16_ERR_SHAPE;
+    if (R == 0) return W4A16_OK;
+    if (!x || !expert_offsets || !w_packed || !scale || !y) return W4A16_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(scale, 2) || !aligned(y, 2) ||
+        !aligned(expert_offsets, 4))
+        return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_gemm_tile(x, expert_offsets, w_packed, scale, zero, y, R, K, N, E, dt,
+                                        (hipStream_t)stream));
+}
+
+// ---- test hooks -------------------------------------------------------------
+
+w4a16_status w4a16_test_unpack(const void *w_packed, void *w, int64_t E, int64_t K, int64_t N, int is_signed,
+                               void *stream) {
+    if (!w || !w_packed) return W4A16_ERR_NULL;
+    if (E < 1) return W4A16_ERR_SHAPE;
+    w4a16_status st = check_kn(K, N, 128);
+    if (st != W4A16_OK) return st;
+    if (!aligned(w, 16) || !aligned(w_packed, 16)) return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_unpack(w_packed, w, E, K, N, is_signed ? 1 : 0, (hipStream_t)stream));
+}
+
+w4a16_status w4a16_test_msd_intermediates(const void *x, const void *w_packed, int64_t M, int64_t K, int64_t N,
+                                          int64_t group_size, float *amax, int8_t *layers, int32_t *yint,
+                                          void *workspace, size_t workspace_bytes, void *stream) {
+    w4a16_status st = check_kn(K, N, group_size);
+    if (st != W4A16_OK) return st;
+    if (M <= 0 || M > 4096) return W4A16_ERR_SHAPE;
+    if (!x || !w_packed || !amax || !layers || !yint) return W4A16_ERR_NULL;
+    if (!workspace || workspace_bytes < w4::msd_plan(M, K, N).total) return W4A16_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(workspace, 16)) return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_msd_intermediates(x, w_packed, M, K, N, amax, layers, yint, workspace,
+                                                (hipStream_t)stream));
+}
+
+int w4a16_test_force_variant(int variant) { return g_force_variant.exchange(variant); }
+
+const char *w4a16_test_variant_name(int64_t M, int64_t K, int64_t N, int dt, int has_zero) {
+    (void)K; (void)N; (void)dt; (void)has_zero;
+    return pick_variant(M) == 1 ? "gemm_small_kernel<NB=2,W=8>" : "gemm_tile_kernel<BM=128,BN=256,WM=2,WN=4>";
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// common.hpp — device helpers shared by the libw4a16 kernels (gfx950 only).
+//
+// Prepacked weight tile (see include/w4a16.h): 1024 bytes per (16-column
+// block, 128-row group).  Slot L = 16*c + j (c = 32-row chunk 0..3, j =
+// column 0..15) is 16 bytes = 4 words; word t holds rows r = 32c + 8t + i,
+// i = 0..7, with the code of row r at bit 4*(i/2) + 16*(i%2).  One 128-bit
+// load therefore gives a lane the 32 codes of one column for one chunk, and
+//   ((word >> 4p) & 0x000F000F)
+// is the pair (i = 2p, i = 2p+1) already in the low/high 16-bit halves that
+// the 16-bit matrix-core operand register expects.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef _Float16 f16x8_t __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef _Float16 f16x2_t __attribute__((__vector_size__(2 * sizeof(_Float16))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+typedef int i32x4_t __attribute__((__vector_size__(4 * sizeof(int))));
+typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+constexpr int kGroup = 128;          // K rows per quantization group
+constexpr int kTileBytes = 1024;     // one (16-column, 128-row) weight tile
+
+// ---------------------------------------------------------------------------
+// 16-bit float <-> fp32
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ float h2f(uint16_t b) {
+    if constexpr (DT == DT_BF16) {
+        return __uint_as_float(((uint32_t)b) << 16);
+    } else {
+        _Float16 h = __builtin_bit_cast(_Float16, b);
+        return (float)h;
+    }
+}
+
+// Round-to-nearest-even fp32 -> 16-bit pattern.
+template <int DT>
+__device__ __forceinline__ uint16_t f2h(float v) {
+    if constexpr (DT == DT_BF16) {
+        __bf16 b = (__bf16)v;          // v_cvt_pk_bf16_f32: RNE
+        return __builtin_bit_cast(uint16_t, b);
+    } else {
+        _Float16 h = (_Float16)v;      // v_cvt_f16_f32: RNE
+        return __builtin_bit_cast(uint16_t, h);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core wrappers.  Operands are passed as four 32-bit registers.
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t &a, const u32x4_t &b, const f32x4_t &c) {
+    if constexpr (DT == DT_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                      __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                     __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16_t mfma32x32x16(const u32x4_t &a, const u32x4_t &b, const f32x16_t &c) {
+    if constexpr (DT == DT_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                      __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                     __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x4_t mfma_i8_16x16x64(const u32x4_t &a, const u32x4_t &b, const i32x4_t &c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
+                                                __builtin_bit_cast(i32x4_t, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// In-register dequantization of one prepacked word (8 codes) into the 16-bit
+// operand of one 16-k matrix-core step.
+//
+// bf16: the exponent pattern 0x4300 (= 128.0) with the code in the 7 mantissa
+//       bits gives exactly 128 + v.  The bias (128 + z) is removed inside the
+//       matrix core by an extra correction step (see kernels), so the operand
+//       costs one shift and one and-or per pair.
+// fp16: 0x6400 (= 1024.0) | v gives 1024 + v; one packed fp16 add of
+//       -(1024 + z) gives the exact integer v - z.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kMagicBf16 = 0x43004300u;   // bf16 128.0 in both halves
+constexpr uint32_t kMagicF16 = 0x64006400u;    // fp16 1024.0 in both halves
+
+template <int DT>
+__device__ __forceinline__ u32x4_t dequant_word(uint32_t w, uint32_t negbias2) {
+    u32x4_t r;
+    constexpr uint32_t magic = DT == DT_BF16 ? kMagicBf16 : kMagicF16;
+    r[0] = (w & 0x000F000Fu) | magic;
+    r[1] = ((w >> 4) & 0x000F000Fu) | magic;
+    r[2] = ((w >> 8) & 0x000F000Fu) | magic;
+    r[3] = ((w >> 12) & 0x000F000Fu) | magic;
+    if constexpr (DT == DT_F16) {
+        f16x2_t nb = __builtin_bit_cast(f16x2_t, negbias2);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            r[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, r[p]) + nb);
+    } else {
+        (void)negbias2;
+    }
+    return r;
+}
+
+// -(1024 + z) as an fp16 pair (exact: 1024 + z < 2048).
+__device__ __forceinline__ uint32_t f16_negbias2(uint32_t z) {
+    uint32_t h = 0xE400u + z;     // fp16 bits of -(1024 + z)
+    return h | (h << 16);
+}
+
+// -(128 + z) as bf16 bits (exact: 128 + z < 256 has 8 significant bits).
+__device__ __forceinline__ uint32_t bf16_negbias(uint32_t z) { return 0xC300u + z; }
+
+// bf16 RNE of an fp32 value, returned as raw bits, and its exact fp32 value.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float v) {
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// Split an fp32 value into three bf16 limbs hi + mid + lo (24 significant
+// bits in total; each subtraction is exact).
+__device__ __forceinline__ void split3_bf16(float v, uint32_t &hi, uint32_t &mid, uint32_t &lo) {
+    hi = bf16_bits_rne(v);
+    float r1 = v - __uint_as_float(hi << 16);
+    mid = bf16_bits_rne(r1);
+    float r2 = r1 - __uint_as_float(mid << 16);
+    lo = bf16_bits_rne(r2);
+}
+
+// Signed int8 operand from biased 4-bit codes (q + 8 in 0..15) held in the
+// low nibble of each byte: (b + 0x78) ^ 0x80 = q as two's complement, with no
+// carry between bytes (b + 0x78 <= 0x87).
+__device__ __forceinline__ uint32_t codes_to_s8(uint32_t b) { return (b + 0x78787878u) ^ 0x80808080u; }
+
+__device__ __forceinline__ u32x4_t ld128(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace w4

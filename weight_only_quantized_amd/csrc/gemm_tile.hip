@@ -1,0 +1,292 @@
+// gemm_tile.hip — large-M W4A16 GEMM and its grouped (MoE) form.
+//
+// Workgroup tile BM x BN over the whole K range; WM x WN waves, each owning a
+// TM x TN = (BM/WM) x (BN/WN) sub-tile computed with 32x32x16 matrix-core
+// steps in fp32.
+//  * Activations: the BM x 128 slice of x for one group is staged in LDS
+//    (double-buffered; the next group's slice is fetched into registers while
+//    the current one is multiplied).  Rows are padded to a 304-byte (bf16) /
+//    272-byte (fp16) stride so the 128-bit operand reads of 8 consecutive rows
+//    hit disjoint banks.
+//  * Weights: every wave loads its own 32-column x 128-row fragments straight
+//    from HBM/L2 into registers (two 128-bit loads per lane per 32 columns) and
+//    dequantizes them into the matrix-core operand: no LDS round trip for the
+//    weights (QUICK abstract: interleave offline so the dequantized weights
+//    skip the shared-memory write-back).
+//  * Per-group scale (design with exact integer weights inside the matrix
+//    core): acc_g = sum_{k in g} x * (v - z) in fp32, y += s[g][n] * acc_g.
+//    For bf16 the operand is 128 + v and the (128 + z) * sum_k x term is taken
+//    out by one extra step whose A operand is the three bf16 limbs of the row's
+//    group sum (computed while staging x) and whose B operand is -(128 + z).
+//  * Grouped: the workgroup index is mapped on the device to (expert, row
+//    tile) from the expert offsets (prefix sum of ceil(rows_e / BM)), so the
+//    host never reads the offsets; surplus workgroups exit at once.
+// Matrix-core mapping (v_mfma_f32_32x32x16_*): lane l feeds row/column l % 32
+// and k-block l / 32 (64 rows of the group: chunks 2*(l/32) and 2*(l/32)+1 of
+// the prepacked slot layout); result register r of lane l is row
+// 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace w4 {
+
+template <int DT, bool ZERO, int BM, int BN, int WM, int WN, bool GROUPED>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
+                 const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
+                 const uint8_t *__restrict__ zero, uint16_t *__restrict__ y,
+                 int64_t M, int64_t K, int64_t N, int E) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int RT = TM / 32, CT = TN / 32;
+    constexpr bool CORR = DT == DT_BF16;
+    constexpr int ROWB = (kGroup + (CORR ? 16 : 0)) * 2 + 16;   // LDS row stride (bytes)
+    constexpr int XP = BM * 16 / NT;                            // 16-byte x chunks per thread
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert((BM * 16) % NT == 0, "x staging must divide evenly");
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BM * ROWB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int G = (int)(K / kGroup);
+    const int64_t NBLK = N / 16;
+
+    int64_t row0, row_end;
+    int64_t e = 0;
+    if constexpr (GROUPED) {
+        __shared__ int s_info[2];
+        __shared__ int scan[NT];
+        const int bid = (int)blockIdx.x;
+        if (tid == 0) s_info[0] = -1;
+        int carry = 0;
+        for (int base = 0; base < E; base += NT) {
+            const int ee = base + tid;
+            const int cnt = ee < E ? offsets[ee + 1] - offsets[ee] : 0;
+            const int tl = cnt > 0 ? (cnt + BM - 1) / BM : 0;
+            scan[tid] = tl;
+            __syncthreads();
+            for (int off = 1; off < NT; off <<= 1) {
+                const int v = tid >= off ? scan[tid - off] : 0;
+                __syncthreads();
+                scan[tid] += v;
+                __syncthreads();
+            }
+            const int incl = scan[tid] + carry, excl = incl - tl;
+            if (ee < E && bid >= excl && bid < incl) {
+                s_info[0] = ee;
+                s_info[1] = bid - excl;
+            }
+            carry += scan[NT - 1];
+            __syncthreads();
+        }
+        if (s_info[0] < 0) return;   // uniform: surplus workgroup
+        e = s_info[0];
+        row0 = offsets[e] + (int64_t)s_info[1] * BM;
+        row_end = offsets[e + 1] < M ? offsets[e + 1] : M;   // offsets[E] == R by contract
+    } else {
+        row0 = (int64_t)blockIdx.x * BM;
+        row_end = M;
+    }
+    const int64_t n0 = (int64_t)blockIdx.y * BN;
+    const int64_t wcol0 = n0 + (int64_t)wn * TN;
+    const bool wave_cols = wcol0 < N;          // N % 64 == 0: a wave's columns are all in or all out
+
+    const uint16_t *sc = scale + e * (int64_t)G * N;
+    const uint8_t *zp = ZERO ? zero + e * (int64_t)G * (N / 2) : nullptr;
+    const uint8_t *we = wp + e * NBLK * (int64_t)G * kTileBytes;
+
+    // ---- activation staging -------------------------------------------------
+    u32x4_t xr[XP];
+    auto load_x = [&](int g) {
+#pragma unroll
+        for (int p = 0; p < XP; ++p) {
+            const int id = p * NT + tid, r = id >> 4, c16 = id & 15;
+            const int64_t grow = row0 + r;
+            if (grow < row_end) xr[p] = ld128(x + grow * K + (int64_t)g * kGroup + c16 * 8);
+            else xr[p] = u32x4_t{0, 0, 0, 0};
+        }
+    };
+    auto store_x = [&](int buf) {
+        uint8_t *base = lds + buf * BM * ROWB;
+#pragma unroll
+        for (int p = 0; p < XP; ++p) {
+            const int id = p * NT + tid, r = id >> 4, c16 = id & 15;
+            *reinterpret_cast<u32x4_t *>(base + r * ROWB + c16 * 16) = xr[p];
+            if constexpr (CORR) {
+                typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
+                const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+                float ps = 0.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xr[p][q]), ones, ps, false);
+                ps += __shfl_xor(ps, 1);
+                ps += __shfl_xor(ps, 2);
+                ps += __shfl_xor(ps, 4);
+                ps += __shfl_xor(ps, 8);
+                if (c16 == 0) {
+                    uint32_t hi, mid, lo;
+                    split3_bf16(ps, hi, mid, lo);
+                    *reinterpret_cast<u32x4_t *>(base + r * ROWB + 256) = u32x4_t{hi | (mid << 16), lo, 0, 0};
+                } else if (c16 == 1) {
+                    *reinterpret_cast<u32x4_t *>(base + r * ROWB + 272) = u32x4_t{0, 0, 0, 0};
+                }
+            }
+        }
+    };
+
+    // ---- weight fragments ---------------------------------------------------
+    const int lj = lane & 31, kg = lane >> 5;
+    int64_t boff[CT];          // byte offset of this lane's slot (chunk 2*kg) in group 0
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        const int64_t n = wcol0 + ct * 32 + lj;
+        const int64_t nb = n >> 4, jj = n & 15;
+        boff[ct] = nb * (int64_t)G * kTileBytes + ((2 * kg) * 16 + jj) * 16;
+    }
+    u32x4_t braw[CT][2], bnext[CT][2];
+    auto load_b = [&](int g, u32x4_t (&dst)[CT][2]) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const uint8_t *p = we + boff[ct] + (int64_t)g * kTileBytes;
+            dst[ct][0] = ld128(p);
+            dst[ct][1] = ld128(p + 256);     // chunk 2*kg + 1: 16 slots further
+        }
+    };
+
+    f32x16_t yacc[RT][CT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) yacc[rt][ct][r] = 0.f;
+
+    load_x(0);
+    store_x(0);
+    if (wave_cols) load_b(0, braw);
+    __syncthreads();
+
+    const int arow = wm * TM + lj;             // LDS row of this lane's A operand (row tile 0)
+    for (int g = 0; g < G; ++g) {
+        const int buf = g & 1;
+        if (g + 1 < G) {
+            load_x(g + 1);
+            if (wave_cols) load_b(g + 1, bnext);
+        }
+        if (wave_cols) {
+            float s[CT];
+            uint32_t nb2[CT];
+            u32x4_t bcorr[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const int64_t n = wcol0 + ct * 32 + lj;
+                s[ct] = h2f<DT>(sc[(int64_t)g * N + n]);
+                uint32_t z = 8;
+                if constexpr (ZERO) {
+                    const uint8_t zb = zp[((int64_t)g * N + n) >> 1];
+                    z = (n & 1) ? (zb >> 4) : (zb & 0xF);
+                }
+                if constexpr (CORR) {
+                    const uint32_t c = bf16_negbias(z);
+                    bcorr[ct] = kg == 0 ? u32x4_t{c | (c << 16), c, 0, 0} : u32x4_t{0, 0, 0, 0};
+                    nb2[ct] = 0;
+                } else {
+                    nb2[ct] = f16_negbias2(z);
+                }
+            }
+            const uint8_t *abase = lds + buf * BM * ROWB + arow * ROWB + kg * 128;
+            f32x16_t acc[RT][CT];
+            if constexpr (CORR) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(
+                        lds + buf * BM * ROWB + (arow + rt * 32) * ROWB + 256 + kg * 16);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mfma32x32x16<DT>(a, bcorr[ct], f32x16_t{});
+                }
+            } else {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[rt][ct][r] = 0.f;
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                u32x4_t a[RT], bq[CT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    a[rt] = *reinterpret_cast<const u32x4_t *>(abase + rt * 32 * ROWB + t * 16);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) bq[ct] = dequant_word<DT>(braw[ct][t >> 2][t & 3], nb2[ct]);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], acc[rt][ct]);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) yacc[rt][ct][r] += s[ct] * acc[rt][ct][r];
+        }
+        if (g + 1 < G) {
+            store_x(buf ^ 1);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                braw[ct][0] = bnext[ct][0];
+                braw[ct][1] = bnext[ct][1];
+            }
+        }
+        __syncthreads();
+    }
+
+    if (!wave_cols) return;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const int64_t col = wcol0 + ct * 32 + lj;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = row0 + wm * TM + rt * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
+                if (row < row_end) y[row * N + col] = f2h<DT>(yacc[rt][ct][r]);
+            }
+        }
+}
+
+template <int DT, bool ZERO, bool GROUPED>
+static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const void *wp, const void *scale,
+                                const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
+                                hipStream_t stream) {
+    constexpr int BM = 128, BN = 256, WM = 2, WN = 4;
+    const int64_t mtiles = GROUPED ? (M + BM - 1) / BM + E : (M + BM - 1) / BM;
+    const dim3 grid((unsigned)mtiles, (unsigned)((N + BN - 1) / BN));
+    hipLaunchKernelGGL((gemm_tile_kernel<DT, ZERO, BM, BN, WM, WN, GROUPED>), grid, dim3(WM * WN * 64), 0,
+                       stream, (const uint16_t *)x, offsets, (const uint8_t *)wp, (const uint16_t *)scale,
+                       (const uint8_t *)zero, (uint16_t *)y, M, K, N, (int)E);
+    return hipGetLastError();
+}
+
+template <bool GROUPED>
+static hipError_t tile_dispatch_dt(const void *x, const int32_t *offsets, const void *wp, const void *scale,
+                                   const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
+                                   int dt, hipStream_t stream) {
+    if (dt == DT_BF16)
+        return zero ? tile_dispatch<DT_BF16, true, GROUPED>(x, offsets, wp, scale, zero, y, M, K, N, E, stream)
+                    : tile_dispatch<DT_BF16, false, GROUPED>(x, offsets, wp, scale, zero, y, M, K, N, E, stream);
+    return zero ? tile_dispatch<DT_F16, true, GROUPED>(x, offsets, wp, scale, zero, y, M, K, N, E, stream)
+                : tile_dispatch<DT_F16, false, GROUPED>(x, offsets, wp, scale, zero, y, M, K, N, E, stream);
+}
+
+hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *wp, const void *scale,
+                            const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
+                            int dt, hipStream_t stream) {
+    if (offsets) return tile_dispatch_dt<true>(x, offsets, wp, scale, zero, y, M, K, N, E, dt, stream);
+    return tile_dispatch_dt<false>(x, nullptr, wp, scale, zero, y, M, K, N, 1, dt, stream);
+}
+
+}  // namespace w4

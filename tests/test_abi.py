@@ -118,3 +118,17 @@ def test_variant_table():
     assert "small" in w4.w4a16_test_variant_name(16, 4096, 14336, 1, 1)
     assert "tile" in w4.w4a16_test_variant_name(17, 4096, 4096, 1, 0)
     assert "tile" in w4.w4a16_test_variant_name(4096, 4096, 4096, 1, 0)
+
+
+def test_no_bit_cast_of_vector_subscript():
+    """Guard for a compiler issue: __builtin_bit_cast applied directly to a
+    vector-subscript expression (v[i]) is lowered as a read of element 0.  The
+    kernels must route such elements through a scalar (the `as<T>` helper)."""
+    csrc = os.path.join(ROOT, "weight_only_quantized_amd", "csrc")
+    bad = []
+    for f in os.listdir(csrc):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            for i, line in enumerate(open(os.path.join(csrc, f)), 1):
+                if re.search(r"__builtin_bit_cast\([^,]+,\s*[^()]*\[[^\]]+\]\s*\)", line):
+                    bad.append(f"{f}:{i}: {line.strip()}")
+    assert not bad, bad

@@ -25,6 +25,15 @@ typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
 
+typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
+
+// Reinterpret a 32-bit value.  Takes the word BY VALUE on purpose: this
+// compiler lowers __builtin_bit_cast applied directly to a vector-subscript
+// expression (v[i]) as a read of element 0, so vector elements must pass
+// through a scalar first.
+template <typename T>
+__device__ __forceinline__ T as(uint32_t w) { return __builtin_bit_cast(T, w); }
+
 constexpr int kGroup = 128;          // K rows per quantization group
 constexpr int kTileBytes = 1024;     // one (16-column, 128-row) weight tile
 
@@ -104,10 +113,10 @@ __device__ __forceinline__ u32x4_t dequant_word(uint32_t w, uint32_t negbias2) {
     r[2] = ((w >> 8) & 0x000F000Fu) | magic;
     r[3] = ((w >> 12) & 0x000F000Fu) | magic;
     if constexpr (DT == DT_F16) {
-        f16x2_t nb = __builtin_bit_cast(f16x2_t, negbias2);
+        const f16x2_t nb = as<f16x2_t>(negbias2);
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            r[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, r[p]) + nb);
+            r[p] = __builtin_bit_cast(uint32_t, as<f16x2_t>(r[p]) + nb);
     } else {
         (void)negbias2;
     }

@@ -75,14 +75,13 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
 
         u32x4_t acorr = {0, 0, 0, 0};
         if constexpr (DT == DT_BF16) {
-            typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
-            const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+            const bf16x2_t ones = as<bf16x2_t>(0x3F803F80u);
             float ps = 0.f;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
-                    ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xa[t][p]), ones, ps, false);
+                    ps = __builtin_amdgcn_fdot2_f32_bf16(as<bf16x2_t>(xa[t][p]), ones, ps, false);
             ps += __shfl_xor(ps, 16);
             ps += __shfl_xor(ps, 32);
             if (kc == 0) {

@@ -114,12 +114,11 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
             const int id = p * NT + tid, r = id >> 4, c16 = id & 15;
             *reinterpret_cast<u32x4_t *>(base + r * ROWB + c16 * 16) = xr[p];
             if constexpr (CORR) {
-                typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
-                const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+                const bf16x2_t ones = as<bf16x2_t>(0x3F803F80u);
                 float ps = 0.f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xr[p][q]), ones, ps, false);
+                    ps = __builtin_amdgcn_fdot2_f32_bf16(as<bf16x2_t>(xr[p][q]), ones, ps, false);
                 ps += __shfl_xor(ps, 1);
                 ps += __shfl_xor(ps, 2);
                 ps += __shfl_xor(ps, 4);

@@ -1,0 +1,386 @@
+#!/usr/bin/env python3
+"""Benchmark of libw4a16 on one MI355X.
+
+Headline workload (one JSON line on stdout): the decode W4A16 configuration,
+M in {1, 4, 16}, K=4096, N=14336, group 128, bf16 activations, unsigned int4
+weights with per-group uint4 zero points.  One step = the three GEMM calls
+(M=1, M=4, M=16) on inputs already resident in HBM.  Weight buffers rotate over
+more than 600 MB of distinct copies so the 256 MB Infinity Cache cannot hold
+them: every step streams its weights from HBM.
+
+value    = algorithmic bytes of K steps / wall time of the K steps
+           (synchronized on both sides) -> GB/s.
+roofline = the dominant kernel (the small-M split-K kernel): algorithmic
+           bytes per launch / its average launch duration, timed with HIP
+           events on the launch stream, against the 8 TB/s HBM peak.
+cpu_baseline = the CPU oracle on the same decode step (host cores).
+
+per_config adds the same measurement for the other workloads (tiny, prefill,
+MSD, MoE grouped); they are reported for completeness, the headline is decode.
+
+Algorithmic bytes of one dense call: x (M*K*2) + packed weights (K*N/2) +
+scales (K/128*N*2) + zero points (K/128*N/2, if any) + y (M*N*2).
+Algorithmic flops: 2*M*N*K (MSD also reports 6*M*N*K int8 ops).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16/fp16 MFMA
+INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA
+ROTATE_BYTES = 600 * 2 ** 20   # distinct bytes touched before a buffer is reused
+
+METRIC = "TFLOP/s + effective HBM GB/s (% of roofline), W4A16 g128, M=1..4096"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "weight_only_quantized_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def dense_bytes(M, K, N, zero):
+    G = K // 128
+    return M * K * 2 + K * N // 2 + G * N * 2 + (G * N // 2 if zero else 0) + M * N * 2
+
+
+# ---------------------------------------------------------------------------
+# GPU workloads
+# ---------------------------------------------------------------------------
+
+class Workload:
+    """Inputs resident on the GPU plus a launch(i) closure (i selects the
+    rotated buffer set)."""
+    name: str
+    calls: list          # list of (label, launch(i), bytes, flops)
+    nsets: int
+
+
+def _dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to("cuda:0")
+
+
+def _prepack(p, w_dev):
+    import torch
+    import weight_only_quantized_amd as w4
+    out = torch.empty(w4.w4a16_prepacked_bytes(p.E, p.K, p.N), dtype=torch.uint8, device="cuda:0")
+    w4.w4a16_prepack(w_dev, out, p.E, p.K, p.N, int(p.signed))
+    return out
+
+
+def _copies(t, nbytes_per_set):
+    n = max(1, -(-ROTATE_BYTES // max(nbytes_per_set, 1)))
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+def decode_workload():
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    ps = {M: synth.decode(M) for M in (1, 4, 16)}
+    p1 = ps[1]
+    wp = _prepack(p1, _dev(p1.w.reshape(-1)))            # same weights for the three M
+    sc, zr = _dev(p1.scale), _dev(p1.zero)
+    per_set = wp.numel() + sc.numel() * 2 + zr.numel()
+    wps = _copies(wp, per_set)
+    scs = [sc] + [sc.clone() for _ in range(len(wps) - 1)]
+    zrs = [zr] + [zr.clone() for _ in range(len(wps) - 1)]
+    xs = {M: _dev(ps[M].x) for M in ps}
+    ys = {M: torch.empty((M, p1.N), dtype=torch.int16, device="cuda:0") for M in ps}
+    K, N = p1.K, p1.N
+    calls = []
+    for M in (1, 4, 16):
+        def launch(i, M=M):
+            j = i % len(wps)
+            w4.w4a16_gemm(xs[M], wps[j], scs[j], zrs[j], ys[M], M, K, N, 128, synth.BF16)
+        calls.append((f"decode_m{M}", launch, dense_bytes(M, K, N, True), 2 * M * N * K))
+    return calls, len(wps)
+
+
+def tiny_workload():
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    p = synth.tiny()
+    wp = _prepack(p, _dev(p.w.reshape(-1)))
+    x, sc = _dev(p.x), _dev(p.scale)
+    y = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda:0")
+
+    def launch(i):
+        w4.w4a16_gemm(x, wp, sc, None, y, p.M, p.K, p.N, 128, synth.F16)
+    return [("tiny", launch, dense_bytes(p.M, p.K, p.N, False), 2 * p.M * p.N * p.K)], 1
+
+
+def prefill_workload():
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    p = synth.prefill()
+    wp = _prepack(p, _dev(p.w.reshape(-1)))
+    x, sc = _dev(p.x), _dev(p.scale)
+    y = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda:0")
+    per_set = wp.numel() + x.numel() * 2 + sc.numel() * 2
+    wps = _copies(wp, per_set)
+    xs = [x] + [x.clone() for _ in range(len(wps) - 1)]
+
+    def launch(i):
+        j = i % len(wps)
+        w4.w4a16_gemm(xs[j], wps[j], sc, None, y, p.M, p.K, p.N, 128, synth.BF16)
+    return [("prefill", launch, dense_bytes(p.M, p.K, p.N, False), 2 * p.M * p.N * p.K)], len(wps)
+
+
+def msd_workload():
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    p = synth.msd()
+    wp = _prepack(p, _dev(p.w.reshape(-1)))
+    x, sc = _dev(p.x), _dev(p.scale)
+    y = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda:0")
+    nb = w4.w4a16_msd_workspace_bytes(p.M, p.K, p.N)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    wps = _copies(wp, wp.numel() + sc.numel() * 2)
+    scs = [sc] + [sc.clone() for _ in range(len(wps) - 1)]
+
+    def launch(i):
+        j = i % len(wps)
+        w4.w4a16_msd_gemm(x, wps[j], scs[j], y, p.M, p.K, p.N, 128, ws, nb)
+    return [("msd", launch, dense_bytes(p.M, p.K, p.N, False), 2 * p.M * p.N * p.K)], len(wps)
+
+
+def moe_workload():
+    import numpy as np
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    p = synth.moe()
+    wp = _prepack(p, _dev(p.w.reshape(-1)))
+    x, sc, off = _dev(p.x), _dev(p.scale), _dev(p.offsets)
+    y = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda:0")
+    active = int(np.count_nonzero(np.diff(p.offsets)))
+    G = p.K // 128
+    nbytes = p.M * p.K * 2 + active * (p.K * p.N // 2 + G * p.N * 2) + p.M * p.N * 2 + (p.E + 1) * 4
+    wps = _copies(wp, wp.numel() + sc.numel() * 2)
+    scs = [sc] + [sc.clone() for _ in range(len(wps) - 1)]
+
+    def launch(i):
+        j = i % len(wps)
+        w4.w4a16_grouped_gemm(x, off, wps[j], scs[j], None, y, p.E, p.M, p.K, p.N, 128, synth.BF16)
+    return [("moe", launch, nbytes, 2 * p.M * p.N * p.K)], len(wps)
+
+
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+
+def run_steps(calls, steps, warmup):
+    """Wall time of `steps` steps (each = every call once), synchronized."""
+    import torch
+    for i in range(warmup):
+        for _, launch, _, _ in calls:
+            launch(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for _, launch, _, _ in calls:
+            launch(warmup + i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def per_launch_ms(calls, steps, warmup):
+    """Average duration of each call: `steps` back-to-back launches of that one
+    call between two HIP events on the launch stream (torch's current stream).
+    Back-to-back launches on one stream leave no measurable gap, so this is the
+    kernel time without the per-event overhead of timing single launches."""
+    import torch
+    out = []
+    for ci, (_, launch, _, _) in enumerate(calls):
+        for i in range(warmup):
+            launch(i)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            launch(warmup + i)
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / steps)
+    return out
+
+
+def measure(name, builder, steps, warmup):
+    calls, nsets = builder()
+    wall = run_steps(calls, steps, warmup)
+    lat = per_launch_ms(calls, steps, 2)
+    step_bytes = sum(c[2] for c in calls)
+    step_flops = sum(c[3] for c in calls)
+    out = {
+        "ms_per_step": wall / steps * 1e3,
+        "GBps": step_bytes * steps / wall / 1e9,
+        "TFLOPs": step_flops * steps / wall / 1e12,
+        "rotated_sets": nsets,
+        "calls": {},
+    }
+    for (label, _, nb, nf), ms in zip(calls, lat):
+        out["calls"][label] = {
+            "event_ms": ms,
+            "bytes": nb,
+            "flops": nf,
+            "GBps": nb / (ms * 1e-3) / 1e9,
+            "TFLOPs": nf / (ms * 1e-3) / 1e12,
+            "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_frac": nf / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        }
+    return calls, out
+
+
+def cpu_baseline(min_seconds=10.0):
+    """The oracle (as it stands) on the decode step, repeated for >= min_seconds."""
+    import oracle
+    import synth
+    ps = [synth.decode(M) for M in (1, 4, 16)]
+    step_bytes = sum(dense_bytes(p.M, p.K, p.N, True) for p in ps)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for p in ps:
+            oracle.w4a16(p.x, p.w, p.scale, p.zero, p.M, p.K, p.N, p.dtype)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": step_bytes * n / el / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": el,
+            "sample": f"{n} full decode steps (M=1,4,16; K=4096, N=14336) in fp64, OpenMP"}
+
+
+def load_traffic(kernel_key):
+    """HBM traffic per launch from committed rocprofv3 counter runs, or None if
+    missing or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    e = d.get(kernel_key)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=["decode", "tiny", "prefill", "msd", "moe"], default=None,
+                    help="run only this workload (profiling); no JSON headline unless decode")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the per-config extras")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is a design note only).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.copy_mb:
+        a = torch.empty(args.copy_mb * 2 ** 20 // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch_read": a.numel() * 4, "write": b.numel() * 4,
+                          "launches": args.steps}))
+        return
+
+    builders = {"decode": decode_workload, "tiny": tiny_workload, "prefill": prefill_workload,
+                "msd": msd_workload, "moe": moe_workload}
+    if args.only and args.only != "decode":
+        _, out = measure(args.only, builders[args.only], args.steps, args.warmup)
+        print(json.dumps({"workload": args.only, **out}), flush=True)
+        return
+
+    print("[bench] decode workload", file=sys.stderr, flush=True)
+    calls, dec = measure("decode", decode_workload, args.steps, args.warmup)
+    ms_step = dec["ms_per_step"]
+    step_bytes = sum(c[2] for c in calls)
+    launch_ms = sum(v["event_ms"] for v in dec["calls"].values())
+    achieved = step_bytes / (launch_ms * 1e-3) / 1e9
+    traffic = load_traffic("gemm_small_kernel")
+
+    extra = {}
+    if not args.no_extra and not args.only:
+        for name in ("tiny", "prefill", "msd", "moe"):
+            print(f"[bench] {name} workload", file=sys.stderr, flush=True)
+            _, extra[name] = measure(name, builders[name], max(10, args.steps // 2), args.warmup)
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": METRIC,
+        "value": step_bytes / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode W4A16 g128: M in {1,4,16}, K=4096, N=14336, bf16 x, uint4 weights "
+                        "+ uint4 zero points, bf16 scales (one step = the three GEMM calls)",
+            "weight_buffers_rotated": dec["rotated_sets"],
+            "tflops": dec["TFLOPs"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gemm_small_kernel<bf16, zero, NB=2, W=8>",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "per_launch_ms": {k: v["event_ms"] for k, v in dec["calls"].items()},
+        },
+        "cpu_baseline": cpu,
+        "per_config": extra,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -35,6 +35,13 @@ w4a16_status w4a16_test_msd_intermediates(const void *x, const void *w_packed, i
  */
 int w4a16_test_force_variant(int variant);
 
+/*
+ * Select the (column blocks, groups per wave) configuration of the small-M
+ * kernel for subsequent calls: idx in [0, count), or -1 for the default.
+ * Tuning only; not thread-safe.  Returns the number of configurations.
+ */
+int w4a16_test_small_config(int idx);
+
 /* Name of the kernel variant the dispatcher picks for a dense call. */
 const char *w4a16_test_variant_name(int64_t M, int64_t K, int64_t N, int dt, int has_zero);
 

@@ -45,6 +45,7 @@ _SIGS = {
     "w4a16_test_msd_intermediates": ([_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, C.c_size_t, _p], C.c_int),
     "w4a16_test_force_variant": ([C.c_int], C.c_int),
     "w4a16_test_variant_name": ([_i64, _i64, _i64, C.c_int, C.c_int], C.c_char_p),
+    "w4a16_test_small_config": ([C.c_int], C.c_int),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -140,3 +141,7 @@ def w4a16_test_force_variant(variant: int) -> int:
 
 def w4a16_test_variant_name(M, K, N, dt, has_zero) -> str:
     return lib().w4a16_test_variant_name(M, K, N, int(dt), int(has_zero)).decode()
+
+
+def w4a16_test_small_config(idx: int) -> int:
+    return lib().w4a16_test_small_config(int(idx))

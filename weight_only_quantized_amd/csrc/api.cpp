@@ -53,11 +53,12 @@ w4a16_status check_kn(int64_t K, int64_t N, int64_t group_size) {
 
 // Dense dispatch table: decode-sized M goes to the split-K kernel, the rest to
 // the LDS-staged tile kernel.
-int pick_variant(int64_t M) {
+int pick_variant(int64_t M, int64_t K) {
+    const bool small_ok = M <= 16 && K <= w4::small_max_k();
     const int forced = g_force_variant.load(std::memory_order_relaxed);
-    if (forced == 1 && M <= 16) return 1;
+    if (forced == 1 && small_ok) return 1;
     if (forced == 2) return 2;
-    return M <= 16 ? 1 : 2;
+    return small_ok ? 1 : 2;
 }
 
 }  // namespace
@@ -105,7 +106,7 @@ w4a16_status w4a16_gemm(const void *x, const void *w_packed, const void *scale, 
         return W4A16_ERR_ALIGN;
     if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
     hipStream_t s = (hipStream_t)stream;
-    if (pick_variant(M) == 1) return map_err(w4::launch_gemm_small(x, w_packed, scale, zero, y, M, K, N, dt, s));
+    if (pick_variant(M, K) == 1) return map_err(w4::launch_gemm_small(x, w_packed, scale, zero, y, M, K, N, dt, s));
     return map_err(w4::launch_gemm_tile(x, nullptr, w_packed, scale, zero, y, M, K, N, 1, dt, s));
 }
 
@@ -178,8 +179,13 @@ w4a16_status w4a16_test_msd_intermediates(const void *x, const void *w_packed, i
 int w4a16_test_force_variant(int variant) { return g_force_variant.exchange(variant); }
 
 const char *w4a16_test_variant_name(int64_t M, int64_t K, int64_t N, int dt, int has_zero) {
-    (void)K; (void)N; (void)dt; (void)has_zero;
-    return pick_variant(M) == 1 ? "gemm_small_kernel<NB=2,W=8>" : "gemm_tile_kernel<BM=128,BN=256,WM=2,WN=4>";
+    (void)N; (void)dt; (void)has_zero;
+    return pick_variant(M, K) == 1 ? "gemm_small_kernel" : "gemm_tile_kernel";
+}
+
+int w4a16_test_small_config(int idx) {
+    w4::set_small_config(idx);
+    return w4::small_config_count();
 }
 
 }  // extern "C"

@@ -64,59 +64,96 @@ __device__ __forceinline__ uint16_t f2h(float v) {
 
 // ---------------------------------------------------------------------------
 // Matrix-core wrappers.  Operands are passed as four 32-bit registers.
+//
+// The destination of a matrix-core instruction must not share registers with
+// its A or B operand: the result registers are written while later passes
+// still read the sources.  The register allocator does not enforce this when
+// A/B die at the instruction (it happily reuses them for the result when the
+// accumulator input is a constant), so every wrapper keeps A and B alive
+// until after the instruction with an empty asm use (no code is emitted).
 // ---------------------------------------------------------------------------
+template <typename R, typename A, typename B>
+__device__ __forceinline__ void keep_live(R &r, const A &a, const B &b) {
+    asm volatile("" : "+v"(r) : "v"(a), "v"(b));
+}
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t &a, const u32x4_t &b, const f32x4_t &c) {
+    f32x4_t r;
     if constexpr (DT == DT_BF16)
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                      __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+        r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     else
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                     __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+        r = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    keep_live(r, a, b);
+    return r;
 }
 
 template <int DT>
 __device__ __forceinline__ f32x16_t mfma32x32x16(const u32x4_t &a, const u32x4_t &b, const f32x16_t &c) {
+    f32x16_t r;
     if constexpr (DT == DT_BF16)
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                      __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+        r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     else
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                                     __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+        r = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    keep_live(r, a, b);
+    return r;
+}
+
+typedef short s16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
+typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+// 16x16x16 bf16 step with 2-register operands (4 bf16 per lane: lane l feeds
+// row/column l % 16, k-block l / 16; result layout as for 16x16x32).
+__device__ __forceinline__ f32x4_t mfma16x16x16_bf16(const u32x2_t &a, const u32x2_t &b, const f32x4_t &c) {
+    f32x4_t r = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                                __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+    keep_live(r, a, b);
+    return r;
 }
 
 __device__ __forceinline__ i32x4_t mfma_i8_16x16x64(const u32x4_t &a, const u32x4_t &b, const i32x4_t &c) {
-    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
-                                                __builtin_bit_cast(i32x4_t, b), c, 0, 0, 0);
+    i32x4_t r = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
+                                                            __builtin_bit_cast(i32x4_t, b), c, 0, 0, 0);
+    keep_live(r, a, b);
+    return r;
 }
 
 // ---------------------------------------------------------------------------
 // In-register dequantization of one prepacked word (8 codes) into the 16-bit
 // operand of one 16-k matrix-core step.
 //
-// bf16: the exponent pattern 0x4300 (= 128.0) with the code in the 7 mantissa
-//       bits gives exactly 128 + v.  The bias (128 + z) is removed inside the
-//       matrix core by an extra correction step (see kernels), so the operand
-//       costs one shift and one and-or per pair.
-// fp16: 0x6400 (= 1024.0) | v gives 1024 + v; one packed fp16 add of
-//       -(1024 + z) gives the exact integer v - z.
+// bf16: a 16-bit pattern with high byte 0x43 and the code in the low byte is
+//       exactly 128 + v (exponent of 128, code in the 7 mantissa bits).  The
+//       bias (128 + z) is removed inside the matrix core by an extra
+//       correction step (see the kernels).
+// fp16: high byte 0x64 and the code in the low byte is 1024 + v; one packed
+//       fp16 add of -(1024 + z) gives the exact integer v - z.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kMagicBf16 = 0x43004300u;   // bf16 128.0 in both halves
-constexpr uint32_t kMagicF16 = 0x64006400u;    // fp16 1024.0 in both halves
 
+// One prepacked word holds rows i = 0..7 of a chunk at bit 4*(i/2) + 16*(i%2),
+// so lo = word & 0x0F0F0F0F has rows (0, 4, 1, 5) in its bytes and
+// hi = (word >> 4) & 0x0F0F0F0F has rows (2, 6, 3, 7).  Each operand register
+// (rows 2p, 2p+1 in its low/high 16 bits) is then one v_perm_b32 that places
+// a code byte under the exponent byte of the magic number: 7 vector ALU
+// instructions per 8 weights, all visible to the compiler's hazard tracking.
 template <int DT>
 __device__ __forceinline__ u32x4_t dequant_word(uint32_t w, uint32_t negbias2) {
+    constexpr uint32_t expb = DT == DT_BF16 ? 0x43434343u : 0x64646464u;   // exponent byte of 128 / 1024
+    const uint32_t lo = w & 0x0F0F0F0Fu;
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
     u32x4_t r;
-    constexpr uint32_t magic = DT == DT_BF16 ? kMagicBf16 : kMagicF16;
-    r[0] = (w & 0x000F000Fu) | magic;
-    r[1] = ((w >> 4) & 0x000F000Fu) | magic;
-    r[2] = ((w >> 8) & 0x000F000Fu) | magic;
-    r[3] = ((w >> 12) & 0x000F000Fu) | magic;
+    // v_perm_b32 selector bytes: 0-3 pick bytes of the second source, 4-7 of the first
+    r[0] = __builtin_amdgcn_perm(expb, lo, 0x04020400u);   // rows 0, 1
+    r[1] = __builtin_amdgcn_perm(expb, hi, 0x04020400u);   // rows 2, 3
+    r[2] = __builtin_amdgcn_perm(expb, lo, 0x04030401u);   // rows 4, 5
+    r[3] = __builtin_amdgcn_perm(expb, hi, 0x04030401u);   // rows 6, 7
     if constexpr (DT == DT_F16) {
         const f16x2_t nb = as<f16x2_t>(negbias2);
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-            r[p] = __builtin_bit_cast(uint32_t, as<f16x2_t>(r[p]) + nb);
+        for (int p = 0; p < 4; ++p) r[p] = __builtin_bit_cast(uint32_t, as<f16x2_t>(r[p]) + nb);
     } else {
         (void)negbias2;
     }

@@ -14,7 +14,10 @@ hipError_t launch_prepack(const void *w, void *out, int64_t E, int64_t K, int64_
 hipError_t launch_unpack(const void *in, void *w, int64_t E, int64_t K, int64_t N, int is_signed,
                          hipStream_t stream);
 
-// Small-M split-K kernel (M <= 16).
+// Small-M split-K kernel (M <= 16, K <= small_max_k()).
+int small_config_count();
+void set_small_config(int idx);
+int64_t small_max_k();
 hipError_t launch_gemm_small(const void *x, const void *wp, const void *scale, const void *zero, void *y,
                              int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream);
 

@@ -1,18 +1,21 @@
 // gemm_small.hip — decode-sized W4A16 GEMM (M <= 16): split-K over the waves
 // of a workgroup, reduced through LDS.
 //
-// Work split: a workgroup owns NB 16-column blocks and the whole K range; wave
-// w owns the GW consecutive 128-row groups w*GW .. w*GW+GW-1, so for every
-// column block its weight tiles are GW consecutive kilobytes.  The kernel is
-// bound by HBM bandwidth, so each wave first issues every load it will need
-// (NB*GW 128-bit weight loads per lane, the scales, zero points and x rows)
-// and only then computes: the whole weight stream is in flight at once instead
-// of one group's worth per round trip.
+// Work split: a workgroup owns NB 16-column blocks and the whole K range.
+// Wave w owns the K slice of SG consecutive 128-row groups w*SG .. w*SG+SG-1
+// for every one of the NB blocks, so it loads its slice of x once (SG x 64
+// bytes per lane) and reuses it for all blocks.  Its NB*SG weight tiles
+// (1 KB each, one 128-bit load per lane) are streamed through a software
+// pipeline D tiles deep: the load of tile q+D is issued before tile q is
+// multiplied, and scheduling barriers keep the compiler from hoisting the
+// later loads, so the memory system always holds D tiles per wave while the
+// wave computes.  Every load is unconditional (clamped row / group indices):
+// a branch around a load forces a wait for all outstanding loads.
 //
 // Per group a wave dequantizes each lane's 32 nibbles in registers and runs
-// 16x16x32 matrix-core steps with x padded to 16 rows.  The per-group scale is
+// 16x16x32 matrix-core steps with x padded to 16 rows; the per-group scale is
 // applied to the fp32 group sum (exact integer weights inside the matrix
-// core), then the partial sums of the waves are added in LDS and rounded once.
+// core) and the waves' partial sums are added in LDS and rounded once.
 //
 // Matrix-core operand mapping (v_mfma_f32_16x16x32_{bf16,f16}): lane l feeds
 // row/column l % 16 and k-block l / 16.  The weight slot of lane l holds
@@ -20,11 +23,12 @@
 // for both operands.  The result register r of lane l is row 4*(l/16) + r,
 // column l % 16.
 //
-// bf16 bias removal: the operand holds 128 + v; one extra 16x16x16 step with
-// A = (hi, mid, lo) bf16 limbs of the row's group sum sum_k x[m][k] (three k
-// slots of k-block 0, zero elsewhere) and B = -(128 + z) subtracts
-// (128 + z) * sum_k x (24-bit sum, exact 16-bit products) before the scale is
-// applied.
+// bf16 bias removal: the dequantized operand is 128 + v.  Four extra steps
+// with B = -(128 + z) in every k slot add -(128 + z) * sum_k x[m][k] to the
+// accumulator (exact 16-bit products, fp32 sums), leaving sum_k x * (v - z).
+// Without zero points z = 8 for every column, so that chain is computed once
+// per group and fed as the accumulator input of every block's chain.
+// fp16 subtracts (1024 + z) exactly with a packed fp16 add instead.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -32,11 +36,12 @@ namespace w4 {
 
 constexpr int kSmallMaxWaves = 16;
 
-template <int DT, bool ZERO, int NB, int GW>
+template <int DT, bool ZERO, int NB, int SG, int D>
 __global__ void __launch_bounds__(kSmallMaxWaves * 64)
 gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp,
                   const uint16_t *__restrict__ scale, const uint8_t *__restrict__ zero,
                   uint16_t *__restrict__ y, int M, int64_t K, int64_t N) {
+    constexpr int T = NB * SG;                    // tiles per wave, ordered block-major
     const int G = (int)(K / kGroup);
     const int W = blockDim.x >> 6;
     const int lane = lane_id();
@@ -44,100 +49,92 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     const int j = lane & 15;       // row of the A operand / column of B and D
     const int kc = lane >> 4;      // 32-row chunk within a group
     const int64_t nb0 = (int64_t)blockIdx.x * NB;
-    const int g0 = wave * GW;
+    const int g0 = wave * SG;
+    const bool row_ok = j < M;
 
-    // Wave-uniform base addresses with 32-bit per-lane offsets, so every load
-    // is a scalar-base + vector-offset access without 64-bit address math.
-    // Loads are unconditional: A-operand rows >= M read row M-1 (they only feed
-    // result rows that are never stored), and a group index past the end is
-    // clamped to the last group with its scale forced to 0.
-    const int jrow = j < M ? j : M - 1;
+    // Wave-uniform bases with 32-bit per-lane offsets (scalar base + vector
+    // offset addressing, no 64-bit address math).
+    const int jrow = row_ok ? j : M - 1;
     const uint8_t *xbase = reinterpret_cast<const uint8_t *>(x);
     const uint32_t xoff = (uint32_t)((int64_t)jrow * K + 32 * kc) * 2u;
     const uint8_t *wblk = wp + nb0 * G * kTileBytes;
     const uint32_t woff = (uint32_t)lane * 16u;
+    const uint32_t zshift = (uint32_t)(j & 1) * 4u;   // nibble of this lane's column
 
-    // ---- phase 1: issue every load of this wave (x first: the in-order load
-    //      counter then never waits on weights it does not need yet) ----------
-    u32x4_t xa[GW][4];
+    // ---- x slice of this wave: A operands of every group, loaded once ---------
+    u32x4_t xa[SG][4];
 #pragma unroll
-    for (int i = 0; i < GW; ++i) {
+    for (int i = 0; i < SG; ++i) {
         const int g = g0 + i < G ? g0 + i : G - 1;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) xa[i][t] = ld128(xbase + (int64_t)g * (kGroup * 2) + xoff + 16 * t);
+        for (int t = 0; t < 4; ++t)
+            xa[i][t] = row_ok ? ld128(xbase + (int64_t)g * (kGroup * 2) + xoff + 16 * t) : u32x4_t{0, 0, 0, 0};
     }
-    u32x4_t raw[GW][NB];
-#pragma unroll
-    for (int i = 0; i < GW; ++i) {
+
+    // ---- weight tile stream ---------------------------------------------------
+    u32x4_t raw[T];
+    uint32_t sbits[T], zbyte[T];
+    auto issue = [&](int q) {
+        const int b = q / SG, i = q % SG;
         const int g = g0 + i < G ? g0 + i : G - 1;
+        raw[q] = ld128(wblk + ((int64_t)b * G + g) * kTileBytes + woff);
+        sbits[q] = scale[(int64_t)g * N + (nb0 + b) * 16 + j];
+        zbyte[q] = ZERO ? zero[(((int64_t)g * N + (nb0 + b) * 16) >> 1) + (j >> 1)] : 0u;
+    };
 #pragma unroll
-        for (int b = 0; b < NB; ++b) raw[i][b] = ld128(wblk + ((int64_t)b * G + g) * kTileBytes + woff);
-    }
-    uint32_t sbits[GW][NB], zbyte[GW][NB];
+    for (int q = 0; q < D && q < T; ++q) issue(q);
+
+    // bias chain for signed weights: identical for every block of a group
+    f32x4_t corr[SG];
+    if constexpr (DT == DT_BF16 && !ZERO) {
+        const uint32_t c2 = bf16_negbias(8) * 0x10001u;
+        const u32x4_t bc = {c2, c2, c2, c2};
 #pragma unroll
-    for (int i = 0; i < GW; ++i) {
-        const bool live = g0 + i < G;
-        const int g = live ? g0 + i : G - 1;
-        const uint16_t *srow = scale + (int64_t)g * N + nb0 * 16;
-        const uint8_t *zrow = ZERO ? zero + (((int64_t)g * N + nb0 * 16) >> 1) : nullptr;
+        for (int i = 0; i < SG; ++i) {
+            corr[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            sbits[i][b] = live ? (uint32_t)srow[b * 16 + j] : 0u;
-            zbyte[i][b] = ZERO ? (uint32_t)zrow[b * 8 + (j >> 1)] : 0u;
+            for (int t = 0; t < 4; ++t) corr[i] = mfma16x16x32<DT>(xa[i][t], bc, corr[i]);
         }
     }
 
-    // ---- phase 2: dequantize and multiply ------------------------------------
     float yacc[NB][4];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) yacc[b][r] = 0.f;
 
-    const uint32_t kc0 = kc == 0 ? 0xFFFFFFFFu : 0u;      // correction slots live in k-block 0
-    const uint32_t zshift = (uint32_t)(j & 1) * 4u;        // nibble of this lane's column
-
 #pragma unroll
-    for (int i = 0; i < GW; ++i) {
-        u32x2_t acorr = {0, 0};
+    for (int q = 0; q < T; ++q) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (q + D < T) issue(q + D);
+        __builtin_amdgcn_sched_barrier(0);
+        const int b = q / SG, i = q % SG;
+        const uint32_t z = ZERO ? __builtin_amdgcn_ubfe(zbyte[q], zshift, 4) : 8u;
+        f32x4_t acc;
+        uint32_t nb2 = 0;
         if constexpr (DT == DT_BF16) {
-            const bf16x2_t ones = as<bf16x2_t>(0x3F803F80u);
-            float ps = 0.f;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    ps = __builtin_amdgcn_fdot2_f32_bf16(as<bf16x2_t>(xa[i][t][p]), ones, ps, false);
-            ps += __shfl_xor(ps, 16);
-            ps += __shfl_xor(ps, 32);
-            uint32_t hi, mid, lo;
-            split3_bf16(ps, hi, mid, lo);
-            acorr[0] = (hi | (mid << 16)) & kc0;
-            acorr[1] = lo & kc0;
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const uint32_t z = ZERO ? __builtin_amdgcn_ubfe(zbyte[i][b], zshift, 4) : 8u;
-            f32x4_t acc;
-            uint32_t nb2 = 0;
-            if constexpr (DT == DT_BF16) {
-                // lanes outside k-block 0 carry A = 0, so B needs no masking
-                const uint32_t c = bf16_negbias(z);
-                const u32x2_t bcorr = {c | (c << 16), c};
-                acc = mfma16x16x16_bf16(acorr, bcorr, f32x4_t{0.f, 0.f, 0.f, 0.f});
-            } else {
-                nb2 = f16_negbias2(z);
+            if constexpr (ZERO) {
+                const uint32_t c2 = bf16_negbias(z) * 0x10001u;
+                const u32x4_t bc = {c2, c2, c2, c2};
                 acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc = mfma16x16x32<DT>(xa[i][t], bc, acc);
+            } else {
+                acc = corr[i];
             }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc = mfma16x16x32<DT>(xa[i][t], dequant_word<DT>(raw[i][b][t], nb2), acc);
-            const float sv = h2f<DT>((uint16_t)sbits[i][b]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) yacc[b][r] += sv * acc[r];
+        } else {
+            nb2 = f16_negbias2(z);
+            acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc = mfma16x16x32<DT>(xa[i][t], dequant_word<DT>(raw[q][t], nb2), acc);
+        // groups past the end (G not a multiple of SG) contribute nothing
+        const float sv = g0 + i < G ? h2f<DT>((uint16_t)sbits[q]) : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[b][r] += sv * acc[r];
     }
 
-    // ---- phase 3: reduce the waves' partial sums -------------------------------
+    // ---- reduce the waves' partial sums ---------------------------------------
     __shared__ float red[kSmallMaxWaves][NB][16][17];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -155,23 +152,24 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     }
 }
 
-// Variant table for the small-M kernel: (NB, GW).  Index 0 is the default;
+// Variant table for the small-M kernel: (NB, SG, D).  Index 0 is the default;
 // the others are kept for tuning through the test hook.
-struct SmallCfg { int nb, gw; };
-static constexpr SmallCfg kSmallCfgs[] = {{2, 4}, {1, 4}, {4, 4}, {1, 2}, {2, 2}, {4, 2}, {1, 8}, {2, 8}};
+struct SmallCfg { int nb, sg, d; };
+static constexpr SmallCfg kSmallCfgs[] = {{4, 2, 4}, {4, 2, 2}, {4, 4, 4}, {2, 2, 4}, {2, 4, 4},
+                                          {8, 2, 4}, {1, 2, 2}, {1, 4, 4}};
 static int g_small_cfg = -1;     // -1: automatic
 
 int small_config_count() { return (int)(sizeof(kSmallCfgs) / sizeof(kSmallCfgs[0])); }
 void set_small_config(int idx) { g_small_cfg = idx; }
 int64_t small_max_k() { return (int64_t)kSmallMaxWaves * 8 * kGroup; }
 
-template <int DT, bool ZERO, int NB, int GW>
+template <int DT, bool ZERO, int NB, int SG, int D>
 static hipError_t small_launch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
                                int64_t M, int64_t K, int64_t N, hipStream_t stream) {
     const int64_t G = K / kGroup;
-    const int64_t waves = (G + GW - 1) / GW;
+    const int64_t waves = (G + SG - 1) / SG;
     const dim3 grid((unsigned)(N / (16 * NB)));
-    hipLaunchKernelGGL((gemm_small_kernel<DT, ZERO, NB, GW>), grid, dim3((unsigned)(waves * 64)), 0, stream,
+    hipLaunchKernelGGL((gemm_small_kernel<DT, ZERO, NB, SG, D>), grid, dim3((unsigned)(waves * 64)), 0, stream,
                        (const uint16_t *)x, (const uint8_t *)wp, (const uint16_t *)scale,
                        (const uint8_t *)zero, (uint16_t *)y, (int)M, K, N);
     return hipGetLastError();
@@ -184,16 +182,18 @@ static hipError_t small_dispatch(const void *x, const void *wp, const void *scal
     int idx = g_small_cfg;
     if (idx < 0 || idx >= small_config_count()) idx = 0;
     SmallCfg c = kSmallCfgs[idx];
-    // at most 16 waves per workgroup: widen the per-wave group count for long K
-    while ((G + c.gw - 1) / c.gw > kSmallMaxWaves && c.gw < 8) c.gw *= 2;
-    if (c.gw == 8 && c.nb > 2) c.nb = 2;
-    if ((G + c.gw - 1) / c.gw > kSmallMaxWaves) return hipErrorInvalidValue;  // K > small_max_k()
-#define W4_SMALL(NBV, GWV)                                                                    \
-    if (c.nb == NBV && c.gw == GWV)                                                           \
-        return small_launch<DT, ZERO, NBV, GWV>(x, wp, scale, zero, y, M, K, N, stream);
-    W4_SMALL(1, 2) W4_SMALL(2, 2) W4_SMALL(4, 2)
-    W4_SMALL(1, 4) W4_SMALL(2, 4) W4_SMALL(4, 4)
-    W4_SMALL(1, 8) W4_SMALL(2, 8)
+    // at most 16 waves per workgroup: widen the per-wave slice for long K
+    while ((G + c.sg - 1) / c.sg > kSmallMaxWaves && c.sg < 8) c.sg *= 2;
+    if ((G + c.sg - 1) / c.sg > kSmallMaxWaves) return hipErrorInvalidValue;   // K > small_max_k()
+    if (c.sg == 8) { c.nb = c.nb > 2 ? 2 : c.nb; c.d = 4; }
+    // N must be a multiple of 16*NB (N % 64 == 0 always allows NB <= 4)
+    while ((N / 16) % c.nb != 0) c.nb /= 2;
+#define W4_SMALL(NBV, SGV, DV)                                                                  \
+    if (c.nb == NBV && c.sg == SGV && c.d == DV)                                                \
+        return small_launch<DT, ZERO, NBV, SGV, DV>(x, wp, scale, zero, y, M, K, N, stream);
+    W4_SMALL(4, 2, 4) W4_SMALL(4, 2, 2) W4_SMALL(4, 4, 4) W4_SMALL(2, 2, 4) W4_SMALL(2, 4, 4)
+    W4_SMALL(8, 2, 4) W4_SMALL(1, 2, 2) W4_SMALL(1, 4, 4) W4_SMALL(4, 8, 4) W4_SMALL(2, 8, 4)
+    W4_SMALL(1, 8, 4) W4_SMALL(2, 2, 2) W4_SMALL(4, 4, 2) W4_SMALL(2, 4, 2) W4_SMALL(1, 4, 2)
 #undef W4_SMALL
     return hipErrorInvalidValue;
 }

@@ -155,13 +155,13 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
 // Variant table for the small-M kernel: (NB, SG, D).  Index 0 is the default;
 // the others are kept for tuning through the test hook.
 struct SmallCfg { int nb, sg, d; };
-static constexpr SmallCfg kSmallCfgs[] = {{4, 2, 4}, {4, 2, 2}, {4, 4, 4}, {2, 2, 4}, {2, 4, 4},
-                                          {8, 2, 4}, {1, 2, 2}, {1, 4, 4}};
+static constexpr SmallCfg kSmallCfgs[] = {{4, 2, 4}, {4, 2, 2}, {2, 4, 4}, {2, 2, 4}, {8, 2, 4},
+                                          {1, 2, 2}, {1, 4, 4}, {8, 1, 4}};
 static int g_small_cfg = -1;     // -1: automatic
 
 int small_config_count() { return (int)(sizeof(kSmallCfgs) / sizeof(kSmallCfgs[0])); }
 void set_small_config(int idx) { g_small_cfg = idx; }
-int64_t small_max_k() { return (int64_t)kSmallMaxWaves * 8 * kGroup; }
+int64_t small_max_k() { return (int64_t)kSmallMaxWaves * 4 * kGroup; }
 
 template <int DT, bool ZERO, int NB, int SG, int D>
 static hipError_t small_launch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
@@ -182,18 +182,19 @@ static hipError_t small_dispatch(const void *x, const void *wp, const void *scal
     int idx = g_small_cfg;
     if (idx < 0 || idx >= small_config_count()) idx = 0;
     SmallCfg c = kSmallCfgs[idx];
-    // at most 16 waves per workgroup: widen the per-wave slice for long K
-    while ((G + c.sg - 1) / c.sg > kSmallMaxWaves && c.sg < 8) c.sg *= 2;
+    // at most 16 waves per workgroup: widen the per-wave slice for long K, and
+    // keep NB * SG <= 8 so the tile pipeline and x slice fit in registers
+    while ((G + c.sg - 1) / c.sg > kSmallMaxWaves && c.sg < 4) c.sg *= 2;
     if ((G + c.sg - 1) / c.sg > kSmallMaxWaves) return hipErrorInvalidValue;   // K > small_max_k()
-    if (c.sg == 8) { c.nb = c.nb > 2 ? 2 : c.nb; c.d = 4; }
+    while (c.nb * c.sg > 8) c.nb /= 2;
     // N must be a multiple of 16*NB (N % 64 == 0 always allows NB <= 4)
     while ((N / 16) % c.nb != 0) c.nb /= 2;
 #define W4_SMALL(NBV, SGV, DV)                                                                  \
     if (c.nb == NBV && c.sg == SGV && c.d == DV)                                                \
         return small_launch<DT, ZERO, NBV, SGV, DV>(x, wp, scale, zero, y, M, K, N, stream);
-    W4_SMALL(4, 2, 4) W4_SMALL(4, 2, 2) W4_SMALL(4, 4, 4) W4_SMALL(2, 2, 4) W4_SMALL(2, 4, 4)
-    W4_SMALL(8, 2, 4) W4_SMALL(1, 2, 2) W4_SMALL(1, 4, 4) W4_SMALL(4, 8, 4) W4_SMALL(2, 8, 4)
-    W4_SMALL(1, 8, 4) W4_SMALL(2, 2, 2) W4_SMALL(4, 4, 2) W4_SMALL(2, 4, 2) W4_SMALL(1, 4, 2)
+    W4_SMALL(4, 2, 4) W4_SMALL(4, 2, 2) W4_SMALL(2, 2, 4) W4_SMALL(2, 4, 4) W4_SMALL(8, 2, 4)
+    W4_SMALL(1, 2, 2) W4_SMALL(1, 4, 4) W4_SMALL(2, 2, 2) W4_SMALL(2, 4, 2) W4_SMALL(1, 4, 2)
+    W4_SMALL(1, 2, 4) W4_SMALL(4, 1, 4) W4_SMALL(2, 1, 4) W4_SMALL(1, 1, 4) W4_SMALL(8, 1, 4)
 #undef W4_SMALL
     return hipErrorInvalidValue;
 }

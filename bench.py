@@ -367,7 +367,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemm_small_kernel<bf16, zero, NB=2, W=8>",
+            "kernel": "gemm_small_kernel<bf16, zero, NB=4, SG=2, D=4>",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -9,7 +9,10 @@ more than 600 MB of distinct copies so the 256 MB Infinity Cache cannot hold
 them: every step streams its weights from HBM.
 
 value    = algorithmic bytes of K steps / wall time of the K steps
-           (synchronized on both sides) -> GB/s.
+           (synchronized on both sides) -> GB/s.  The K steps are launched
+           from one captured HIP graph (a decode loop is launch-bound when
+           each call goes through Python: a call costs more host time than
+           the kernel takes on the GPU).
 roofline = the dominant kernel (the small-M split-K kernel): algorithmic
            bytes per launch / its average launch duration, timed with HIP
            events on the launch stream, against the 8 TB/s HBM peak.
@@ -188,36 +191,55 @@ def moe_workload():
 # timing
 # ---------------------------------------------------------------------------
 
+def _capture(calls, first, count):
+    """One HIP graph holding `count` steps (every call once per step, buffer set
+    first + i for step i), captured on a side stream.  Replaying it launches the
+    kernels back to back with no host work in between, as a serving loop that
+    captures its decode step would."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            for _, launch, _, _ in calls:
+                launch(first + i)
+    return g
+
+
 def run_steps(calls, steps, warmup):
-    """Wall time of `steps` steps (each = every call once), synchronized."""
+    """Wall time of exactly `steps` steps, synchronized on both sides.
+
+    Warmup: `warmup` eager steps, then the same `warmup` steps replayed from a
+    graph of their own (loads the graph path).  Timed: one replay of a graph
+    holding the `steps` steps."""
     import torch
     for i in range(warmup):
         for _, launch, _, _ in calls:
             launch(i)
     torch.cuda.synchronize()
+    gw = _capture(calls, 0, max(warmup, 1))
+    g = _capture(calls, warmup, steps)
+    gw.replay()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        for _, launch, _, _ in calls:
-            launch(warmup + i)
+    g.replay()
     torch.cuda.synchronize()
     return time.perf_counter() - t0
 
 
 def per_launch_ms(calls, steps, warmup):
-    """Average duration of each call: `steps` back-to-back launches of that one
-    call between two HIP events on the launch stream (torch's current stream).
-    Back-to-back launches on one stream leave no measurable gap, so this is the
-    kernel time without the per-event overhead of timing single launches."""
+    """Average duration of each call: a graph of `steps` back-to-back launches of
+    that one call (rotating buffer sets), replayed once to warm up and once
+    between two HIP events on the replay stream (torch's current stream)."""
     import torch
     out = []
-    for ci, (_, launch, _, _) in enumerate(calls):
-        for i in range(warmup):
-            launch(i)
+    for ci in range(len(calls)):
+        one = [calls[ci]]
+        g = _capture(one, warmup, steps)
+        g.replay()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        for i in range(steps):
-            launch(warmup + i)
+        g.replay()
         b.record()
         torch.cuda.synchronize()
         out.append(a.elapsed_time(b) / steps)

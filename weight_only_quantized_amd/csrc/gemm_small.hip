@@ -23,12 +23,18 @@
 // for both operands.  The result register r of lane l is row 4*(l/16) + r,
 // column l % 16.
 //
-// bf16 bias removal: the dequantized operand is 128 + v.  Four extra steps
-// with B = -(128 + z) in every k slot add -(128 + z) * sum_k x[m][k] to the
-// accumulator (exact 16-bit products, fp32 sums), leaving sum_k x * (v - z).
-// Without zero points z = 8 for every column, so that chain is computed once
-// per group and fed as the accumulator input of every block's chain.
-// fp16 subtracts (1024 + z) exactly with a packed fp16 add instead.
+// bf16 bias removal: the dequantized operand is 128 + v.  Per group, four
+// extra steps with B = 1.0 in every slot give the row sums S of x; each tile
+// then adds -(128 + z) * S with one fused multiply-add per result register,
+// leaving sum_k x * (v - z).  Without zero points z = 8 for every column, so
+// the four extra steps use B = -136 and their result is the accumulator
+// input of every block's chain.  fp16 subtracts (1024 + z) exactly with a
+// packed fp16 add instead.
+//
+// Scales and zero points are fetched once per group for all NB blocks (one
+// 16-bit and one 8-bit load per lane) and handed to the lanes that use them
+// with a cross-lane permute; per tile a wave then issues a single memory
+// instruction, the 128-bit weight load.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -41,6 +47,7 @@ __global__ void __launch_bounds__(kSmallMaxWaves * 64)
 gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp,
                   const uint16_t *__restrict__ scale, const uint8_t *__restrict__ zero,
                   uint16_t *__restrict__ y, int M, int64_t K, int64_t N) {
+    static_assert(NB == 1 || NB == 2 || NB == 4, "one 64-lane load covers the scales of <= 4 blocks");
     constexpr int T = NB * SG;                    // tiles per wave, ordered block-major
     const int G = (int)(K / kGroup);
     const int W = blockDim.x >> 6;
@@ -50,16 +57,15 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     const int kc = lane >> 4;      // 32-row chunk within a group
     const int64_t nb0 = (int64_t)blockIdx.x * NB;
     const int g0 = wave * SG;
-    const bool row_ok = j < M;
 
-    // Wave-uniform bases with 32-bit per-lane offsets (scalar base + vector
-    // offset addressing, no 64-bit address math).
-    const int jrow = row_ok ? j : M - 1;
+    // Rows >= M read row M - 1 (in bounds, finite): the matrix core keeps rows
+    // apart, and those result rows are never stored.  No branch around the
+    // loads, so no wait for every outstanding load.
+    const int jrow = j < M ? j : M - 1;
     const uint8_t *xbase = reinterpret_cast<const uint8_t *>(x);
     const uint32_t xoff = (uint32_t)((int64_t)jrow * K + 32 * kc) * 2u;
     const uint8_t *wblk = wp + nb0 * G * kTileBytes;
     const uint32_t woff = (uint32_t)lane * 16u;
-    const uint32_t zshift = (uint32_t)(j & 1) * 4u;   // nibble of this lane's column
 
     // ---- x slice of this wave: A operands of every group, loaded once ---------
     u32x4_t xa[SG][4];
@@ -67,27 +73,43 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     for (int i = 0; i < SG; ++i) {
         const int g = g0 + i < G ? g0 + i : G - 1;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            xa[i][t] = row_ok ? ld128(xbase + (int64_t)g * (kGroup * 2) + xoff + 16 * t) : u32x4_t{0, 0, 0, 0};
+        for (int t = 0; t < 4; ++t) xa[i][t] = ld128(xbase + (int64_t)g * (kGroup * 2) + xoff + 16 * t);
+    }
+
+    // ---- scales and zero points: one load per group for all NB blocks -------
+    // Lane l fetches column 16*nb0 + l % (16*NB) and keeps scale | zero << 16;
+    // the lane that multiplies block b fetches it from lane 16*b + j with a
+    // cross-lane permute (no memory access) when the tile is reached.
+    uint32_t sz[SG];
+    {
+        const int cl = lane & (16 * NB - 1);
+        const int64_t col = nb0 * 16 + cl;
+#pragma unroll
+        for (int i = 0; i < SG; ++i) {
+            const int g = g0 + i < G ? g0 + i : G - 1;
+            uint32_t v = scale[(int64_t)g * N + col];
+            if constexpr (ZERO) v |= __builtin_amdgcn_ubfe(zero[((int64_t)g * N + col) >> 1], (uint32_t)(cl & 1) * 4u, 4) << 16;
+            sz[i] = v;
+        }
     }
 
     // ---- weight tile stream ---------------------------------------------------
     u32x4_t raw[T];
-    uint32_t sbits[T], zbyte[T];
     auto issue = [&](int q) {
         const int b = q / SG, i = q % SG;
         const int g = g0 + i < G ? g0 + i : G - 1;
         raw[q] = ld128(wblk + ((int64_t)b * G + g) * kTileBytes + woff);
-        sbits[q] = scale[(int64_t)g * N + (nb0 + b) * 16 + j];
-        zbyte[q] = ZERO ? zero[(((int64_t)g * N + (nb0 + b) * 16) >> 1) + (j >> 1)] : 0u;
     };
 #pragma unroll
     for (int q = 0; q < D && q < T; ++q) issue(q);
 
-    // bias chain for signed weights: identical for every block of a group
+    // bf16: per group either the bias chain of signed weights (-136 * row sum,
+    // the same for every block, used as accumulator input) or, with zero
+    // points, the row sums of x (B = 1.0 in every slot) that each tile scales
+    // by its column's -(128 + z).
     f32x4_t corr[SG];
-    if constexpr (DT == DT_BF16 && !ZERO) {
-        const uint32_t c2 = bf16_negbias(8) * 0x10001u;
+    if constexpr (DT == DT_BF16) {
+        const uint32_t c2 = ZERO ? 0x3F803F80u : bf16_negbias(8) * 0x10001u;
         const u32x4_t bc = {c2, c2, c2, c2};
 #pragma unroll
         for (int i = 0; i < SG; ++i) {
@@ -109,27 +131,25 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
         if (q + D < T) issue(q + D);
         __builtin_amdgcn_sched_barrier(0);
         const int b = q / SG, i = q % SG;
-        const uint32_t z = ZERO ? __builtin_amdgcn_ubfe(zbyte[q], zshift, 4) : 8u;
+        const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * b + j) << 2, (int)sz[i]);
+        const uint32_t z = ZERO ? v >> 16 : 8u;
         f32x4_t acc;
         uint32_t nb2 = 0;
-        if constexpr (DT == DT_BF16) {
-            if constexpr (ZERO) {
-                const uint32_t c2 = bf16_negbias(z) * 0x10001u;
-                const u32x4_t bc = {c2, c2, c2, c2};
-                acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int t = 0; t < 4; ++t) acc = mfma16x16x32<DT>(xa[i][t], bc, acc);
-            } else {
-                acc = corr[i];
-            }
+        if constexpr (DT == DT_BF16 && !ZERO) {
+            acc = corr[i];
         } else {
-            nb2 = f16_negbias2(z);
             acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if constexpr (DT == DT_F16) nb2 = f16_negbias2(z);
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc = mfma16x16x32<DT>(xa[i][t], dequant_word<DT>(raw[q][t], nb2), acc);
+        if constexpr (DT == DT_BF16 && ZERO) {
+            const float nbias = -(float)(128u + z);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(nbias, corr[i][r], acc[r]);
+        }
         // groups past the end (G not a multiple of SG) contribute nothing
-        const float sv = g0 + i < G ? h2f<DT>((uint16_t)sbits[q]) : 0.f;
+        const float sv = g0 + i < G ? h2f<DT>((uint16_t)(v & 0xFFFFu)) : 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) yacc[b][r] += sv * acc[r];
     }
@@ -152,11 +172,12 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     }
 }
 
-// Variant table for the small-M kernel: (NB, SG, D).  Index 0 is the default;
-// the others are kept for tuning through the test hook.
+// Variant table for the small-M kernel: (NB, SG, D).  Index 0 is the default
+// for M <= 4, index 1 (every tile of a wave in flight at once) for M > 4; the
+// others are kept for tuning through the test hook.
 struct SmallCfg { int nb, sg, d; };
-static constexpr SmallCfg kSmallCfgs[] = {{4, 2, 4}, {4, 2, 2}, {2, 4, 4}, {2, 2, 4}, {8, 2, 4},
-                                          {1, 2, 2}, {1, 4, 4}, {8, 1, 4}};
+static constexpr SmallCfg kSmallCfgs[] = {{4, 2, 4}, {4, 2, 8}, {4, 2, 2}, {2, 4, 4}, {2, 2, 4},
+                                          {1, 2, 2}, {1, 4, 4}, {4, 1, 4}};
 static int g_small_cfg = -1;     // -1: automatic
 
 int small_config_count() { return (int)(sizeof(kSmallCfgs) / sizeof(kSmallCfgs[0])); }
@@ -180,21 +201,25 @@ static hipError_t small_dispatch(const void *x, const void *wp, const void *scal
                                  int64_t M, int64_t K, int64_t N, hipStream_t stream) {
     const int64_t G = K / kGroup;
     int idx = g_small_cfg;
-    if (idx < 0 || idx >= small_config_count()) idx = 0;
+    if (idx < 0 || idx >= small_config_count()) idx = M > 4 ? 1 : 0;
     SmallCfg c = kSmallCfgs[idx];
     // at most 16 waves per workgroup: widen the per-wave slice for long K, and
-    // keep NB * SG <= 8 so the tile pipeline and x slice fit in registers
+    // keep NB * SG <= 8 and D <= NB * SG so the tile pipeline and x slice fit
+    // in registers
     while ((G + c.sg - 1) / c.sg > kSmallMaxWaves && c.sg < 4) c.sg *= 2;
     if ((G + c.sg - 1) / c.sg > kSmallMaxWaves) return hipErrorInvalidValue;   // K > small_max_k()
     while (c.nb * c.sg > 8) c.nb /= 2;
+    if (c.d > c.nb * c.sg) c.d = c.nb * c.sg >= 4 ? 4 : 2;
     // N must be a multiple of 16*NB (N % 64 == 0 always allows NB <= 4)
     while ((N / 16) % c.nb != 0) c.nb /= 2;
 #define W4_SMALL(NBV, SGV, DV)                                                                  \
     if (c.nb == NBV && c.sg == SGV && c.d == DV)                                                \
         return small_launch<DT, ZERO, NBV, SGV, DV>(x, wp, scale, zero, y, M, K, N, stream);
-    W4_SMALL(4, 2, 4) W4_SMALL(4, 2, 2) W4_SMALL(2, 2, 4) W4_SMALL(2, 4, 4) W4_SMALL(8, 2, 4)
-    W4_SMALL(1, 2, 2) W4_SMALL(1, 4, 4) W4_SMALL(2, 2, 2) W4_SMALL(2, 4, 2) W4_SMALL(1, 4, 2)
-    W4_SMALL(1, 2, 4) W4_SMALL(4, 1, 4) W4_SMALL(2, 1, 4) W4_SMALL(1, 1, 4) W4_SMALL(8, 1, 4)
+    W4_SMALL(4, 2, 4) W4_SMALL(4, 2, 8) W4_SMALL(4, 2, 2) W4_SMALL(2, 4, 4) W4_SMALL(2, 2, 4)
+    W4_SMALL(2, 4, 8) W4_SMALL(1, 2, 2) W4_SMALL(1, 4, 4) W4_SMALL(2, 2, 2) W4_SMALL(2, 4, 2)
+    W4_SMALL(1, 4, 2) W4_SMALL(1, 2, 4) W4_SMALL(4, 1, 4) W4_SMALL(2, 1, 4) W4_SMALL(1, 1, 4)
+    W4_SMALL(1, 1, 2) W4_SMALL(2, 1, 2) W4_SMALL(4, 4, 4) W4_SMALL(4, 4, 8) W4_SMALL(2, 2, 8)
+    W4_SMALL(1, 4, 8) W4_SMALL(4, 1, 2)
 #undef W4_SMALL
     return hipErrorInvalidValue;
 }

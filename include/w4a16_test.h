@@ -42,6 +42,22 @@ int w4a16_test_force_variant(int variant);
  */
 int w4a16_test_small_config(int idx);
 
+/*
+ * Select the workgroup tile configuration (rows x columns, waves) of the
+ * tile kernel, dense and grouped, for subsequent calls: idx in [0, count),
+ * or -1 for the default.  Tuning only; not thread-safe.  Returns the number
+ * of configurations.
+ */
+int w4a16_test_tile_config(int idx);
+
+/*
+ * Select the configuration (row tiles per workgroup, column blocks per wave,
+ * waves) of the MSD product kernel for subsequent calls: idx in [0, count), or
+ * -1 for the default.  w4a16_msd_workspace_bytes() covers every configuration.
+ * Tuning only; not thread-safe.  Returns the number of configurations.
+ */
+int w4a16_test_msd_config(int idx);
+
 /* Name of the kernel variant the dispatcher picks for a dense call. */
 const char *w4a16_test_variant_name(int64_t M, int64_t K, int64_t N, int dt, int has_zero);
 

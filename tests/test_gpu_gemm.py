@@ -118,3 +118,21 @@ def test_m_zero_and_errors_leave_y_untouched():
     assert ei.value.status == 4
     torch.cuda.synchronize()
     assert np.all(to_host_u16(y) == 0x1234)
+
+
+@pytest.mark.parametrize("cfg", range(6))
+@pytest.mark.parametrize("dt,signed", [(synth.BF16, False), (synth.F16, True)])
+def test_tile_configs(orc, cfg, dt, signed):
+    """Every workgroup tile configuration of the tile kernel, dense form:
+    ragged row and column tiles."""
+    import weight_only_quantized_amd as w4
+    count = w4.w4a16_test_tile_config(-1)
+    if cfg >= count:
+        pytest.skip(f"only {count} tile configurations")
+    p = synth.make_dense(200, 512, 320, dt, signed=signed, seed=cfg,
+                         scale_range=(0.005, 0.02) if dt == synth.F16 else (0.002, 0.01))
+    w4.w4a16_test_tile_config(cfg)
+    try:
+        _run_and_check(orc, p, f"tile_cfg{cfg}", variant=2)
+    finally:
+        w4.w4a16_test_tile_config(-1)

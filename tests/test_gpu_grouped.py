@@ -43,3 +43,21 @@ def test_many_experts_over_workgroup_scan(orc):
     counts[rng.integers(0, 700, 5)] = 70
     p = synth.make_grouped(700, int(counts.sum()), 1, 128, 64, synth.BF16, counts=counts, seed=2)
     _check(orc, p, "many_experts")
+
+
+@pytest.mark.parametrize("cfg", range(6))
+@pytest.mark.parametrize("dt,signed", [(synth.BF16, True), (synth.F16, False)])
+def test_tile_configs(orc, cfg, dt, signed):
+    """Every workgroup tile configuration of the tile kernel, grouped form:
+    partial row tiles, an empty expert, a partial column tile."""
+    import weight_only_quantized_amd as w4
+    count = w4.w4a16_test_tile_config(-1)
+    if cfg >= count:
+        pytest.skip(f"only {count} tile configurations")
+    counts = [5, 0, 70, 33, 1, 129]
+    p = synth.make_grouped(len(counts), sum(counts), 1, 384, 320, dt, signed=signed, counts=counts, seed=cfg)
+    prev = w4.w4a16_test_tile_config(cfg)
+    try:
+        _check(orc, p, f"grouped_tile_cfg{cfg}")
+    finally:
+        w4.w4a16_test_tile_config(-1)

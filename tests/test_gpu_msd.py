@@ -108,3 +108,25 @@ def test_msd_workspace_errors():
     assert ei.value.status == 5
     torch.cuda.synchronize()
     assert np.all(to_host_u16(y) == 0x2222)
+
+
+@pytest.mark.parametrize("cfg", range(6))
+def test_msd_configs(orc, cfg):
+    """Every configuration of the MSD product kernel: bit-exact per-group
+    int32 products and the merged output, with ragged row and column tiles."""
+    import weight_only_quantized_amd as w4
+    count = w4.w4a16_test_msd_config(-1)
+    if cfg >= count:
+        pytest.skip(f"only {count} MSD configurations")
+    M, K, N = 70, 512, 320
+    p = synth.msd(M=M, K=K, N=N, seed=20 + cfg)
+    w4.w4a16_test_msd_config(cfg)
+    try:
+        print(f"[case] msd config {cfg} M={M} K={K} N={N}", flush=True)
+        amax, layers, yint = _intermediates(p)
+        ra = orc.msd_amax(p.x, M, K)
+        rl = orc.msd_layers(p.x, ra, M, K)
+        assert np.array_equal(yint, orc.msd_yint(rl, p.w, M, K, N))
+        _check_msd(orc, p, f"msd_cfg{cfg}")
+    finally:
+        w4.w4a16_test_msd_config(-1)

@@ -46,6 +46,8 @@ _SIGS = {
     "w4a16_test_force_variant": ([C.c_int], C.c_int),
     "w4a16_test_variant_name": ([_i64, _i64, _i64, C.c_int, C.c_int], C.c_char_p),
     "w4a16_test_small_config": ([C.c_int], C.c_int),
+    "w4a16_test_tile_config": ([C.c_int], C.c_int),
+    "w4a16_test_msd_config": ([C.c_int], C.c_int),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -145,3 +147,11 @@ def w4a16_test_variant_name(M, K, N, dt, has_zero) -> str:
 
 def w4a16_test_small_config(idx: int) -> int:
     return lib().w4a16_test_small_config(int(idx))
+
+
+def w4a16_test_tile_config(idx: int) -> int:
+    return lib().w4a16_test_tile_config(int(idx))
+
+
+def w4a16_test_msd_config(idx: int) -> int:
+    return lib().w4a16_test_msd_config(int(idx))

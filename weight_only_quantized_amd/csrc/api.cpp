@@ -113,7 +113,7 @@ w4a16_status w4a16_gemm(const void *x, const void *w_packed, const void *scale, 
 size_t w4a16_msd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
     if (check_kn(K, N, group_size) != W4A16_OK || M < 0) return 0;
     if (M == 0) return 0;
-    return w4::msd_plan(M, K, N).total;
+    return w4::msd_workspace_bytes(M, K, N);
 }
 
 w4a16_status w4a16_msd_gemm(const void *x, const void *w_packed, const void *antiquant_scale, void *y,
@@ -124,7 +124,7 @@ w4a16_status w4a16_msd_gemm(const void *x, const void *w_packed, const void *ant
     if (M < 0 || M > (int64_t(1) << 24)) return W4A16_ERR_SHAPE;
     if (M == 0) return W4A16_OK;
     if (!x || !w_packed || !antiquant_scale || !y) return W4A16_ERR_NULL;
-    if (!workspace || workspace_bytes < w4::msd_plan(M, K, N).total) return W4A16_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < w4::msd_workspace_bytes(M, K, N)) return W4A16_ERR_WORKSPACE;
     if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(antiquant_scale, 2) || !aligned(y, 16) ||
         !aligned(workspace, 16))
         return W4A16_ERR_ALIGN;
@@ -169,7 +169,7 @@ w4a16_status w4a16_test_msd_intermediates(const void *x, const void *w_packed, i
     if (st != W4A16_OK) return st;
     if (M <= 0 || M > 4096) return W4A16_ERR_SHAPE;
     if (!x || !w_packed || !amax || !layers || !yint) return W4A16_ERR_NULL;
-    if (!workspace || workspace_bytes < w4::msd_plan(M, K, N).total) return W4A16_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < w4::msd_workspace_bytes(M, K, N)) return W4A16_ERR_WORKSPACE;
     if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(workspace, 16)) return W4A16_ERR_ALIGN;
     if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
     return map_err(w4::launch_msd_intermediates(x, w_packed, M, K, N, amax, layers, yint, workspace,
@@ -186,6 +186,16 @@ const char *w4a16_test_variant_name(int64_t M, int64_t K, int64_t N, int dt, int
 int w4a16_test_small_config(int idx) {
     w4::set_small_config(idx);
     return w4::small_config_count();
+}
+
+int w4a16_test_tile_config(int idx) {
+    w4::set_tile_config(idx);
+    return w4::tile_config_count();
+}
+
+int w4a16_test_msd_config(int idx) {
+    w4::set_msd_config(idx);
+    return w4::msd_config_count();
 }
 
 }  // extern "C"

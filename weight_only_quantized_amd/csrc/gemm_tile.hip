@@ -89,23 +89,36 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
         row_end = M;
     }
     const int64_t n0 = (int64_t)blockIdx.y * BN;
-    const int64_t wcol0 = n0 + (int64_t)wn * TN;
-    const bool wave_cols = wcol0 < N;          // N % 64 == 0: a wave's columns are all in or all out
+    // A wave whose columns lie past N (N % 64 == 0, so a wave's columns are all
+    // in or all out) still runs the loop on the last columns, with every load
+    // in bounds, and stores nothing: no branch around any load in the loop.
+    const bool wave_cols = n0 + (int64_t)wn * TN < N;
+    const int64_t wcol0 = wave_cols ? n0 + (int64_t)wn * TN : N - TN;
 
     const uint16_t *sc = scale + e * (int64_t)G * N;
     const uint8_t *zp = ZERO ? zero + e * (int64_t)G * (N / 2) : nullptr;
     const uint8_t *we = wp + e * NBLK * (int64_t)G * kTileBytes;
 
     // ---- activation staging -------------------------------------------------
+    // Rows past the tile's end read the last valid row (finite data whose
+    // result rows are never stored).
     u32x4_t xr[XP];
     auto load_x = [&](int g) {
 #pragma unroll
         for (int p = 0; p < XP; ++p) {
             const int id = p * NT + tid, r = id >> 4, c16 = id & 15;
-            const int64_t grow = row0 + r;
-            if (grow < row_end) xr[p] = ld128(x + grow * K + (int64_t)g * kGroup + c16 * 8);
-            else xr[p] = u32x4_t{0, 0, 0, 0};
+            const int64_t grow = row0 + r < row_end ? row0 + r : row_end - 1;
+            xr[p] = ld128(x + grow * K + (int64_t)g * kGroup + c16 * 8);
         }
+    };
+    // Sum of a value over the 16 lanes of a row (lanes 16i .. 16i+15) with
+    // row rotations: every lane ends with the row's sum.
+    auto row16_sum = [](float v) {
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false));
+        return v;
     };
     auto store_x = [&](int buf) {
         uint8_t *base = lds + buf * BM * ROWB;
@@ -119,22 +132,18 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     ps = __builtin_amdgcn_fdot2_f32_bf16(as<bf16x2_t>(xr[p][q]), ones, ps, false);
-                ps += __shfl_xor(ps, 1);
-                ps += __shfl_xor(ps, 2);
-                ps += __shfl_xor(ps, 4);
-                ps += __shfl_xor(ps, 8);
-                if (c16 == 0) {
-                    uint32_t hi, mid, lo;
-                    split3_bf16(ps, hi, mid, lo);
-                    *reinterpret_cast<u32x4_t *>(base + r * ROWB + 256) = u32x4_t{hi | (mid << 16), lo, 0, 0};
-                } else if (c16 == 1) {
-                    *reinterpret_cast<u32x4_t *>(base + r * ROWB + 272) = u32x4_t{0, 0, 0, 0};
-                }
+                ps = row16_sum(ps);
+                uint32_t hi, mid, lo;
+                split3_bf16(ps, hi, mid, lo);
+                // lanes c16 = 0, 1 of the row write the 32-byte limb slot:
+                // {hi | mid << 16, lo, 0, 0} then zeros
+                const u32x4_t limb = c16 == 0 ? u32x4_t{hi | (mid << 16), lo, 0, 0} : u32x4_t{0, 0, 0, 0};
+                if (c16 < 2) *reinterpret_cast<u32x4_t *>(base + r * ROWB + 256 + 16 * c16) = limb;
             }
         }
     };
 
-    // ---- weight fragments ---------------------------------------------------
+    // ---- weight fragments, scales and zero points -----------------------------
     const int lj = lane & 31, kg = lane >> 5;
     int64_t boff[CT];          // byte offset of this lane's slot (chunk 2*kg) in group 0
 #pragma unroll
@@ -144,12 +153,23 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
         boff[ct] = nb * (int64_t)G * kTileBytes + ((2 * kg) * 16 + jj) * 16;
     }
     u32x4_t braw[CT][2], bnext[CT][2];
-    auto load_b = [&](int g, u32x4_t (&dst)[CT][2]) {
+    // scales and zero points stay in their loaded 16/8-bit types: a mask of
+    // the loaded value would be a use of the load, and the compiler may place
+    // it right after the prefetch (forcing a wait for every load in flight)
+    uint16_t sraw[CT], snext[CT];
+    uint8_t zraw[CT], znext[CT];
+    auto load_b = [&](int g, u32x4_t (&dst)[CT][2], uint16_t (&sdst)[CT], uint8_t (&zdst)[CT]) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             const uint8_t *p = we + boff[ct] + (int64_t)g * kTileBytes;
             dst[ct][0] = ld128(p);
             dst[ct][1] = ld128(p + 256);     // chunk 2*kg + 1: 16 slots further
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const int64_t n = wcol0 + ct * 32 + lj;
+            sdst[ct] = sc[(int64_t)g * N + n];
+            zdst[ct] = ZERO ? zp[((int64_t)g * N + n) >> 1] : (uint8_t)0;
         }
     };
 
@@ -162,85 +182,84 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
             for (int r = 0; r < 16; ++r) yacc[rt][ct][r] = 0.f;
 
     load_x(0);
+    load_b(0, braw, sraw, zraw);
     store_x(0);
-    if (wave_cols) load_b(0, braw);
     __syncthreads();
 
+    // Every step issues the loads of the next group first (the last step
+    // re-reads group G - 1: no branch, so the counters of outstanding loads
+    // stay exact and each wait covers only what is used), multiplies the
+    // current group from registers and LDS, then stages the next x slice.
+    // Two register sets for the weights, scales and zero points alternate
+    // between steps, so a prefetch is waited for only in the step that uses
+    // it (a register copy would wait for it at once).
     const int arow = wm * TM + lj;             // LDS row of this lane's A operand (row tile 0)
-    for (int g = 0; g < G; ++g) {
+    auto step = [&](int g, const u32x4_t (&bw)[CT][2], const uint16_t (&sw)[CT], const uint8_t (&zw)[CT],
+                    u32x4_t (&bn)[CT][2], uint16_t (&sn)[CT], uint8_t (&zn)[CT]) {
         const int buf = g & 1;
-        if (g + 1 < G) {
-            load_x(g + 1);
-            if (wave_cols) load_b(g + 1, bnext);
-        }
-        if (wave_cols) {
-            float s[CT];
-            uint32_t nb2[CT];
-            u32x4_t bcorr[CT];
+        const int gn = g + 1 < G ? g + 1 : g;
+        load_x(gn);
+        load_b(gn, bn, sn, zn);
+        float s[CT];
+        uint32_t nb2[CT];
+        u32x4_t bcorr[CT];
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const int64_t n = wcol0 + ct * 32 + lj;
-                s[ct] = h2f<DT>(sc[(int64_t)g * N + n]);
-                uint32_t z = 8;
-                if constexpr (ZERO) {
-                    const uint8_t zb = zp[((int64_t)g * N + n) >> 1];
-                    z = (n & 1) ? (zb >> 4) : (zb & 0xF);
-                }
-                if constexpr (CORR) {
-                    const uint32_t c = bf16_negbias(z);
-                    bcorr[ct] = kg == 0 ? u32x4_t{c | (c << 16), c, 0, 0} : u32x4_t{0, 0, 0, 0};
-                    nb2[ct] = 0;
-                } else {
-                    nb2[ct] = f16_negbias2(z);
-                }
-            }
-            const uint8_t *abase = lds + buf * BM * ROWB + arow * ROWB + kg * 128;
-            f32x16_t acc[RT][CT];
+        for (int ct = 0; ct < CT; ++ct) {
+            const int64_t n = wcol0 + ct * 32 + lj;
+            s[ct] = h2f<DT>(sw[ct]);
+            uint32_t z = 8;
+            if constexpr (ZERO) z = __builtin_amdgcn_ubfe((uint32_t)zw[ct], (uint32_t)(n & 1) * 4u, 4);
             if constexpr (CORR) {
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(
-                        lds + buf * BM * ROWB + (arow + rt * 32) * ROWB + 256 + kg * 16);
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mfma32x32x16<DT>(a, bcorr[ct], f32x16_t{});
-                }
+                const uint32_t c = bf16_negbias(z);
+                bcorr[ct] = kg == 0 ? u32x4_t{c | (c << 16), c, 0, 0} : u32x4_t{0, 0, 0, 0};
+                nb2[ct] = 0;
             } else {
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[rt][ct][r] = 0.f;
+                nb2[ct] = f16_negbias2(z);
             }
+        }
+        const uint8_t *abase = lds + buf * BM * ROWB + arow * ROWB + kg * 128;
+        f32x16_t acc[RT][CT];
+        if constexpr (CORR) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                u32x4_t a[RT], bq[CT];
+            for (int rt = 0; rt < RT; ++rt) {
+                const u32x4_t a = *reinterpret_cast<const u32x4_t *>(
+                    lds + buf * BM * ROWB + (arow + rt * 32) * ROWB + 256 + kg * 16);
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-                    a[rt] = *reinterpret_cast<const u32x4_t *>(abase + rt * 32 * ROWB + t * 16);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) bq[ct] = dequant_word<DT>(braw[ct][t >> 2][t & 3], nb2[ct]);
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], acc[rt][ct]);
+                for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mfma32x32x16<DT>(a, bcorr[ct], f32x16_t{});
             }
+        } else {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) yacc[rt][ct][r] += s[ct] * acc[rt][ct][r];
+                    for (int r = 0; r < 16; ++r) acc[rt][ct][r] = 0.f;
         }
-        if (g + 1 < G) {
-            store_x(buf ^ 1);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                braw[ct][0] = bnext[ct][0];
-                braw[ct][1] = bnext[ct][1];
-            }
+        for (int t = 0; t < 8; ++t) {
+            u32x4_t a[RT], bq[CT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                a[rt] = *reinterpret_cast<const u32x4_t *>(abase + rt * 32 * ROWB + t * 16);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) bq[ct] = dequant_word<DT>(bw[ct][t >> 2][t & 3], nb2[ct]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], acc[rt][ct]);
         }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) yacc[rt][ct][r] += s[ct] * acc[rt][ct][r];
+        store_x(buf ^ 1);
         __syncthreads();
+    };
+    for (int g = 0; g < G; g += 2) {
+        step(g, braw, sraw, zraw, bnext, snext, znext);
+        if (g + 1 < G) step(g + 1, bnext, snext, znext, braw, sraw, zraw);
     }
 
     if (!wave_cols) return;
@@ -257,17 +276,51 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
         }
 }
 
-template <int DT, bool ZERO, bool GROUPED>
-static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const void *wp, const void *scale,
-                                const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
-                                hipStream_t stream) {
-    constexpr int BM = 128, BN = 256, WM = 2, WN = 4;
+// Workgroup tile configurations (BM x BN rows x columns, WM x WN waves).
+// Index 0 is the dense default; the grouped default follows the average row
+// count per expert (small row tiles waste less of the matrix core on experts
+// with few rows).  The others are kept for tuning through the test hook.
+struct TileCfg { int bm, bn, wm, wn; };
+static constexpr TileCfg kTileCfgs[] = {{128, 256, 2, 4}, {64, 256, 2, 4}, {32, 256, 1, 4},
+                                        {64, 128, 2, 2}, {32, 128, 1, 4}, {128, 128, 2, 2}};
+static int g_tile_cfg = -1;      // -1: automatic
+
+int tile_config_count() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0])); }
+void set_tile_config(int idx) { g_tile_cfg = idx; }
+
+template <int DT, bool ZERO, bool GROUPED, int BM, int BN, int WM, int WN>
+static hipError_t tile_launch(const void *x, const int32_t *offsets, const void *wp, const void *scale,
+                              const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
+                              hipStream_t stream) {
+    // grouped: every expert may end in a partial row tile, hence + E
     const int64_t mtiles = GROUPED ? (M + BM - 1) / BM + E : (M + BM - 1) / BM;
     const dim3 grid((unsigned)mtiles, (unsigned)((N + BN - 1) / BN));
     hipLaunchKernelGGL((gemm_tile_kernel<DT, ZERO, BM, BN, WM, WN, GROUPED>), grid, dim3(WM * WN * 64), 0,
                        stream, (const uint16_t *)x, offsets, (const uint8_t *)wp, (const uint16_t *)scale,
                        (const uint8_t *)zero, (uint16_t *)y, M, K, N, (int)E);
     return hipGetLastError();
+}
+
+template <int DT, bool ZERO, bool GROUPED>
+static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const void *wp, const void *scale,
+                                const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
+                                hipStream_t stream) {
+    int idx = g_tile_cfg;
+    if (idx < 0 || idx >= tile_config_count()) {
+        idx = 0;
+        if (GROUPED) {
+            const int64_t avg = M / E;          // mean rows per expert
+            idx = avg <= 48 ? 2 : avg <= 96 ? 1 : 0;
+        }
+    }
+    const TileCfg c = kTileCfgs[idx];
+#define W4_TILE(BMV, BNV, WMV, WNV)                                                                    \
+    if (c.bm == BMV && c.bn == BNV && c.wm == WMV && c.wn == WNV)                                      \
+        return tile_launch<DT, ZERO, GROUPED, BMV, BNV, WMV, WNV>(x, offsets, wp, scale, zero, y, M, K, N, E, stream);
+    W4_TILE(128, 256, 2, 4) W4_TILE(64, 256, 2, 4) W4_TILE(32, 256, 1, 4) W4_TILE(64, 128, 2, 2)
+    W4_TILE(32, 128, 1, 4) W4_TILE(128, 128, 2, 2)
+#undef W4_TILE
+    return hipErrorInvalidValue;
 }
 
 template <bool GROUPED>

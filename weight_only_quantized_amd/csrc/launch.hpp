@@ -22,6 +22,8 @@ hipError_t launch_gemm_small(const void *x, const void *wp, const void *scale, c
                              int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream);
 
 // LDS-staged tile kernel; grouped when offsets != nullptr (then M = R rows).
+int tile_config_count();
+void set_tile_config(int idx);
 hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *wp, const void *scale,
                             const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
                             int dt, hipStream_t stream);
@@ -38,6 +40,9 @@ struct MsdPlan {
     size_t off_coef, off_amax, off_layers, off_part, total;
 };
 MsdPlan msd_plan(int64_t M, int64_t K, int64_t N);
+size_t msd_workspace_bytes(int64_t M, int64_t K, int64_t N);
+int msd_config_count();
+void set_msd_config(int idx);
 hipError_t launch_msd(const void *x, const void *wp, const void *scale, void *y, int64_t M, int64_t K,
                       int64_t N, void *workspace, hipStream_t stream);
 hipError_t launch_msd_intermediates(const void *x, const void *wp, int64_t M, int64_t K, int64_t N,

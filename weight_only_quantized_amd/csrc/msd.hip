@@ -106,27 +106,109 @@ __device__ __forceinline__ u32x4_t weight_i8(uint32_t w0, uint32_t w1) {
 }
 
 // Integer products of the three layers with the weights (eq.9) and the merge
-// (eqs.10-11).  Waves split the columns (NB 16-column blocks each); a
-// workgroup owns W*NB blocks, MT 16-row tiles of x rows and one K slice
-// (blockIdx.y).  Lane l of v_mfma_i32_16x16x64_i8 feeds row/column l % 16,
-// k-block l / 16 (32 rows of the group: prepacked chunk l / 16; step t uses its
-// words 2t and 2t+1).  Result register r of lane l is row 4*(l/16) + r,
-// column l % 16.
-template <int MT, int NB, int W, bool DUMP>
+// (eqs.10-11).
+//
+// A workgroup owns ROWS = 16*MT x rows, W*NB 16-column blocks (NB per wave)
+// and one K slice of GPS groups (blockIdx.y; the last slice may hold fewer:
+// its missing groups get zero coefficients).  The three layers of
+// its rows over the whole slice and their merge coefficients are loaded into
+// LDS once (one barrier); then every wave streams its own weight tiles with no
+// further synchronisation: the tiles of group g + 2 are fetched while group g
+// is multiplied (three register sets in a ring), every layer fragment read
+// from LDS serves the wave's NB blocks, and every load is unconditional
+// (clamped indices).  LDS rows are padded by 16 bytes so the 16 rows read by
+// one operand load fall on disjoint banks.
+//
+// Lane l of v_mfma_i32_16x16x64_i8 feeds row/column l % 16 and k-block l / 16:
+// the weight slot of lane l holds rows 32*(l/16) + 0..31 of the group, step s
+// uses its words 2s, 2s+1 (rows 32*(l/16) + 16s + 0..15) and the layer bytes
+// 32*(l/16) + 16s .. +15 of the same row order.  Result register r of lane l
+// is row 4*(l/16) + r, column l % 16.
+template <int MT> struct MsdLds {
+    static constexpr int GPSMAX = MT == 1 ? 16 : MT == 2 ? 8 : 4;     // ~100 KB of layers
+    static constexpr int ROWS = 16 * MT;
+    static constexpr int AROW = GPSMAX * kGroup + 16;                  // LDS row stride (bytes)
+};
+
+template <int MT, int NB, int W, int GPS, bool DUMP>
 __global__ void __launch_bounds__(W * 64)
 msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coef,
                 const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
                 float *__restrict__ part, uint16_t *__restrict__ y, int32_t *__restrict__ yint,
                 int64_t M, int64_t Mpad, int64_t K, int64_t N, int64_t gps) {
+    constexpr int NT = W * 64;
+    constexpr int ROWS = MsdLds<MT>::ROWS, AROW = MsdLds<MT>::AROW;
+    static_assert(GPS <= MsdLds<MT>::GPSMAX, "slice must fit in LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t sA[3 * ROWS * AROW];
+    __shared__ __attribute__((aligned(16))) float sC[GPS * 3 * ROWS];
+
     const int64_t G = K / kGroup;
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, kc = lane >> 4;
-    const int64_t nb0 = ((int64_t)blockIdx.x * W + wave) * NB;
-    const int64_t ks = blockIdx.y;
-    const int64_t m0 = (int64_t)blockIdx.z * 16 * MT;
-    const int64_t g_begin = ks * gps;
-    const int64_t g_end = g_begin + gps < G ? g_begin + gps : G;
-    if (nb0 >= N / 16) return;
+    const int64_t NBLK = N / 16;
+    const int64_t m0 = (int64_t)blockIdx.z * ROWS;
+    const int64_t g_begin = (int64_t)blockIdx.y * gps;
+    const int ng = (int)((g_begin + gps < G ? g_begin + gps : G) - g_begin);    // groups of this slice
+    // N % 64 == 0 and NB divides 4: a wave's blocks are all in or all out; a
+    // wave past the end runs on the last blocks and stores nothing
+    const int64_t nbw = ((int64_t)blockIdx.x * W + wave) * NB;
+    const bool wave_cols = nbw < NBLK;
+    const int64_t nb0 = wave_cols ? nbw : NBLK - NB;
+
+    // ---- weight tiles and scales: three register sets in a ring ----------------
+    // Wave-uniform base pointers (scalar registers) plus one fixed 32-bit lane
+    // offset: a group only moves the scalar base, so no per-group vector
+    // address is ever formed (or kept live).
+    const uint8_t *wu = wp + (nb0 * G + g_begin) * kTileBytes;
+    const uint16_t *su = scale + g_begin * N + nb0 * 16;
+    const uint32_t woff = (uint32_t)lane * 16u;
+    u32x4_t wr[3][NB];
+    uint16_t sr[3][NB];
+    auto load_w = [&](int gl, u32x4_t (&wd)[NB], uint16_t (&sd)[NB]) {   // gl: group within the slice
+        const int gc = __builtin_amdgcn_readfirstlane(gl < ng ? gl : ng - 1);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            wd[b] = ld128(wu + ((int64_t)b * G + gc) * kTileBytes + woff);
+        if constexpr (!DUMP) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) sd[b] = su[(int64_t)gc * N + b * 16 + j];
+        }
+    };
+
+    // ---- layers and coefficients of the slice into LDS ------------------------
+    // chunk c: layer l, row, 16-byte piece p of the slice's gps*128 bytes
+    {
+        // every thread issues all of its layer loads before its first LDS
+        // store (one memory round trip), after the first two groups' weights
+        load_w(0, wr[0], sr[0]);
+        load_w(1, wr[1], sr[1]);
+        constexpr int CMAX = 3 * ROWS * GPS * 8;                  // chunks of a full slice
+        constexpr int CPT = (CMAX + NT - 1) / NT;
+        const int pieces = ng * 8;
+        const int chunks = 3 * ROWS * pieces;
+        u32x4_t v[CPT];
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int c1 = u * NT + tid, c = c1 < chunks ? c1 : chunks - 1;
+            const int lr = c / pieces, pc = c % pieces;                // lr = l * ROWS + row
+            const int l = lr / ROWS, row = lr % ROWS;
+            v[u] = ld128(layers + (l * Mpad + m0 + row) * K + g_begin * kGroup + pc * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int c = u * NT + tid;
+            if (c < chunks) {
+                const int lr = c / pieces, pc = c % pieces;
+                *reinterpret_cast<u32x4_t *>(&sA[lr * AROW + pc * 16]) = v[u];
+            }
+        }
+        for (int i = tid; i < GPS * 3 * ROWS; i += NT) {
+            const int gl = i / (3 * ROWS), lr = i % (3 * ROWS);
+            sC[i] = gl < ng ? coef[((g_begin + gl) * 3 + lr / ROWS) * Mpad + m0 + lr % ROWS] : 0.f;
+        }
+    }
+    __syncthreads();
 
     float yacc[NB][MT][4];
 #pragma unroll
@@ -136,27 +218,30 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
 #pragma unroll
             for (int r = 0; r < 4; ++r) yacc[b][mt][r] = 0.f;
 
-    for (int64_t g = g_begin; g < g_end; ++g) {
+    auto step = [&](int gl, const u32x4_t (&wc)[NB], const uint16_t (&sc)[NB], u32x4_t (&wn)[NB],
+                    uint16_t (&sn)[NB]) {
+        // keep each group's code in its own scheduling region: hoisting the
+        // next groups' LDS reads would only raise register pressure
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(gl + 2, wn, sn);
         u32x4_t bop[NB][2];
         float s[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const u32x4_t raw = ld128(wp + ((nb0 + b) * G + g) * kTileBytes + lane * 16);
-            bop[b][0] = weight_i8(raw[0], raw[1]);
-            bop[b][1] = weight_i8(raw[2], raw[3]);
-            s[b] = DUMP ? 0.f : h2f<DT_F16>(scale[g * N + (nb0 + b) * 16 + j]);
+            bop[b][0] = weight_i8(wc[b][0], wc[b][1]);
+            bop[b][1] = weight_i8(wc[b][2], wc[b][3]);
+            s[b] = DUMP ? 0.f : h2f<DT_F16>(sc[b]);
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int64_t arow = m0 + 16 * mt + j;            // A-operand row (padded rows are zero)
             u32x4_t a[3][2];
             float c[3][4];
 #pragma unroll
             for (int l = 0; l < 3; ++l) {
-                const int8_t *ap = layers + (l * Mpad + arow) * K + g * kGroup + 32 * kc;
-                a[l][0] = ld128(ap);
-                a[l][1] = ld128(ap + 16);
-                const f32x4_t cv = *reinterpret_cast<const f32x4_t *>(coef + (g * 3 + l) * Mpad + m0 + 16 * mt + 4 * kc);
+                const uint8_t *ap = sA + (l * ROWS + mt * 16 + j) * AROW + gl * kGroup + 32 * kc;
+                a[l][0] = *reinterpret_cast<const u32x4_t *>(ap);
+                a[l][1] = *reinterpret_cast<const u32x4_t *>(ap + 16);
+                const f32x4_t cv = *reinterpret_cast<const f32x4_t *>(&sC[(gl * 3 + l) * ROWS + mt * 16 + 4 * kc]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) c[l][r] = cv[r];
             }
@@ -169,13 +254,16 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
                     Y[l] = mfma_i8_16x16x64(a[l][1], bop[b][1], Y[l]);
                 }
                 if constexpr (DUMP) {
+                    if (wave_cols) {
 #pragma unroll
-                    for (int l = 0; l < 3; ++l)
+                        for (int l = 0; l < 3; ++l)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int64_t row = m0 + 16 * mt + 4 * kc + r;
-                            if (row < M) yint[((g * 3 + l) * M + row) * N + (nb0 + b) * 16 + j] = Y[l][r];
-                        }
+                            for (int r = 0; r < 4; ++r) {
+                                const int64_t row = m0 + 16 * mt + 4 * kc + r;
+                                if (row < M && gl < ng)
+                                    yint[(((g_begin + gl) * 3 + l) * M + row) * N + (nb0 + b) * 16 + j] = Y[l][r];
+                            }
+                    }
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -185,10 +273,43 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
                 }
             }
         }
+        // the accumulators are consumed only by the final (conditional)
+        // stores; without this tie the compiler sinks every group's merge to
+        // those stores and keeps all products and coefficients live
+        if constexpr (!DUMP) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(yacc[b][mt][r]));
+        }
+    };
+    // fully unrolled: the ring index of every register set is static and the
+    // counters of outstanding loads stay exact (steps past a short final slice
+    // multiply zero coefficients)
+#pragma unroll
+    for (int gl = 0; gl < GPS; ++gl) {
+        if (gl % 3 == 0) step(gl, wr[0], sr[0], wr[2], sr[2]);
+        if (gl % 3 == 1) step(gl, wr[1], sr[1], wr[0], sr[0]);
+        if (gl % 3 == 2) step(gl, wr[2], sr[2], wr[1], sr[1]);
     }
-    if constexpr (DUMP) return;
 
-    const bool split = gridDim.y > 1;
+    if constexpr (DUMP) return;
+    if (!wave_cols) return;
+    if (gridDim.y > 1) {
+        // K slices: fp32 partial sums in the matrix-core result layout, one
+        // contiguous 16-byte store per lane and tile (padding rows included;
+        // their layers are zero)
+        float *ps = part + (((int64_t)blockIdx.y * gridDim.z + blockIdx.z) * NBLK + nb0) * (MT * 256);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                *reinterpret_cast<f32x4_t *>(ps + (b * MT + mt) * 256 + lane * 4) =
+                    f32x4_t{yacc[b][mt][0], yacc[b][mt][1], yacc[b][mt][2], yacc[b][mt][3]};
+        return;
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -197,25 +318,30 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
             for (int r = 0; r < 4; ++r) {
                 const int64_t row = m0 + 16 * mt + 4 * kc + r;
                 const int64_t col = (nb0 + b) * 16 + j;
-                if (row < M) {
-                    if (split) part[(ks * M + row) * N + col] = yacc[b][mt][r];
-                    else y[row * N + col] = f2h<DT_F16>(yacc[b][mt][r]);
-                }
+                if (row < M) y[row * N + col] = f2h<DT_F16>(yacc[b][mt][r]);
             }
 }
 
+// Sum of the K slices' partial sums (matrix-core result layout: per row chunk z,
+// 16-column block nb and 16-row tile mt, 64 lanes x 4 result registers) and
+// rounding to fp16.  One thread per lane and tile; slice stride `slice` floats.
 __global__ void __launch_bounds__(256)
-msd_reduce_kernel(const float *__restrict__ part, uint16_t *__restrict__ y, int64_t MN, int ksplit) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= MN) return;          // MN % 4 == 0 (N % 64 == 0)
-    f32x4_t acc = *reinterpret_cast<const f32x4_t *>(part + i);
-    for (int k = 1; k < ksplit; ++k) {
-        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(part + k * MN + i);
-        acc += v;
-    }
-    uint32_t lo = f2h<DT_F16>(acc[0]) | ((uint32_t)f2h<DT_F16>(acc[1]) << 16);
-    uint32_t hi = f2h<DT_F16>(acc[2]) | ((uint32_t)f2h<DT_F16>(acc[3]) << 16);
-    *reinterpret_cast<uint2 *>(y + i) = make_uint2(lo, hi);
+msd_reduce_kernel(const float *__restrict__ part, uint16_t *__restrict__ y, int64_t M, int64_t N, int mt_count,
+                  int64_t nlanes, int64_t slice, int ksplit) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;      // (z, nb, mt, lane)
+    if (t >= nlanes) return;
+    f32x4_t acc = *reinterpret_cast<const f32x4_t *>(part + t * 4);
+    for (int k = 1; k < ksplit; ++k) acc += *reinterpret_cast<const f32x4_t *>(part + k * slice + t * 4);
+    const int lane = (int)(t & 63);
+    const int64_t tile = t >> 6;
+    const int mt = (int)(tile % mt_count);
+    const int64_t nb = (tile / mt_count) % (N / 16);
+    const int64_t z = tile / mt_count / (N / 16);
+    const int64_t row0 = (z * mt_count + mt) * 16 + 4 * (lane >> 4);
+    const int64_t col = nb * 16 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (row0 + r < M) y[(row0 + r) * N + col] = f2h<DT_F16>(acc[r]);
 }
 
 // Plain-order copy of the layers for the test hook.
@@ -232,28 +358,59 @@ __global__ void msd_layers_plain_kernel(const int8_t *__restrict__ src, int8_t *
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-MsdPlan msd_plan(int64_t M, int64_t K, int64_t N) {
+// Configurations of msd_gemm_kernel: (16-row tiles per workgroup, column
+// blocks per wave, waves).  Index 0 is the default; the others are kept for
+// tuning through the test hook.
+struct MsdCfg { int mt, nb, waves; };
+static constexpr MsdCfg kMsdCfgs[] = {{2, 4, 8}, {2, 4, 4}, {1, 4, 8}, {4, 2, 8}, {2, 2, 8}, {4, 4, 4}};
+static int g_msd_cfg = -1;       // -1: automatic
+int msd_config_count() { return (int)(sizeof(kMsdCfgs) / sizeof(kMsdCfgs[0])); }
+void set_msd_config(int idx) { g_msd_cfg = idx; }
+
+static MsdPlan msd_plan_cfg(int64_t M, int64_t K, int64_t N, const MsdCfg &c) {
     MsdPlan p{};
     const int64_t G = K / kGroup;
-    const int64_t mrows = M < 64 ? M : 64;
-    p.mt = mrows <= 16 ? 1 : (mrows <= 32 ? 2 : 4);
+    p.mt = c.mt;
+    while (p.mt > 1 && 16 * (p.mt / 2) >= M) p.mt /= 2;      // no more row tiles than rows
     p.mchunks = (int)((M + 16 * p.mt - 1) / (16 * p.mt));
     if (p.mchunks < 1) p.mchunks = 1;
-    p.mpad = (int64_t)p.mchunks * 16 * p.mt;
-    p.nb = 2;
-    p.waves = 4;
-    const int64_t colwg = N / (16 * p.nb * p.waves) + (N % (16 * p.nb * p.waves) ? 1 : 0);
-    // aim for at least ~512 workgroups over K slices, each slice >= 4 groups
-    int64_t ks = 1;
-    while (colwg * p.mchunks * ks < 512 && G / (ks * 2) >= 4) ks *= 2;
-    p.ksplit = (int)ks;
-    p.gps = (G + ks - 1) / ks;
+    p.mpad = (M + 63) / 64 * 64;                               // layers padded for every configuration
+    if (p.mpad < 64) p.mpad = 64;
+    p.nb = c.nb;
+    p.waves = c.waves;
+    const int64_t colwg = (N / 16 + p.nb * p.waves - 1) / (p.nb * p.waves);
+    // slice length: the longest power of two that fits in LDS and still
+    // gives the grid about 2048 waves (else the shortest, 2 groups)
+    const int64_t gpsmax = p.mt == 1 ? MsdLds<1>::GPSMAX : p.mt == 2 ? MsdLds<2>::GPSMAX : MsdLds<4>::GPSMAX;
+    const int64_t target = 2048 / p.waves;
+    p.gps = 2;
+    for (int64_t g = gpsmax; g >= 2; g /= 2)
+        if (colwg * p.mchunks * ((G + g - 1) / g) >= target || g == 2) { p.gps = g; break; }
+    p.ksplit = (int)((G + p.gps - 1) / p.gps);
     p.off_coef = 0;
     p.off_amax = align_up(p.off_coef + sizeof(float) * (size_t)(G * 3 * p.mpad), 256);
     p.off_layers = align_up(p.off_amax + sizeof(float) * (size_t)(M * G), 256);
     p.off_part = align_up(p.off_layers + (size_t)(3 * p.mpad * K), 256);
-    p.total = align_up(p.off_part + (p.ksplit > 1 ? sizeof(float) * (size_t)(p.ksplit * M * N) : 0), 256);
+    const int64_t rows_cov = (int64_t)p.mchunks * 16 * p.mt;   // rows covered by the row chunks
+    p.total = align_up(p.off_part + (p.ksplit > 1 ? sizeof(float) * (size_t)(p.ksplit * rows_cov * N) : 0), 256);
     return p;
+}
+
+MsdPlan msd_plan(int64_t M, int64_t K, int64_t N) {
+    int idx = g_msd_cfg;
+    if (idx < 0 || idx >= msd_config_count()) idx = 0;
+    return msd_plan_cfg(M, K, N, kMsdCfgs[idx]);
+}
+
+size_t msd_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    // the largest plan over all configurations, so that a size queried once
+    // fits whichever configuration runs
+    size_t mx = 0;
+    for (int i = 0; i < msd_config_count(); ++i) {
+        const size_t t = msd_plan_cfg(M, K, N, kMsdCfgs[i]).total;
+        mx = t > mx ? t : mx;
+    }
+    return mx;
 }
 
 template <bool DUMP>
@@ -263,15 +420,27 @@ static hipError_t msd_gemm_launch(const MsdPlan &p, const int8_t *layers, const 
     const int64_t colwg = (N / 16 + p.nb * p.waves - 1) / (p.nb * p.waves);
     const dim3 grid((unsigned)colwg, (unsigned)ksplit, (unsigned)p.mchunks);
     const dim3 block(p.waves * 64);
-#define W4_MSD_LAUNCH(MTV)                                                                                     \
-    hipLaunchKernelGGL((msd_gemm_kernel<MTV, 2, 4, DUMP>), grid, block, 0, stream, layers, coef,                 \
-                       (const uint8_t *)wp, (const uint16_t *)scale, part, (uint16_t *)y, yint, M, p.mpad, K, N, \
-                       gps)
-    if (p.mt == 1) W4_MSD_LAUNCH(1);
-    else if (p.mt == 2) W4_MSD_LAUNCH(2);
-    else W4_MSD_LAUNCH(4);
+#define W4_MSD_LAUNCH(MTV, NBV, WV, GV)                                                                       \
+    if (p.mt == MTV && p.nb == NBV && p.waves == WV && gps == GV) {                                            \
+        hipLaunchKernelGGL((msd_gemm_kernel<MTV, NBV, WV, GV, DUMP>), grid, block, 0, stream, layers, coef,      \
+                           (const uint8_t *)wp, (const uint16_t *)scale, part, (uint16_t *)y, yint, M, p.mpad, \
+                           K, N, gps);                                                                         \
+        return hipGetLastError();                                                                              \
+    }
+#define W4_MSD_GPS1(MTV, NBV, WV) W4_MSD_LAUNCH(MTV, NBV, WV, 2) W4_MSD_LAUNCH(MTV, NBV, WV, 4)               \
+    W4_MSD_LAUNCH(MTV, NBV, WV, 8) W4_MSD_LAUNCH(MTV, NBV, WV, 16)
+#define W4_MSD_GPS2(MTV, NBV, WV) W4_MSD_LAUNCH(MTV, NBV, WV, 2) W4_MSD_LAUNCH(MTV, NBV, WV, 4)               \
+    W4_MSD_LAUNCH(MTV, NBV, WV, 8)
+#define W4_MSD_GPS4(MTV, NBV, WV) W4_MSD_LAUNCH(MTV, NBV, WV, 2) W4_MSD_LAUNCH(MTV, NBV, WV, 4)
+    W4_MSD_GPS2(2, 4, 8) W4_MSD_GPS2(2, 4, 4) W4_MSD_GPS1(1, 4, 8) W4_MSD_GPS4(4, 2, 8)
+    W4_MSD_GPS2(2, 2, 8) W4_MSD_GPS4(4, 4, 4)
+    // configurations reduced to fewer row tiles for small M
+    W4_MSD_GPS1(1, 4, 4) W4_MSD_GPS1(1, 2, 8)
+#undef W4_MSD_GPS1
+#undef W4_MSD_GPS2
+#undef W4_MSD_GPS4
 #undef W4_MSD_LAUNCH
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 static hipError_t msd_pre(const MsdPlan &p, const void *x, uint8_t *ws, int64_t M, int64_t K,
@@ -293,9 +462,10 @@ hipError_t launch_msd(const void *x, const void *wp, const void *scale, void *y,
     err = msd_gemm_launch<false>(p, (const int8_t *)(ws + p.off_layers), (const float *)(ws + p.off_coef), wp,
                                  scale, (float *)(ws + p.off_part), y, nullptr, M, K, N, p.ksplit, p.gps, stream);
     if (err != hipSuccess || p.ksplit == 1) return err;
-    const int64_t MN = M * N;
-    hipLaunchKernelGGL(msd_reduce_kernel, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, stream,
-                       (const float *)(ws + p.off_part), (uint16_t *)y, MN, p.ksplit);
+    const int64_t slice = (int64_t)p.mchunks * 16 * p.mt * N;     // floats per K slice
+    const int64_t nlanes = slice / 4;
+    hipLaunchKernelGGL(msd_reduce_kernel, dim3((unsigned)((nlanes + 255) / 256)), dim3(256), 0, stream,
+                       (const float *)(ws + p.off_part), (uint16_t *)y, M, N, p.mt, nlanes, slice, p.ksplit);
     return hipGetLastError();
 }
 
@@ -314,9 +484,9 @@ hipError_t launch_msd_intermediates(const void *x, const void *wp, int64_t M, in
                        (const int8_t *)(ws + p.off_layers), layers, M, p.mpad, K);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // one group per K slice, so every group's products are written separately
+    // the products of every group are written separately
     return msd_gemm_launch<true>(p, (const int8_t *)(ws + p.off_layers), (const float *)(ws + p.off_coef), wp,
-                                 nullptr, nullptr, nullptr, yint, M, K, N, (int)(K / kGroup), 1, stream);
+                                 nullptr, nullptr, nullptr, yint, M, K, N, p.ksplit, p.gps, stream);
 }
 
 }  // namespace w4

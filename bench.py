@@ -389,7 +389,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemm_small_kernel<bf16, zero, NB=4, SG=2, D=4>",
+            "kernel": "gemm_small_kernel<bf16, zero, NB=4, SG=2, D=4 (M<=4) or D=8 (M=16)>",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -44,6 +44,7 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     constexpr int XP = BM * 16 / NT;                            // 16-byte x chunks per thread
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert((BM * 16) % NT == 0, "x staging must divide evenly");
+    static_assert(XP <= 16, "one row-sum split per lane");
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BM * ROWB];
 
@@ -120,28 +121,44 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
         v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false));
         return v;
     };
+    // x slice into LDS; for bf16 also the three bf16 limbs of each row's sum
+    // (16 lanes hold a row's 16 chunks; after the row reduction every lane of
+    // the row has the sum, and lane c16 = p splits and stores the sum of its
+    // p-th row, so each lane splits one sum).  The 16 bytes after the limbs
+    // are zero (written once before the loop).
     auto store_x = [&](int buf) {
         uint8_t *base = lds + buf * BM * ROWB;
+        float ps[XP];
 #pragma unroll
         for (int p = 0; p < XP; ++p) {
             const int id = p * NT + tid, r = id >> 4, c16 = id & 15;
             *reinterpret_cast<u32x4_t *>(base + r * ROWB + c16 * 16) = xr[p];
             if constexpr (CORR) {
                 const bf16x2_t ones = as<bf16x2_t>(0x3F803F80u);
-                float ps = 0.f;
+                float v = 0.f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    ps = __builtin_amdgcn_fdot2_f32_bf16(as<bf16x2_t>(xr[p][q]), ones, ps, false);
-                ps = row16_sum(ps);
-                uint32_t hi, mid, lo;
-                split3_bf16(ps, hi, mid, lo);
-                // lanes c16 = 0, 1 of the row write the 32-byte limb slot:
-                // {hi | mid << 16, lo, 0, 0} then zeros
-                const u32x4_t limb = c16 == 0 ? u32x4_t{hi | (mid << 16), lo, 0, 0} : u32x4_t{0, 0, 0, 0};
-                if (c16 < 2) *reinterpret_cast<u32x4_t *>(base + r * ROWB + 256 + 16 * c16) = limb;
+                    v = __builtin_amdgcn_fdot2_f32_bf16(as<bf16x2_t>(xr[p][q]), ones, v, false);
+                ps[p] = row16_sum(v);
+            }
+        }
+        if constexpr (CORR) {
+            const int c16 = tid & 15;
+            float mine = ps[0];
+#pragma unroll
+            for (int p = 1; p < XP; ++p) mine = c16 == p ? ps[p] : mine;
+            uint32_t hi, mid, lo;
+            split3_bf16(mine, hi, mid, lo);
+            if (c16 < XP) {
+                const int r = (c16 * NT + tid) >> 4;
+                *reinterpret_cast<u32x4_t *>(base + r * ROWB + 256) = u32x4_t{hi | (mid << 16), lo, 0, 0};
             }
         }
     };
+    if constexpr (CORR) {
+        for (int r = tid; r < 2 * BM; r += NT)
+            *reinterpret_cast<u32x4_t *>(lds + r * ROWB + 272) = u32x4_t{0, 0, 0, 0};
+    }
 
     // ---- weight fragments, scales and zero points -----------------------------
     const int lj = lane & 31, kg = lane >> 5;
@@ -218,23 +235,21 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
             }
         }
         const uint8_t *abase = lds + buf * BM * ROWB + arow * ROWB + kg * 128;
-        f32x16_t acc[RT][CT];
+        // accumulator inputs of the first step: the bias correction (bf16; one
+        // per row tile when every column has z = 8, else one per column tile)
+        // or zero.  Passing it as the matrix-core C input avoids copying one
+        // correction into several accumulators.
+        f32x16_t cin[RT][ZERO ? CT : 1];
         if constexpr (CORR) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 const u32x4_t a = *reinterpret_cast<const u32x4_t *>(
                     lds + buf * BM * ROWB + (arow + rt * 32) * ROWB + 256 + kg * 16);
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mfma32x32x16<DT>(a, bcorr[ct], f32x16_t{});
+                for (int ci = 0; ci < (ZERO ? CT : 1); ++ci) cin[rt][ci] = mfma32x32x16<DT>(a, bcorr[ci], f32x16_t{});
             }
-        } else {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[rt][ct][r] = 0.f;
         }
+        f32x16_t acc[RT][CT];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             u32x4_t a[RT], bq[CT];
@@ -246,7 +261,14 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], acc[rt][ct]);
+                for (int ct = 0; ct < CT; ++ct) {
+                    if (t == 0) {
+                        if constexpr (CORR) acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], cin[rt][ZERO ? ct : 0]);
+                        else acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], f32x16_t{});
+                    } else {
+                        acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], acc[rt][ct]);
+                    }
+                }
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)

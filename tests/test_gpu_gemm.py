@@ -120,7 +120,7 @@ def test_m_zero_and_errors_leave_y_untouched():
     assert np.all(to_host_u16(y) == 0x1234)
 
 
-@pytest.mark.parametrize("cfg", range(6))
+@pytest.mark.parametrize("cfg", range(8))
 @pytest.mark.parametrize("dt,signed", [(synth.BF16, False), (synth.F16, True)])
 def test_tile_configs(orc, cfg, dt, signed):
     """Every workgroup tile configuration of the tile kernel, dense form:

@@ -45,7 +45,7 @@ def test_many_experts_over_workgroup_scan(orc):
     _check(orc, p, "many_experts")
 
 
-@pytest.mark.parametrize("cfg", range(6))
+@pytest.mark.parametrize("cfg", range(8))
 @pytest.mark.parametrize("dt,signed", [(synth.BF16, True), (synth.F16, False)])
 def test_tile_configs(orc, cfg, dt, signed):
     """Every workgroup tile configuration of the tile kernel, grouped form:

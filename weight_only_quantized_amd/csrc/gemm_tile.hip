@@ -30,8 +30,10 @@
 
 namespace w4 {
 
+// At least two waves per SIMD: two resident workgroups of four waves (or one
+// of eight) per compute unit, each wave within 256 registers.
 template <int DT, bool ZERO, int BM, int BN, int WM, int WN, bool GROUPED>
-__global__ void __launch_bounds__(WM * WN * 64)
+__global__ void __launch_bounds__(WM * WN * 64, 2)
 gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
                  const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
                  const uint8_t *__restrict__ zero, uint16_t *__restrict__ y,
@@ -301,10 +303,12 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
 // Workgroup tile configurations (BM x BN rows x columns, WM x WN waves).
 // Index 0 is the dense default; the grouped default follows the average row
 // count per expert (small row tiles waste less of the matrix core on experts
-// with few rows).  The others are kept for tuning through the test hook.
+// with few rows, and small workgroups let several share a compute unit).
+// The others are kept for tuning through the test hook.
 struct TileCfg { int bm, bn, wm, wn; };
 static constexpr TileCfg kTileCfgs[] = {{128, 256, 2, 4}, {64, 256, 2, 4}, {32, 256, 1, 4},
-                                        {64, 128, 2, 2}, {32, 128, 1, 4}, {128, 128, 2, 2}};
+                                        {64, 128, 2, 2}, {32, 128, 1, 4}, {128, 128, 2, 2},
+                                        {64, 256, 1, 4}, {64, 128, 1, 2}};
 static int g_tile_cfg = -1;      // -1: automatic
 
 int tile_config_count() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0])); }
@@ -331,8 +335,10 @@ static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const voi
     if (idx < 0 || idx >= tile_config_count()) {
         idx = 0;
         if (GROUPED) {
+            // few rows per expert: 32 x 128 tiles of four waves (several
+            // resident workgroups per compute unit, little padding)
             const int64_t avg = M / E;          // mean rows per expert
-            idx = avg <= 48 ? 2 : avg <= 96 ? 1 : 0;
+            idx = avg <= 96 ? 4 : 0;
         }
     }
     const TileCfg c = kTileCfgs[idx];
@@ -340,7 +346,7 @@ static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const voi
     if (c.bm == BMV && c.bn == BNV && c.wm == WMV && c.wn == WNV)                                      \
         return tile_launch<DT, ZERO, GROUPED, BMV, BNV, WMV, WNV>(x, offsets, wp, scale, zero, y, M, K, N, E, stream);
     W4_TILE(128, 256, 2, 4) W4_TILE(64, 256, 2, 4) W4_TILE(32, 256, 1, 4) W4_TILE(64, 128, 2, 2)
-    W4_TILE(32, 128, 1, 4) W4_TILE(128, 128, 2, 2)
+    W4_TILE(32, 128, 1, 4) W4_TILE(128, 128, 2, 2) W4_TILE(64, 256, 1, 4) W4_TILE(64, 128, 1, 2)
 #undef W4_TILE
     return hipErrorInvalidValue;
 }

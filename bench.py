@@ -45,12 +45,18 @@ ROTATE_BYTES = 600 * 2 ** 20   # distinct bytes touched before a buffer is reuse
 METRIC = "TFLOP/s + effective HBM GB/s (% of roofline), W4A16 g128, M=1..4096"
 
 
-def kernel_source_hash() -> str:
+# Sources that define the decode kernel (the dominant kernel of the headline
+# step): committed HBM-traffic counts are valid only for these exact files.
+DECODE_KERNEL_SOURCES = ("gemm_small.hip", "common.hpp")
+
+
+def kernel_source_hash(files=None) -> str:
+    """Hash of kernel sources (all of csrc/ by default)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "weight_only_quantized_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    names = sorted(files) if files else sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp", ".cpp")))
+    for f in names:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -303,7 +309,7 @@ def load_traffic(kernel_key):
     except (OSError, ValueError):
         return None
     e = d.get(kernel_key)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("source_hash") != kernel_source_hash(DECODE_KERNEL_SOURCES):
         return None
     return e.get("bytes_per_launch")
 
@@ -400,6 +406,7 @@ def main():
         "cpu_baseline": cpu,
         "per_config": extra,
         "kernel_source_hash": kernel_source_hash(),
+        "decode_kernel_source_hash": kernel_source_hash(DECODE_KERNEL_SOURCES),
     }
     print(json.dumps(line), flush=True)
 

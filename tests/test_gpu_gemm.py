@@ -51,6 +51,8 @@ def test_prefill_full(orc):
     (5, 512, 256, synth.BF16, True, 2),     # small M forced onto the tile kernel
     (1, 512, 256, synth.F16, False, 2),
     (16, 4096, 512, synth.BF16, False, 1),
+    (1, 9216, 128, synth.BF16, False, 0),   # K past the small-M kernel's 64 groups: tile kernel
+    (3, 8192, 192, synth.F16, True, 0),     # exactly 64 groups: small-M kernel, 4 groups per wave
 ])
 def test_edge_shapes(orc, M, K, N, dt, signed, variant):
     p = synth.make_dense(M, K, N, dt, signed=signed, seed=M + K + N,

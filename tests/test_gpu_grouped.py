@@ -61,3 +61,12 @@ def test_tile_configs(orc, cfg, dt, signed):
         _check(orc, p, f"grouped_tile_cfg{cfg}")
     finally:
         w4.w4a16_test_tile_config(-1)
+
+
+@pytest.mark.parametrize("counts,n", [([1, 1, 1], 64), ([2, 0, 31], 192), ([40] * 9, 64)])
+def test_fewer_items_than_xcds(orc, counts, n):
+    """Fewer (row tile, column block) items than XCDs, or a count that is not a
+    multiple of it: most per-XCD ranges are empty or uneven."""
+    p = synth.make_grouped(len(counts), sum(counts), 1, 256, n, synth.BF16, signed=True, counts=counts,
+                           seed=sum(counts))
+    _check(orc, p, f"grouped_small_{counts[:4]}_{n}")

@@ -18,9 +18,15 @@
 //    For bf16 the operand is 128 + v and the (128 + z) * sum_k x term is taken
 //    out by one extra step whose A operand is the three bf16 limbs of the row's
 //    group sum (computed while staging x) and whose B operand is -(128 + z).
-//  * Grouped: the workgroup index is mapped on the device to (expert, row
-//    tile) from the expert offsets (prefix sum of ceil(rows_e / BM)), so the
-//    host never reads the offsets; surplus workgroups exit at once.
+//  * Grouped: the work items are (row tile, column block) pairs, the row tiles
+//    numbered over all experts from the expert offsets (prefix sum of
+//    ceil(rows_e / BM)), computed on the device so the host never reads the
+//    offsets.  The hardware hands workgroup i to XCD i % 8, and each XCD has
+//    its own L2; XCD x therefore takes an equal, contiguous range of the items
+//    in (row tile, column block) order, so the row tiles of one expert and the
+//    expert's weights stay in one L2 (two where a range boundary splits an
+//    expert).  With another XCD count the map is still a bijection, only the
+//    locality changes.  Surplus workgroups exit at once.
 // Matrix-core mapping (v_mfma_f32_32x32x16_*): lane l feeds row/column l % 32
 // and k-block l / 32 (64 rows of the group: chunks 2*(l/32) and 2*(l/32)+1 of
 // the prepacked slot layout); result register r of lane l is row
@@ -29,6 +35,9 @@
 #include "launch.hpp"
 
 namespace w4 {
+
+// XCDs of an MI355X; workgroups are dispatched to them round-robin.
+constexpr int kXcds = 8;
 
 // At least two waves per SIMD: two resident workgroups of four waves (or one
 // of eight) per compute unit, each wave within 256 registers.
@@ -55,18 +64,41 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     const int G = (int)(K / kGroup);
     const int64_t NBLK = N / 16;
 
-    int64_t row0, row_end;
+    int64_t row0, row_end, n0;
     int64_t e = 0;
     if constexpr (GROUPED) {
-        __shared__ int s_info[2];
+        __shared__ int s_info[3];
         __shared__ int scan[NT];
-        const int bid = (int)blockIdx.x;
-        if (tid == 0) s_info[0] = -1;
+        auto tiles_of = [&](int ee) {
+            const int cnt = ee < E ? offsets[ee + 1] - offsets[ee] : 0;
+            return cnt > 0 ? (cnt + BM - 1) / BM : 0;
+        };
+        // total row tiles over all experts
+        if (tid == 0) {
+            s_info[0] = -1;
+            s_info[2] = 0;
+        }
+        __syncthreads();
+        int part = 0;
+        for (int ee = tid; ee < E; ee += NT) part += tiles_of(ee);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+        if (lane == 0) atomicAdd(&s_info[2], part);
+        __syncthreads();
+        // this workgroup's item: slot bid / 8 of XCD bid % 8's contiguous range
+        const int64_t ncb = (N + BN - 1) / BN;
+        const int64_t items = (int64_t)s_info[2] * ncb;
+        const int64_t bid = blockIdx.x;
+        const int64_t xcd = bid % kXcds, first = items * xcd / kXcds, last = items * (xcd + 1) / kXcds;
+        const int64_t item = first + bid / kXcds;
+        if (item >= last) return;   // uniform: surplus workgroup
+        const int tile = (int)(item / ncb);
+        n0 = (item % ncb) * BN;
+        // expert and row tile within it (block-wide inclusive scan per chunk)
         int carry = 0;
         for (int base = 0; base < E; base += NT) {
             const int ee = base + tid;
-            const int cnt = ee < E ? offsets[ee + 1] - offsets[ee] : 0;
-            const int tl = cnt > 0 ? (cnt + BM - 1) / BM : 0;
+            const int tl = tiles_of(ee);
             scan[tid] = tl;
             __syncthreads();
             for (int off = 1; off < NT; off <<= 1) {
@@ -76,22 +108,21 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
                 __syncthreads();
             }
             const int incl = scan[tid] + carry, excl = incl - tl;
-            if (ee < E && bid >= excl && bid < incl) {
+            if (ee < E && tile >= excl && tile < incl) {
                 s_info[0] = ee;
-                s_info[1] = bid - excl;
+                s_info[1] = tile - excl;
             }
             carry += scan[NT - 1];
             __syncthreads();
         }
-        if (s_info[0] < 0) return;   // uniform: surplus workgroup
-        e = s_info[0];
+        e = s_info[0];   // always found: tile < total row tiles
         row0 = offsets[e] + (int64_t)s_info[1] * BM;
         row_end = offsets[e + 1] < M ? offsets[e + 1] : M;   // offsets[E] == R by contract
     } else {
         row0 = (int64_t)blockIdx.x * BM;
         row_end = M;
+        n0 = (int64_t)blockIdx.y * BN;
     }
-    const int64_t n0 = (int64_t)blockIdx.y * BN;
     // A wave whose columns lie past N (N % 64 == 0, so a wave's columns are all
     // in or all out) still runs the loop on the last columns, with every load
     // in bounds, and stores nothing: no branch around any load in the loop.
@@ -318,9 +349,13 @@ template <int DT, bool ZERO, bool GROUPED, int BM, int BN, int WM, int WN>
 static hipError_t tile_launch(const void *x, const int32_t *offsets, const void *wp, const void *scale,
                               const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
                               hipStream_t stream) {
-    // grouped: every expert may end in a partial row tile, hence + E
+    // grouped: every expert may end in a partial row tile, hence + E; the
+    // items go on a 1-D grid rounded up to whole rounds over the XCDs
+    const int64_t ncb = (N + BN - 1) / BN;
     const int64_t mtiles = GROUPED ? (M + BM - 1) / BM + E : (M + BM - 1) / BM;
-    const dim3 grid((unsigned)mtiles, (unsigned)((N + BN - 1) / BN));
+    const int64_t slots = (mtiles * ncb + kXcds - 1) / kXcds * kXcds;
+    if (GROUPED && slots > INT32_MAX) return hipErrorInvalidConfiguration;
+    const dim3 grid = GROUPED ? dim3((unsigned)slots) : dim3((unsigned)mtiles, (unsigned)ncb);
     hipLaunchKernelGGL((gemm_tile_kernel<DT, ZERO, BM, BN, WM, WN, GROUPED>), grid, dim3(WM * WN * 64), 0,
                        stream, (const uint16_t *)x, offsets, (const uint8_t *)wp, (const uint16_t *)scale,
                        (const uint8_t *)zero, (uint16_t *)y, M, K, N, (int)E);

@@ -32,9 +32,12 @@
 // packed fp16 add instead.
 //
 // Scales and zero points are fetched once per group for all NB blocks (one
-// 16-bit and one 8-bit load per lane) and handed to the lanes that use them
-// with a cross-lane permute; per tile a wave then issues a single memory
-// instruction, the 128-bit weight load.
+// 16-bit and one 8-bit load per lane), packed as scale | bias << 16 (bias =
+// 128 + z for bf16, z for fp16; scale 0 for a group past the end of K) and
+// handed to the lanes that use them with a cross-lane permute; per tile a
+// wave then issues a single memory instruction, the 128-bit weight load, as
+// a buffer load whose tile offset is a scalar register (no per-load address
+// arithmetic in the vector ALU).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -64,8 +67,11 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     const int jrow = j < M ? j : M - 1;
     const uint8_t *xbase = reinterpret_cast<const uint8_t *>(x);
     const uint32_t xoff = (uint32_t)((int64_t)jrow * K + 32 * kc) * 2u;
-    const uint8_t *wblk = wp + nb0 * G * kTileBytes;
-    const uint32_t woff = (uint32_t)lane * 16u;
+    // buffer resource over this workgroup's NB * G weight tiles (raw, 32-bit
+    // data format; every offset below is in range)
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(wp + nb0 * G * kTileBytes), (short)0, NB * G * kTileBytes, 0x00020000);
+    const int woff = lane * 16;
 
     // ---- x slice of this wave: A operands of every group, loaded once ---------
     u32x4_t xa[SG][4];
@@ -77,19 +83,24 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     }
 
     // ---- scales and zero points: one load per group for all NB blocks -------
-    // Lane l fetches column 16*nb0 + l % (16*NB) and keeps scale | zero << 16;
+    // Lane l fetches column 16*nb0 + l % (16*NB) and keeps scale | bias << 16;
     // the lane that multiplies block b fetches it from lane 16*b + j with a
-    // cross-lane permute (no memory access) when the tile is reached.
+    // cross-lane permute (no memory access) when the tile is reached.  A group
+    // past the end of K (G not a multiple of SG) gets scale 0: its clamped,
+    // finite tile then contributes nothing.
+    constexpr uint32_t kBiasBase = DT == DT_BF16 ? 128u : 0u;
     uint32_t sz[SG];
     {
         const int cl = lane & (16 * NB - 1);
         const int64_t col = nb0 * 16 + cl;
 #pragma unroll
         for (int i = 0; i < SG; ++i) {
-            const int g = g0 + i < G ? g0 + i : G - 1;
-            uint32_t v = scale[(int64_t)g * N + col];
-            if constexpr (ZERO) v |= __builtin_amdgcn_ubfe(zero[((int64_t)g * N + col) >> 1], (uint32_t)(cl & 1) * 4u, 4) << 16;
-            sz[i] = v;
+            const bool live = g0 + i < G;
+            const int g = live ? g0 + i : G - 1;
+            const uint32_t sbits = scale[(int64_t)g * N + col];
+            uint32_t zb = 8u;
+            if constexpr (ZERO) zb = __builtin_amdgcn_ubfe(zero[((int64_t)g * N + col) >> 1], (uint32_t)(cl & 1) * 4u, 4);
+            sz[i] = (live ? sbits : 0u) | (kBiasBase + zb) << 16;
         }
     }
 
@@ -98,7 +109,7 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     auto issue = [&](int q) {
         const int b = q / SG, i = q % SG;
         const int g = g0 + i < G ? g0 + i : G - 1;
-        raw[q] = ld128(wblk + ((int64_t)b * G + g) * kTileBytes + woff);
+        raw[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, woff, (b * G + g) * kTileBytes, 0));
     };
 #pragma unroll
     for (int q = 0; q < D && q < T; ++q) issue(q);
@@ -132,24 +143,23 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
         __builtin_amdgcn_sched_barrier(0);
         const int b = q / SG, i = q % SG;
         const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * b + j) << 2, (int)sz[i]);
-        const uint32_t z = ZERO ? v >> 16 : 8u;
         f32x4_t acc;
         uint32_t nb2 = 0;
         if constexpr (DT == DT_BF16 && !ZERO) {
             acc = corr[i];
         } else {
             acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if constexpr (DT == DT_F16) nb2 = f16_negbias2(z);
+            if constexpr (DT == DT_F16) nb2 = ZERO ? f16_negbias2(v >> 16) : f16_negbias2(8u);
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc = mfma16x16x32<DT>(xa[i][t], dequant_word<DT>(raw[q][t], nb2), acc);
         if constexpr (DT == DT_BF16 && ZERO) {
-            const float nbias = -(float)(128u + z);
+            // 128 + z sits in byte 2: one byte-to-float conversion
+            const float nbias = -(float)((v >> 16) & 0xFFu);
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(nbias, corr[i][r], acc[r]);
         }
-        // groups past the end (G not a multiple of SG) contribute nothing
-        const float sv = g0 + i < G ? h2f<DT>((uint16_t)(v & 0xFFFFu)) : 0.f;
+        const float sv = h2f<DT>((uint16_t)(v & 0xFFFFu));
 #pragma unroll
         for (int r = 0; r < 4; ++r) yacc[b][r] += sv * acc[r];
     }

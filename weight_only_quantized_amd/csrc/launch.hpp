@@ -37,7 +37,7 @@ struct MsdPlan {
     int waves;         // waves per workgroup
     int ksplit;        // K slices (workgroups along K)
     int64_t gps;       // groups per K slice
-    size_t off_coef, off_amax, off_layers, off_part, total;
+    size_t off_coef, off_lsum, off_amax, off_layers, off_part, total;
 };
 MsdPlan msd_plan(int64_t M, int64_t K, int64_t N);
 size_t msd_workspace_bytes(int64_t M, int64_t K, int64_t N);

@@ -10,9 +10,17 @@
 // three stages across rounds, §6.2; here the waves of a compute unit overlap
 // matrix-core products and vector merges of different groups).
 //
-// Workspace (caller-owned): coef [G][3][Mpad] fp32 (A_max / (7.49*14.98^j)),
-// amax [M][G] fp32, layers [3][Mpad][K] int8 in operand order, and for K
-// splits > 1 partial sums [ksplit][M][N] fp32.
+// Workspace (caller-owned): coef [G][4][Mpad] fp32 (A_max / (7.49*14.98^j)
+// for j = 0..2, then the code-bias term 8 * sum_j coef_j * S_j), layer sums
+// S [G][3][Mpad] int32 (sum over the group of each layer), amax [M][G] fp32,
+// layers [3][Mpad][K] int8 in operand order, and for K splits > 1 partial
+// sums [ksplit][M][N] fp32.
+//
+// The weights enter the integer matrix core as their stored codes u = q + 8
+// (0..15, no conversion to signed bytes): each layer's product is then
+// Y'_j = Y_j + 8 * S_j, and the merge starts its chain from -8 * sum_j
+// coef_j * S_j (one fused multiply-add absorbs it, the cancellation is exact
+// inside the fma), so the merge costs no more than with signed operands.
 //
 // Layer storage order: inside each aligned 8-k block, byte p holds
 // k = base + {0,4,1,5,2,6,3,7}[p].  That is the order in which the int8
@@ -55,8 +63,9 @@ __device__ __forceinline__ void msd_decompose(float a, float amax, int &l1, int 
 // One 256-thread workgroup handles 16 (row, group) pairs; 16 lanes per pair,
 // 8 elements per lane.
 __global__ void __launch_bounds__(256)
-msd_decompose_kernel(const uint16_t *__restrict__ x, float *__restrict__ coef, float *__restrict__ amax_out,
-                     int8_t *__restrict__ layers, int64_t M, int64_t Mpad, int64_t K) {
+msd_decompose_kernel(const uint16_t *__restrict__ x, float *__restrict__ coef, int32_t *__restrict__ lsum,
+                     float *__restrict__ amax_out, int8_t *__restrict__ layers, int64_t M, int64_t Mpad,
+                     int64_t K) {
     const int64_t G = K / kGroup;
     const int64_t pair = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
     const int sub = threadIdx.x & 15;
@@ -84,6 +93,19 @@ msd_decompose_kernel(const uint16_t *__restrict__ x, float *__restrict__ coef, f
     int l[3][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) msd_decompose(a[i], am, l[0][i], l[1][i], l[2][i]);
+    // layer sums over the group (16 lanes x 8 elements), exact in int32
+    int ls[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        int t = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t += l[j][i];
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        t += __shfl_xor(t, 4);
+        t += __shfl_xor(t, 8);
+        ls[j] = t;
+    }
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         uint64_t packed = 0;
@@ -92,17 +114,22 @@ msd_decompose_kernel(const uint16_t *__restrict__ x, float *__restrict__ coef, f
         *reinterpret_cast<uint64_t *>(layers + (j * Mpad + m) * K + g * kGroup + sub * 8) = packed;
     }
     if (sub == 0) {
-        coef[(g * 3 + 0) * Mpad + m] = am * kR0;
-        coef[(g * 3 + 1) * Mpad + m] = am * kR1;
-        coef[(g * 3 + 2) * Mpad + m] = am * kR2;
+        const float c0 = am * kR0, c1 = am * kR1, c2 = am * kR2;
+        coef[(g * 4 + 0) * Mpad + m] = c0;
+        coef[(g * 4 + 1) * Mpad + m] = c1;
+        coef[(g * 4 + 2) * Mpad + m] = c2;
+        coef[(g * 4 + 3) * Mpad + m] =
+            8.f * __builtin_fmaf(c0, (float)ls[0], __builtin_fmaf(c1, (float)ls[1], c2 * (float)ls[2]));
+#pragma unroll
+        for (int j = 0; j < 3; ++j) lsum[(g * 3 + j) * Mpad + m] = ls[j];
         if (real) amax_out[m * G + g] = am;
     }
 }
 
-// Signed int8 operand of one 16x16x64 step from two prepacked words.
-__device__ __forceinline__ u32x4_t weight_i8(uint32_t w0, uint32_t w1) {
-    return u32x4_t{codes_to_s8(w0 & 0x0F0F0F0Fu), codes_to_s8((w0 >> 4) & 0x0F0F0F0Fu),
-                   codes_to_s8(w1 & 0x0F0F0F0Fu), codes_to_s8((w1 >> 4) & 0x0F0F0F0Fu)};
+// int8 operand of one 16x16x64 step from two prepacked words: the stored
+// codes u = q + 8 (0..15), one per byte.
+__device__ __forceinline__ u32x4_t weight_u4(uint32_t w0, uint32_t w1) {
+    return u32x4_t{w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
 }
 
 // Integer products of the three layers with the weights (eq.9) and the merge
@@ -133,14 +160,15 @@ template <int MT> struct MsdLds {
 template <int MT, int NB, int W, int GPS, bool DUMP>
 __global__ void __launch_bounds__(W * 64)
 msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coef,
-                const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
+                const int32_t *__restrict__ lsum, const uint8_t *__restrict__ wp,
+                const uint16_t *__restrict__ scale,
                 float *__restrict__ part, uint16_t *__restrict__ y, int32_t *__restrict__ yint,
                 int64_t M, int64_t Mpad, int64_t K, int64_t N, int64_t gps) {
     constexpr int NT = W * 64;
     constexpr int ROWS = MsdLds<MT>::ROWS, AROW = MsdLds<MT>::AROW;
     static_assert(GPS <= MsdLds<MT>::GPSMAX, "slice must fit in LDS");
     __shared__ __attribute__((aligned(16))) uint8_t sA[3 * ROWS * AROW];
-    __shared__ __attribute__((aligned(16))) float sC[GPS * 3 * ROWS];
+    __shared__ __attribute__((aligned(16))) float sC[GPS * 4 * ROWS];
 
     const int64_t G = K / kGroup;
     const int tid = threadIdx.x, lane = lane_id();
@@ -183,29 +211,32 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
         // store (one memory round trip), after the first two groups' weights
         load_w(0, wr[0], sr[0]);
         load_w(1, wr[1], sr[1]);
-        constexpr int CMAX = 3 * ROWS * GPS * 8;                  // chunks of a full slice
+        // every group slot of the slice is filled: slots past a short final
+        // slice copy its last group (finite bytes, multiplied by zero
+        // coefficients), so the chunk count and its divisions are static
+        constexpr int PIECES = GPS * 8;                            // 16-byte pieces per row
+        constexpr int CMAX = 3 * ROWS * PIECES;
         constexpr int CPT = (CMAX + NT - 1) / NT;
-        const int pieces = ng * 8;
-        const int chunks = 3 * ROWS * pieces;
         u32x4_t v[CPT];
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
-            const int c1 = u * NT + tid, c = c1 < chunks ? c1 : chunks - 1;
-            const int lr = c / pieces, pc = c % pieces;                // lr = l * ROWS + row
+            const int c1 = u * NT + tid, c = c1 < CMAX ? c1 : CMAX - 1;
+            const int lr = c / PIECES, pc = c % PIECES;                // lr = l * ROWS + row
             const int l = lr / ROWS, row = lr % ROWS;
-            v[u] = ld128(layers + (l * Mpad + m0 + row) * K + g_begin * kGroup + pc * 16);
+            const int gl = pc / 8 < ng ? pc / 8 : ng - 1;
+            v[u] = ld128(layers + (l * Mpad + m0 + row) * K + (g_begin + gl) * kGroup + (pc % 8) * 16);
         }
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
             const int c = u * NT + tid;
-            if (c < chunks) {
-                const int lr = c / pieces, pc = c % pieces;
+            if (CMAX % NT == 0 || c < CMAX) {
+                const int lr = c / PIECES, pc = c % PIECES;
                 *reinterpret_cast<u32x4_t *>(&sA[lr * AROW + pc * 16]) = v[u];
             }
         }
-        for (int i = tid; i < GPS * 3 * ROWS; i += NT) {
-            const int gl = i / (3 * ROWS), lr = i % (3 * ROWS);
-            sC[i] = gl < ng ? coef[((g_begin + gl) * 3 + lr / ROWS) * Mpad + m0 + lr % ROWS] : 0.f;
+        for (int i = tid; i < GPS * 4 * ROWS; i += NT) {
+            const int gl = i / (4 * ROWS), lr = i % (4 * ROWS);
+            sC[i] = gl < ng ? coef[((g_begin + gl) * 4 + lr / ROWS) * Mpad + m0 + lr % ROWS] : 0.f;
         }
     }
     __syncthreads();
@@ -228,20 +259,23 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
         float s[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            bop[b][0] = weight_i8(wc[b][0], wc[b][1]);
-            bop[b][1] = weight_i8(wc[b][2], wc[b][3]);
+            bop[b][0] = weight_u4(wc[b][0], wc[b][1]);
+            bop[b][1] = weight_u4(wc[b][2], wc[b][3]);
             s[b] = DUMP ? 0.f : h2f<DT_F16>(sc[b]);
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             u32x4_t a[3][2];
-            float c[3][4];
+            float c[4][4];
 #pragma unroll
             for (int l = 0; l < 3; ++l) {
                 const uint8_t *ap = sA + (l * ROWS + mt * 16 + j) * AROW + gl * kGroup + 32 * kc;
                 a[l][0] = *reinterpret_cast<const u32x4_t *>(ap);
                 a[l][1] = *reinterpret_cast<const u32x4_t *>(ap + 16);
-                const f32x4_t cv = *reinterpret_cast<const f32x4_t *>(&sC[(gl * 3 + l) * ROWS + mt * 16 + 4 * kc]);
+            }
+#pragma unroll
+            for (int l = 0; l < 4; ++l) {
+                const f32x4_t cv = *reinterpret_cast<const f32x4_t *>(&sC[(gl * 4 + l) * ROWS + mt * 16 + 4 * kc]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) c[l][r] = cv[r];
             }
@@ -261,13 +295,16 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
                             for (int r = 0; r < 4; ++r) {
                                 const int64_t row = m0 + 16 * mt + 4 * kc + r;
                                 if (row < M && gl < ng)
-                                    yint[(((g_begin + gl) * 3 + l) * M + row) * N + (nb0 + b) * 16 + j] = Y[l][r];
+                                    yint[(((g_begin + gl) * 3 + l) * M + row) * N + (nb0 + b) * 16 + j] =
+                                        Y[l][r] - 8 * lsum[((g_begin + gl) * 3 + l) * Mpad + row];
                             }
                     }
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float t = (float)Y[0][r] * c[0][r] + (float)Y[1][r] * c[1][r] + (float)Y[2][r] * c[2][r];
+                        float t = __builtin_fmaf((float)Y[0][r], c[0][r], -c[3][r]);
+                        t = __builtin_fmaf((float)Y[1][r], c[1][r], t);
+                        t = __builtin_fmaf((float)Y[2][r], c[2][r], t);
                         yacc[b][mt][r] += s[b] * t;
                     }
                 }
@@ -388,7 +425,8 @@ static MsdPlan msd_plan_cfg(int64_t M, int64_t K, int64_t N, const MsdCfg &c) {
         if (colwg * p.mchunks * ((G + g - 1) / g) >= target || g == 2) { p.gps = g; break; }
     p.ksplit = (int)((G + p.gps - 1) / p.gps);
     p.off_coef = 0;
-    p.off_amax = align_up(p.off_coef + sizeof(float) * (size_t)(G * 3 * p.mpad), 256);
+    p.off_lsum = align_up(p.off_coef + sizeof(float) * (size_t)(G * 4 * p.mpad), 256);
+    p.off_amax = align_up(p.off_lsum + sizeof(int32_t) * (size_t)(G * 3 * p.mpad), 256);
     p.off_layers = align_up(p.off_amax + sizeof(float) * (size_t)(M * G), 256);
     p.off_part = align_up(p.off_layers + (size_t)(3 * p.mpad * K), 256);
     const int64_t rows_cov = (int64_t)p.mchunks * 16 * p.mt;   // rows covered by the row chunks
@@ -414,7 +452,8 @@ size_t msd_workspace_bytes(int64_t M, int64_t K, int64_t N) {
 }
 
 template <bool DUMP>
-static hipError_t msd_gemm_launch(const MsdPlan &p, const int8_t *layers, const float *coef, const void *wp,
+static hipError_t msd_gemm_launch(const MsdPlan &p, const int8_t *layers, const float *coef,
+                                  const int32_t *lsum, const void *wp,
                                   const void *scale, float *part, void *y, int32_t *yint, int64_t M,
                                   int64_t K, int64_t N, int ksplit, int64_t gps, hipStream_t stream) {
     const int64_t colwg = (N / 16 + p.nb * p.waves - 1) / (p.nb * p.waves);
@@ -423,7 +462,7 @@ static hipError_t msd_gemm_launch(const MsdPlan &p, const int8_t *layers, const 
 #define W4_MSD_LAUNCH(MTV, NBV, WV, GV)                                                                       \
     if (p.mt == MTV && p.nb == NBV && p.waves == WV && gps == GV) {                                            \
         hipLaunchKernelGGL((msd_gemm_kernel<MTV, NBV, WV, GV, DUMP>), grid, block, 0, stream, layers, coef,      \
-                           (const uint8_t *)wp, (const uint16_t *)scale, part, (uint16_t *)y, yint, M, p.mpad, \
+                           lsum, (const uint8_t *)wp, (const uint16_t *)scale, part, (uint16_t *)y, yint, M, p.mpad, \
                            K, N, gps);                                                                         \
         return hipGetLastError();                                                                              \
     }
@@ -448,7 +487,8 @@ static hipError_t msd_pre(const MsdPlan &p, const void *x, uint8_t *ws, int64_t 
     const int64_t G = K / kGroup;
     const int64_t pairs = p.mpad * G;
     hipLaunchKernelGGL(msd_decompose_kernel, dim3((unsigned)((pairs + 15) / 16)), dim3(256), 0, stream,
-                       (const uint16_t *)x, (float *)(ws + p.off_coef), (float *)(ws + p.off_amax),
+                       (const uint16_t *)x, (float *)(ws + p.off_coef), (int32_t *)(ws + p.off_lsum),
+                       (float *)(ws + p.off_amax),
                        (int8_t *)(ws + p.off_layers), M, p.mpad, K);
     return hipGetLastError();
 }
@@ -459,7 +499,8 @@ hipError_t launch_msd(const void *x, const void *wp, const void *scale, void *y,
     uint8_t *ws = (uint8_t *)workspace;
     hipError_t err = msd_pre(p, x, ws, M, K, stream);
     if (err != hipSuccess) return err;
-    err = msd_gemm_launch<false>(p, (const int8_t *)(ws + p.off_layers), (const float *)(ws + p.off_coef), wp,
+    err = msd_gemm_launch<false>(p, (const int8_t *)(ws + p.off_layers), (const float *)(ws + p.off_coef),
+                                 (const int32_t *)(ws + p.off_lsum), wp,
                                  scale, (float *)(ws + p.off_part), y, nullptr, M, K, N, p.ksplit, p.gps, stream);
     if (err != hipSuccess || p.ksplit == 1) return err;
     const int64_t slice = (int64_t)p.mchunks * 16 * p.mt * N;     // floats per K slice
@@ -485,7 +526,8 @@ hipError_t launch_msd_intermediates(const void *x, const void *wp, int64_t M, in
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     // the products of every group are written separately
-    return msd_gemm_launch<true>(p, (const int8_t *)(ws + p.off_layers), (const float *)(ws + p.off_coef), wp,
+    return msd_gemm_launch<true>(p, (const int8_t *)(ws + p.off_layers), (const float *)(ws + p.off_coef),
+                                 (const int32_t *)(ws + p.off_lsum), wp,
                                  nullptr, nullptr, nullptr, yint, M, K, N, p.ksplit, p.gps, stream);
 }
 

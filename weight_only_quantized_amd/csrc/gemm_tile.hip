@@ -332,14 +332,18 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
 }
 
 // Workgroup tile configurations (BM x BN rows x columns, WM x WN waves).
-// Index 0 is the dense default; the grouped default follows the average row
-// count per expert (small row tiles waste less of the matrix core on experts
-// with few rows, and small workgroups let several share a compute unit).
-// The others are kept for tuning through the test hook.
+// Index 0 is the dense default: 64 x 64 wave tiles in workgroups of four
+// waves, two resident per compute unit, so that one workgroup's matrix-core
+// steps overlap the other's vector work across their separate per-group
+// barriers (measured ~5% faster on 4096^3 than one eight-wave 128 x 256
+// workgroup with the same wave tile).  The grouped default follows the
+// average row count per expert (small row tiles waste less of the matrix
+// core on experts with few rows).  The others are kept for tuning through
+// the test hook.
 struct TileCfg { int bm, bn, wm, wn; };
-static constexpr TileCfg kTileCfgs[] = {{128, 256, 2, 4}, {64, 256, 2, 4}, {32, 256, 1, 4},
+static constexpr TileCfg kTileCfgs[] = {{64, 256, 1, 4}, {64, 256, 2, 4}, {32, 256, 1, 4},
                                         {64, 128, 2, 2}, {32, 128, 1, 4}, {128, 128, 2, 2},
-                                        {64, 256, 1, 4}, {64, 128, 1, 2}};
+                                        {128, 256, 2, 4}, {64, 128, 1, 2}};
 static int g_tile_cfg = -1;      // -1: automatic
 
 int tile_config_count() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0])); }

@@ -244,6 +244,7 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     // between steps, so a prefetch is waited for only in the step that uses
     // it (a register copy would wait for it at once).
     const int arow = wm * TM + lj;             // LDS row of this lane's A operand (row tile 0)
+    constexpr int kStageStep = 4;              // k-step after which the next x slice is staged
     auto step = [&](int g, const u32x4_t (&bw)[CT][2], const uint16_t (&sw)[CT], const uint8_t (&zw)[CT],
                     u32x4_t (&bn)[CT][2], uint16_t (&sn)[CT], uint8_t (&zn)[CT]) {
         const int buf = g & 1;
@@ -302,6 +303,11 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
                         acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], acc[rt][ct]);
                     }
                 }
+            // stage the next group's x slice halfway through the products: its
+            // vector work (row sums, limb split) then overlaps matrix-core
+            // steps.  The buffer written was last read in the previous step,
+            // before that step's barrier.
+            if (t == kStageStep) store_x(buf ^ 1);
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -309,7 +315,6 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) yacc[rt][ct][r] += s[ct] * acc[rt][ct][r];
-        store_x(buf ^ 1);
         __syncthreads();
     };
     for (int g = 0; g < G; g += 2) {

@@ -61,6 +61,11 @@ def lib():
             "oracle_msd_decompose_one": ([C.c_float, C.c_float, _p, _p], None),
             "oracle_msd_yint": ([_p, _p, _i64, _i64, _i64, _i64, _p], None),
             "oracle_msd": ([_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p], None),
+            "oracle_moe_align": ([_p, _i64, _i64, _i64, _p, _p, _p], _i64),
+            "oracle_silu_and_mul": ([_p, _i64, _i64, C.c_int, _p], None),
+            "oracle_moe_sum": ([_p, _p, _p, _i64, _i64, _i64, C.c_int, _p], None),
+            "oracle_fused_moe": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                  C.c_int, _p, _i64, _p], None),
             "oracle_prepack": ([_p, _p, _i64, _i64, _i64, C.c_int], None),
             "oracle_unpack": ([_p, _p, _i64, _i64, _i64, C.c_int], None),
         }
@@ -160,6 +165,50 @@ def msd(x, w, scale, M, K, N, group=128, intermediates=False):
     if intermediates:
         return y64, y, amax, layers
     return y64, y
+
+
+def moe_align(topk_ids, E):
+    """Stable routing prep: returns (offsets [E+1], sorted [R], row_of [T*topk])."""
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    T, topk = ids.shape
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    sorted_ = np.zeros(max(T * topk, 1), dtype=np.int32)
+    row_of = np.zeros(max(T * topk, 1), dtype=np.int32)
+    R = lib().oracle_moe_align(_ptr(ids), T, topk, E, _ptr(offsets), _ptr(sorted_), _ptr(row_of))
+    return offsets, sorted_[:R].copy(), row_of[:T * topk].copy()
+
+
+def silu_and_mul(h, dtype):
+    """h: uint16 bits [R][2I] -> a [R][I] bits."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    R, I2 = h.shape
+    a = np.empty((R, I2 // 2), dtype=np.uint16)
+    lib().oracle_silu_and_mul(_ptr(h), R, I2 // 2, dtype, _ptr(a))
+    return a
+
+
+def moe_sum(o, row_of, topk_w, dtype):
+    """o: uint16 bits [R][N]; row_of [T*topk]; topk_w fp32 [T][topk] -> [T][N] bits."""
+    o = np.ascontiguousarray(o, dtype=np.uint16)
+    w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    T, topk = w.shape
+    N = o.shape[1]
+    out = np.empty((T, N), dtype=np.uint16)
+    lib().oracle_moe_sum(_ptr(o), _ptr(np.ascontiguousarray(row_of, np.int32)), _ptr(w), T, topk, N,
+                         dtype, _ptr(out))
+    return out
+
+
+def fused_moe(c, tokens=None):
+    """Whole fused-experts chain of a synth.MoeChain for the given tokens
+    (default: all); returns [P][H] bits."""
+    tok = np.arange(c.T, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, np.int64)
+    out = np.empty((tok.shape[0], c.H), dtype=np.uint16)
+    lib().oracle_fused_moe(_ptr(c.x), _ptr(np.ascontiguousarray(c.topk_ids, np.int32)),
+                           _ptr(np.ascontiguousarray(c.topk_w, np.float32)), _ptr(c.w13), _ptr(c.s13),
+                           _ptr(c.z13), _ptr(c.w2), _ptr(c.s2), _ptr(c.z2), c.T, c.topk, c.E, c.H, c.I,
+                           128, c.dtype, _ptr(tok), tok.shape[0], _ptr(out))
+    return out
 
 
 def prepack(w, E, K, N, is_signed):

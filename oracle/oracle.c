@@ -391,3 +391,94 @@ void oracle_unpack(const uint8_t *packed, uint8_t *w, int64_t E, int64_t K, int6
                 *dst |= (uint8_t)((n & 1) ? (code << 4) : code);
             }
 }
+
+/* ------------------------------------------------------------------------- */
+/* MoE fused-experts chain                                                    */
+/* ------------------------------------------------------------------------- */
+
+int64_t oracle_moe_align(const int32_t *topk_ids, int64_t T, int64_t topk, int64_t E,
+                         int32_t *offsets, int32_t *sorted, int32_t *row_of) {
+    int64_t n = T * topk;
+    /* counting sort, stable in the entry index */
+    int64_t *next = (int64_t *)calloc((size_t)E + 1, sizeof(int64_t));
+    assert(next);
+    for (int64_t i = 0; i < n; ++i) {
+        int32_t e = topk_ids[i];
+        if (e >= 0 && e < E) next[e + 1] += 1;
+    }
+    for (int64_t e = 0; e < E; ++e) next[e + 1] += next[e];
+    for (int64_t e = 0; e <= E; ++e) offsets[e] = (int32_t)next[e];
+    for (int64_t i = 0; i < n; ++i) {
+        int32_t e = topk_ids[i];
+        if (e >= 0 && e < E) {
+            int64_t r = next[e]++;
+            sorted[r] = (int32_t)i;
+            row_of[i] = (int32_t)r;
+        } else {
+            row_of[i] = -1;
+        }
+    }
+    int64_t R = offsets[E];
+    free(next);
+    return R;
+}
+
+static double silu(double g) { return g / (1.0 + exp(-g)); }
+
+void oracle_silu_and_mul(const uint16_t *h, int64_t R, int64_t I, int dtype, uint16_t *a) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t i = 0; i < I; ++i) {
+            double g = to_double(h[r * 2 * I + i], dtype);
+            double u = to_double(h[r * 2 * I + I + i], dtype);
+            double v = silu(g) * u;
+            oracle_round_array(&v, &a[r * I + i], 1, dtype);
+        }
+}
+
+void oracle_moe_sum(const uint16_t *o, const int32_t *row_of, const float *topk_w,
+                    int64_t T, int64_t topk, int64_t N, int dtype, uint16_t *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t k = 0; k < topk; ++k) {
+                int32_t r = row_of[t * topk + k];
+                if (r < 0) continue;
+                s += (double)topk_w[t * topk + k] * to_double(o[(int64_t)r * N + n], dtype);
+            }
+            oracle_round_array(&s, &out[t * N + n], 1, dtype);
+        }
+}
+
+void oracle_fused_moe(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                      const uint8_t *w13, const uint16_t *s13, const uint8_t *z13,
+                      const uint8_t *w2, const uint16_t *s2, const uint8_t *z2,
+                      int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I,
+                      int64_t group, int dtype, const int64_t *tok, int64_t P, uint16_t *out) {
+    (void)T;
+    int64_t G1 = H / group, G2 = I / group;
+    uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(2 * I));
+    uint16_t *a = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)I);
+    uint16_t *ob = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)H);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)H);
+    assert(h && a && ob && acc);
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t t = tok[p];
+        for (int64_t n = 0; n < H; ++n) acc[n] = 0.0;
+        for (int64_t k = 0; k < topk; ++k) {
+            int32_t e = topk_ids[t * topk + k];
+            if (e < 0 || e >= E) continue;
+            /* gate/up projection of the token, rounded to the dtype */
+            oracle_w4a16(x + t * H, w13 + e * H * I, s13 + e * G1 * 2 * I,
+                         z13 ? z13 + e * G1 * I : NULL, 1, H, 2 * I, group, dtype, NULL, h);
+            oracle_silu_and_mul(h, 1, I, dtype, a);
+            /* down projection, rounded to the dtype */
+            oracle_w4a16(a, w2 + e * I * (H / 2), s2 + e * G2 * H, z2 ? z2 + e * G2 * (H / 2) : NULL,
+                         1, I, H, group, dtype, NULL, ob);
+            for (int64_t n = 0; n < H; ++n) acc[n] += (double)topk_w[t * topk + k] * to_double(ob[n], dtype);
+        }
+        oracle_round_array(acc, out + p * H, H, dtype);
+    }
+    free(h); free(a); free(ob); free(acc);
+}

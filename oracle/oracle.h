@@ -81,6 +81,42 @@ void oracle_msd(const uint16_t *x, const uint8_t *w, const uint16_t *scale, int6
 void oracle_prepack(const uint8_t *w, uint8_t *packed, int64_t E, int64_t K, int64_t N, int is_signed);
 void oracle_unpack(const uint8_t *packed, uint8_t *w, int64_t E, int64_t K, int64_t N, int is_signed);
 
+/* ---- MoE fused-experts chain (pwwt.cn notes, §5: fused_experts_impl runs
+ * moe_gemm -> fuse_silu_mul -> moe_gemm; FlagGems-vLLM operator list, MoE and
+ * activation tables: moe_align_block_size, silu_and_mul, moe_sum).  Routing
+ * entry i = t*topk + k of token t picks expert topk_ids[i] with weight
+ * topk_w[i] (fp32); ids outside [0, E) are not routed. ---- */
+
+/* Routing prep: routed entries ordered by (expert, i) and numbered
+ * r = 0..R-1; offsets[e] = routed entries with expert < e (offsets[E] = R),
+ * sorted[r] = i of row r (R entries written), row_of[i] = r, or -1 when
+ * entry i is not routed.  Returns R. */
+int64_t oracle_moe_align(const int32_t *topk_ids, int64_t T, int64_t topk, int64_t E,
+                         int32_t *offsets, int32_t *sorted, int32_t *row_of);
+
+/* a[r][i] = RNE( silu(h[r][i]) * h[r][I + i] ), silu(g) = g / (1 + exp(-g)),
+ * in fp64; h is [R][2I] (gate half first), a is [R][I], dtype of both. */
+void oracle_silu_and_mul(const uint16_t *h, int64_t R, int64_t I, int dtype, uint16_t *a);
+
+/* out[t][n] = RNE( sum over routed k, ascending, of topk_w[t*topk+k] *
+ * o[row_of[t*topk+k]][n] ) in fp64; a token with no routed entry gets 0. */
+void oracle_moe_sum(const uint16_t *o, const int32_t *row_of, const float *topk_w,
+                    int64_t T, int64_t topk, int64_t N, int dtype, uint16_t *out);
+
+/* The whole chain for tokens tok[0..P-1]:
+ *   h   = RNE(x[t] . dequant(W13_e))            [2I]   (W13_e: [H][2I])
+ *   a   = silu_and_mul(h)                       [I]
+ *   o   = RNE(a . dequant(W2_e))                [H]    (W2_e: [I][H])
+ *   out[p] = RNE( sum_k topk_w[t,k] * o_k )     [H]
+ * with e = topk_ids[t*topk+k] over the routed k, the weights in the plain
+ * layouts (w13 [E][H][I], s13 [E][H/128][2I], z13 [E][H/128][I] or NULL;
+ * w2 [E][I][H/2], s2 [E][I/128][H], z2 [E][I/128][H/2] or NULL). */
+void oracle_fused_moe(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                      const uint8_t *w13, const uint16_t *s13, const uint8_t *z13,
+                      const uint8_t *w2, const uint16_t *s2, const uint8_t *z2,
+                      int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I,
+                      int64_t group, int dtype, const int64_t *tok, int64_t P, uint16_t *out);
+
 #ifdef __cplusplus
 }
 #endif

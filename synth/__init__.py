@@ -241,3 +241,68 @@ def moe(seed=0) -> Problem:
     """MoE grouped: 64 experts, 512 tokens, top-8 Zipf(1.1) routing,
     K=2048, N=1408; x bf16 N(0,1); signed int4; scale bf16 U[0.002,0.01]."""
     return make_grouped(64, 512, 8, 2048, 1408, BF16, alpha=1.1, signed=True, seed=seed, name="moe")
+
+
+# ---------------------------------------------------------------------------
+# MoE fused-experts chain (routing, gate/up and down expert weights)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class MoeChain:
+    """Inputs of one fused-experts call in the plain layouts: tokens x
+    [T][H], routing ids/weights [T][topk], gate/up weights W13 [E][H][2I]
+    (gate columns 0..I-1, up columns I..2I-1) and down weights W2 [E][I][H],
+    each with per-group scales (and zero points when unsigned)."""
+    x: np.ndarray                  # uint16 [T][H]
+    topk_ids: np.ndarray           # int32 [T][topk]
+    topk_w: np.ndarray             # float32 [T][topk]
+    w13: np.ndarray                # uint8 [E][H][I]      (2I nibbles per row)
+    s13: np.ndarray                # uint16 [E][H/128][2I]
+    z13: Optional[np.ndarray]      # uint8 [E][H/128][I] or None
+    w2: np.ndarray                 # uint8 [E][I][H/2]
+    s2: np.ndarray                 # uint16 [E][I/128][H]
+    z2: Optional[np.ndarray]       # uint8 [E][I/128][H/2] or None
+    T: int
+    topk: int
+    E: int
+    H: int
+    I: int
+    dtype: int
+    name: str = ""
+
+    @property
+    def signed(self) -> bool:
+        return self.z13 is None
+
+
+def make_moe_chain(T, topk, E, H, I, dtype=BF16, alpha=1.1, signed=True, seed=0,
+                   scale_range=(0.002, 0.01), ids: Optional[np.ndarray] = None, name="") -> MoeChain:
+    """Fused-experts inputs: x ~ N(0,1); routing ids from :func:`zipf_routing`
+    (``ids`` overrides them, e.g. with out-of-range entries); routing weights
+    drawn U[0.05, 1) and normalised to sum 1 per token; int4 weights and
+    uniform scales as in :func:`make_grouped`."""
+    assert H % GROUP == 0 and I % GROUP == 0
+    x = to_bits(_normal(stream(seed, "tokens"), (T, H)), dtype)
+    if ids is None:
+        ids = zipf_routing(T, E, topk, alpha, seed) if T else np.zeros((0, topk), np.int64)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    wr = 0.05 + 0.95 * stream(seed, "mask").random((T, topk))
+    wr = (wr / wr.sum(axis=1, keepdims=True)).astype(np.float32) if T else wr.astype(np.float32)
+    _, w13 = _weights(seed, (E, H, 2 * I), signed, tag="w")
+    s13 = _scales(seed, (E, H // GROUP, 2 * I), scale_range[0], scale_range[1], dtype, tag="s")
+    _, w2 = _weights(seed, (E, I, H), signed, tag="w2")
+    s2 = _scales(seed, (E, I // GROUP, H), scale_range[0], scale_range[1], dtype, tag="s2")
+    z13 = z2 = None
+    if not signed:
+        z13 = pack_nibbles(stream(seed, "z").integers(6, 10, size=(E, H // GROUP, 2 * I), dtype=np.int8).view(np.uint8))
+        z2 = pack_nibbles(stream(seed, "z2").integers(6, 10, size=(E, I // GROUP, H), dtype=np.int8).view(np.uint8))
+    return MoeChain(x=x, topk_ids=ids, topk_w=wr, w13=w13, s13=s13, z13=z13, w2=w2, s2=s2, z2=z2,
+                    T=T, topk=topk, E=E, H=H, I=I, dtype=dtype, name=name)
+
+
+def moe_chain(seed=0) -> MoeChain:
+    """Fused-experts chain at the MoE workload's sizes: 64 experts, 512
+    tokens, top-8 Zipf(1.1) routing, hidden H=2048, expert width I=1408 (the
+    grouped GEMM's K and N); x bf16 N(0,1); signed int4; scales bf16
+    U[0.002,0.01]."""
+    return make_moe_chain(512, 8, 64, 2048, 1408, BF16, alpha=1.1, signed=True, seed=seed, name="moe_chain")

@@ -19,7 +19,11 @@ roofline = the dominant kernel (the small-M split-K kernel): algorithmic
 cpu_baseline = the CPU oracle on the same decode step (host cores).
 
 per_config adds the same measurement for the other workloads (tiny, prefill,
-MSD, MoE grouped); they are reported for completeness, the headline is decode.
+MSD, MoE grouped, and the MoE fused-experts chain: routing prep, gather, gate/up
+grouped GEMM, SiLU and multiply, down grouped GEMM, weighted sum); they are
+reported for completeness, the headline is decode.  The chain's algorithmic
+bytes: tokens in and out (T*H*2 each), routing ids and weights (T*topk*8), and
+the active experts' gate/up and down weights with their scales.
 
 Algorithmic bytes of one dense call: x (M*K*2) + packed weights (K*N/2) +
 scales (K/128*N*2) + zero points (K/128*N/2, if any) + y (M*N*2).
@@ -193,6 +197,45 @@ def moe_workload():
     return [("moe", launch, nbytes, 2 * p.M * p.N * p.K)], len(wps)
 
 
+def moe_chain_workload():
+    """Fused-experts chain (routing prep, gather, gate/up grouped GEMM, SiLU and
+    multiply, down grouped GEMM, weighted sum) at the MoE workload's sizes."""
+    import numpy as np
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    c = synth.moe_chain()
+    dev = "cuda:0"
+
+    def pack(wplain, K, N):
+        out = torch.empty(w4.w4a16_prepacked_bytes(c.E, K, N), dtype=torch.uint8, device=dev)
+        w4.w4a16_prepack(_dev(wplain.reshape(-1)), out, c.E, K, N, int(c.signed))
+        return out
+    w13, w2 = pack(c.w13, c.H, 2 * c.I), pack(c.w2, c.I, c.H)
+    s13, s2 = _dev(c.s13), _dev(c.s2)
+    x, ids = _dev(c.x), _dev(np.ascontiguousarray(c.topk_ids, np.int32))
+    tw = _dev(np.ascontiguousarray(c.topk_w, np.float32))
+    out = torch.empty((c.T, c.H), dtype=torch.int16, device=dev)
+    nb = w4.w4a16_fused_moe_workspace_bytes(c.T, c.topk, c.E, c.H, c.I)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    per_set = w13.numel() + w2.numel() + (s13.numel() + s2.numel()) * 2
+    sets = _copies(w13, per_set)
+    w2s = [w2] + [w2.clone() for _ in range(len(sets) - 1)]
+    s13s = [s13] + [s13.clone() for _ in range(len(sets) - 1)]
+    s2s = [s2] + [s2.clone() for _ in range(len(sets) - 1)]
+    active = np.unique(c.topk_ids[(c.topk_ids >= 0) & (c.topk_ids < c.E)]).size
+    R = int(((c.topk_ids >= 0) & (c.topk_ids < c.E)).sum())
+    wbytes = c.H * 2 * c.I // 2 + c.H // 128 * 2 * c.I * 2 + c.I * c.H // 2 + c.I // 128 * c.H * 2
+    nbytes = c.T * c.H * 2 * 2 + c.T * c.topk * 8 + active * wbytes
+    flops = 2 * R * c.H * 2 * c.I + 2 * R * c.I * c.H
+
+    def launch(i):
+        j = i % len(sets)
+        w4.w4a16_fused_moe(x, ids, tw, sets[j], s13s[j], None, w2s[j], s2s[j], None, out, c.T, c.topk, c.E,
+                           c.H, c.I, 128, synth.BF16, ws, nb)
+    return [("moe_chain", launch, nbytes, flops)], len(sets)
+
+
 # ---------------------------------------------------------------------------
 # timing
 # ---------------------------------------------------------------------------
@@ -319,7 +362,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["decode", "tiny", "prefill", "msd", "moe"], default=None,
+    ap.add_argument("--only", choices=["decode", "tiny", "prefill", "msd", "moe", "moe_chain"], default=None,
                     help="run only this workload (profiling); no JSON headline unless decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-config extras")
@@ -348,7 +391,7 @@ def main():
         return
 
     builders = {"decode": decode_workload, "tiny": tiny_workload, "prefill": prefill_workload,
-                "msd": msd_workload, "moe": moe_workload}
+                "msd": msd_workload, "moe": moe_workload, "moe_chain": moe_chain_workload}
     if args.only and args.only != "decode":
         _, out = measure(args.only, builders[args.only], args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **out}), flush=True)
@@ -364,7 +407,7 @@ def main():
 
     extra = {}
     if not args.no_extra and not args.only:
-        for name in ("tiny", "prefill", "msd", "moe"):
+        for name in ("tiny", "prefill", "msd", "moe", "moe_chain"):
             print(f"[bench] {name} workload", file=sys.stderr, flush=True)
             _, extra[name] = measure(name, builders[name], max(10, args.steps // 2), args.warmup)
             torch.cuda.empty_cache()

@@ -142,6 +142,86 @@ w4a16_status w4a16_grouped_gemm(const void *x, const int32_t *expert_offsets, co
                                 int64_t R, int64_t K, int64_t N, int64_t group_size, int dt,
                                 void *stream);
 
+/*
+ * ---- MoE fused-experts chain ---------------------------------------------
+ * The chain named by the pages: an expert GEMM, a fused SiLU-and-multiply
+ * and a second expert GEMM (pwwt.cn notes, §5, lmslim's fused_experts_impl),
+ * with the routing prep and the weighted sum of the experts' outputs
+ * (FlagGems-vLLM operator list, MoE table: moe_align_block_size, moe_sum;
+ * activation table: silu_and_mul).  Routing entry i = t*topk + k of token t
+ * selects expert topk_ids[i] (int32) with weight topk_w[i] (fp32); an id
+ * outside [0, E) is not routed and contributes nothing.  Requires
+ * 1 <= E <= 1024, topk >= 1, T*topk < 2^31.  Every device pointer below is
+ * 4-byte aligned (int/float arrays) or 16-byte aligned (16-bit tensors).
+ */
+
+/*
+ * Routing prep: routed entries ordered by (expert, entry index), numbered
+ * r = 0..R-1 (a stable counting sort, so the result is unique).
+ *   topk_ids        [T][topk] int32
+ *   expert_offsets  out, int32[E+1]: rows of expert e are
+ *                   offsets[e] .. offsets[e+1]-1, offsets[E] = R
+ *   sorted_ids      out, int32[T*topk]: entry index of row r (r < R)
+ *   row_of          out, int32[T*topk]: row of entry i, or -1 if not routed
+ */
+w4a16_status w4a16_moe_align(const int32_t *topk_ids, int64_t T, int64_t topk, int64_t E,
+                             int32_t *expert_offsets, int32_t *sorted_ids, int32_t *row_of, void *stream);
+
+/*
+ * x_sorted[r] = x[sorted_ids[r] / topk] for the routed rows r < offsets[E]
+ * (read on the device).  x [T][H], x_sorted [T*topk][H], dtype dt;
+ * H % 8 == 0.
+ */
+w4a16_status w4a16_moe_gather(const void *x, const int32_t *sorted_ids, const int32_t *expert_offsets,
+                              int64_t T, int64_t topk, int64_t E, int64_t H, void *x_sorted, int dt,
+                              void *stream);
+
+/*
+ * a[r][i] = silu(h[r][i]) * h[r][I + i], silu(g) = g / (1 + exp(-g)), in
+ * fp32, rounded once to dt (FlagGems-vLLM operator list, activation table:
+ * SiLU activation combined with an elementwise multiply; the gate is the
+ * first half).  h [R][2I], a [R][I]; I % 8 == 0.  row_count, if not NULL, is
+ * a DEVICE int32 holding the number of rows to process (at most R), e.g.
+ * expert_offsets + E.
+ */
+w4a16_status w4a16_silu_and_mul(const void *h, const int32_t *row_count, int64_t R, int64_t I, void *a,
+                                int dt, void *stream);
+
+/*
+ * out[t][n] = sum over routed k (ascending) of topk_w[t][k] * o[row_of[t*topk+k]][n],
+ * in fp32, rounded once to dt (FlagGems-vLLM operator list, MoE table:
+ * sum of the experts' outputs).  o [rows][N], out [T][N]; N % 8 == 0.
+ */
+w4a16_status w4a16_moe_sum(const void *o, const int32_t *row_of, const float *topk_w, int64_t T, int64_t topk,
+                           int64_t N, void *out, int dt, void *stream);
+
+/* Workspace of w4a16_fused_moe: offsets, the permutation, the token of every
+ * routed row and the intermediates h [T*topk][2I], a [T*topk][I],
+ * o [T*topk][H].  0 for invalid sizes. */
+size_t w4a16_fused_moe_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I);
+
+/*
+ * The whole chain for T tokens of width H through experts of width I:
+ *   h = x[token of row] . dequant(W13_e)  (grouped W4A16 over the routed
+ *                                    rows, which read their token's x row
+ *                                    directly; W13_e [H][2I], gate columns
+ *                                    first), rounded to dt
+ *   a = silu_and_mul(h)              rounded to dt
+ *   o = a . dequant(W2_e)            (grouped W4A16; W2_e [I][H]), rounded to dt
+ *   out[t] = moe_sum(o)              [T][H], dt
+ * w13_packed / w2_packed are the prepacked weights of all E experts (K = H,
+ * N = 2I and K = I, N = H); s13 [E][H/128][2I], s2 [E][I/128][H] in dt;
+ * z13 [E][H/128][I], z2 [E][I/128][H/2] uint4 zero points or both NULL
+ * (signedness as in w4a16_gemm).  Needs H % 128 == 0, I % 128 == 0.
+ * The workspace (at least w4a16_fused_moe_workspace_bytes) is used
+ * asynchronously; calls sharing one must be ordered on one stream.
+ */
+w4a16_status w4a16_fused_moe(const void *x, const int32_t *topk_ids, const float *topk_w,
+                             const void *w13_packed, const void *s13, const void *z13,
+                             const void *w2_packed, const void *s2, const void *z2, void *out,
+                             int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I, int64_t group_size,
+                             int dt, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

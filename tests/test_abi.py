@@ -132,3 +132,37 @@ def test_no_bit_cast_of_vector_subscript():
                 if re.search(r"__builtin_bit_cast\([^,]+,\s*[^()]*\[[^\]]+\]\s*\)", line):
                     bad.append(f"{f}:{i}: {line.strip()}")
     assert not bad, bad
+
+
+def test_moe_chain_validation():
+    """Host-side argument checks of the fused-experts entry points (no launch)."""
+    L = w4.lib()
+    # routing: E outside [1, 1024], topk < 1, misaligned or missing buffers
+    assert L.w4a16_moe_align(FAKE, 8, 2, 0, FAKE, FAKE, FAKE, None) == 2
+    assert L.w4a16_moe_align(FAKE, 8, 2, 1025, FAKE, FAKE, FAKE, None) == 3
+    assert L.w4a16_moe_align(FAKE, 8, 0, 4, FAKE, FAKE, FAKE, None) == 2
+    assert L.w4a16_moe_align(FAKE, 8, 2, 4, None, FAKE, FAKE, None) == 1
+    assert L.w4a16_moe_align(FAKE + 2, 8, 2, 4, FAKE, FAKE, FAKE, None) == 4
+    assert L.w4a16_moe_gather(FAKE, FAKE, FAKE, 8, 2, 4, 100, FAKE, 1, None) == 2      # H % 8
+    assert L.w4a16_moe_gather(FAKE, FAKE, FAKE, 8, 2, 4, 128, FAKE + 8, 1, None) == 4
+    assert L.w4a16_moe_gather(FAKE, FAKE, FAKE, 0, 2, 4, 128, FAKE, 1, None) == 0       # no tokens
+    assert L.w4a16_silu_and_mul(FAKE, None, 4, 12, FAKE, 1, None) == 2                 # I % 8
+    assert L.w4a16_silu_and_mul(FAKE, None, 4, 16, FAKE, 7, None) == 3
+    assert L.w4a16_silu_and_mul(FAKE, FAKE + 2, 4, 16, FAKE, 1, None) == 4
+    assert L.w4a16_silu_and_mul(FAKE, None, 0, 16, FAKE, 1, None) == 0
+    assert L.w4a16_moe_sum(FAKE, FAKE, FAKE, 4, 2, 20, FAKE, 1, None) == 2             # N % 8
+    assert L.w4a16_moe_sum(FAKE, None, FAKE, 4, 2, 16, FAKE, 1, None) == 1
+    ws = w4.w4a16_fused_moe_workspace_bytes(16, 2, 4, 256, 128)
+    assert ws > 16 * 2 * (2 * 128 + 128 + 256) * 2                                       # h, a, o
+    assert w4.w4a16_fused_moe_workspace_bytes(16, 2, 4, 256, 100) == 0
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 16, 2, 4, 256, 128, 128, 1, FAKE, ws, None]
+    a = list(args); a[15] = 64
+    assert L.w4a16_fused_moe(*a) == 3                                                   # group size
+    a = list(args); a[14] = 96
+    assert L.w4a16_fused_moe(*a) == 2                                                   # I % 128
+    a = list(args); a[5] = FAKE
+    assert L.w4a16_fused_moe(*a) == 1                                                   # one zero pointer only
+    a = list(args); a[18] = ws - 1
+    assert L.w4a16_fused_moe(*a) == 5
+    a = list(args); a[17] = FAKE + 8
+    assert L.w4a16_fused_moe(*a) == 4

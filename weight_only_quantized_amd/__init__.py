@@ -41,6 +41,13 @@ _SIGS = {
     "w4a16_msd_workspace_bytes": ([_i64, _i64, _i64, _i64], C.c_size_t),
     "w4a16_msd_gemm": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, C.c_size_t, _p], C.c_int),
     "w4a16_grouped_gemm": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, C.c_int, _p], C.c_int),
+    "w4a16_moe_align": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], C.c_int),
+    "w4a16_moe_gather": ([_p, _p, _p, _i64, _i64, _i64, _i64, _p, C.c_int, _p], C.c_int),
+    "w4a16_silu_and_mul": ([_p, _p, _i64, _i64, _p, C.c_int, _p], C.c_int),
+    "w4a16_moe_sum": ([_p, _p, _p, _i64, _i64, _i64, _p, C.c_int, _p], C.c_int),
+    "w4a16_fused_moe_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64], C.c_size_t),
+    "w4a16_fused_moe": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, C.c_int,
+                         _p, C.c_size_t, _p], C.c_int),
     "w4a16_test_unpack": ([_p, _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
     "w4a16_test_msd_intermediates": ([_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, C.c_size_t, _p], C.c_int),
     "w4a16_test_force_variant": ([C.c_int], C.c_int),
@@ -121,6 +128,38 @@ def w4a16_grouped_gemm(x, expert_offsets, w_packed, scale, zero, y, E, R, K, N, 
     _check(lib().w4a16_grouped_gemm(_ptr(x), _ptr(expert_offsets), _ptr(w_packed), _ptr(scale), _ptr(zero),
                                     _ptr(y), E, R, K, N, group_size, int(dt), _stream(stream)),
            "w4a16_grouped_gemm")
+
+
+def w4a16_moe_align(topk_ids, T, topk, E, expert_offsets, sorted_ids, row_of, stream=None):
+    _check(lib().w4a16_moe_align(_ptr(topk_ids), T, topk, E, _ptr(expert_offsets), _ptr(sorted_ids),
+                                 _ptr(row_of), _stream(stream)), "w4a16_moe_align")
+
+
+def w4a16_moe_gather(x, sorted_ids, expert_offsets, T, topk, E, H, x_sorted, dt=W4A16_BF16, stream=None):
+    _check(lib().w4a16_moe_gather(_ptr(x), _ptr(sorted_ids), _ptr(expert_offsets), T, topk, E, H,
+                                  _ptr(x_sorted), int(dt), _stream(stream)), "w4a16_moe_gather")
+
+
+def w4a16_silu_and_mul(h, row_count, R, I, a, dt=W4A16_BF16, stream=None):
+    _check(lib().w4a16_silu_and_mul(_ptr(h), _ptr(row_count), R, I, _ptr(a), int(dt), _stream(stream)),
+           "w4a16_silu_and_mul")
+
+
+def w4a16_moe_sum(o, row_of, topk_w, T, topk, N, out, dt=W4A16_BF16, stream=None):
+    _check(lib().w4a16_moe_sum(_ptr(o), _ptr(row_of), _ptr(topk_w), T, topk, N, _ptr(out), int(dt),
+                               _stream(stream)), "w4a16_moe_sum")
+
+
+def w4a16_fused_moe_workspace_bytes(T, topk, E, H, I) -> int:
+    return lib().w4a16_fused_moe_workspace_bytes(T, topk, E, H, I)
+
+
+def w4a16_fused_moe(x, topk_ids, topk_w, w13_packed, s13, z13, w2_packed, s2, z2, out, T, topk, E, H, I,
+                    group_size=GROUP_SIZE, dt=W4A16_BF16, workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().w4a16_fused_moe(_ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w13_packed), _ptr(s13), _ptr(z13),
+                                 _ptr(w2_packed), _ptr(s2), _ptr(z2), _ptr(out), T, topk, E, H, I, group_size,
+                                 int(dt), _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "w4a16_fused_moe")
 
 
 # ---- test hooks (include/w4a16_test.h) ----------------------------------------

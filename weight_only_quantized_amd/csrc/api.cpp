@@ -149,6 +149,106 @@ w4a16_status w4a16_grouped_gemm(const void *x, const int32_t *expert_offsets, co
                                         (hipStream_t)stream));
 }
 
+// ---- MoE fused-experts chain -------------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+w4a16_status check_route(int64_t T, int64_t topk, int64_t E) {
+    if (T < 0 || topk < 1 || E < 1) return W4A16_ERR_SHAPE;
+    if (E > w4::kMoeMaxExperts) return W4A16_ERR_UNSUPPORTED;
+    if (topk > (int64_t(1) << 20) || T > (int64_t(1) << 31) / topk - 1) return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+bool dt_ok(int dt) { return dt == W4A16_F16 || dt == W4A16_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+w4a16_status w4a16_moe_align(const int32_t *topk_ids, int64_t T, int64_t topk, int64_t E,
+                             int32_t *expert_offsets, int32_t *sorted_ids, int32_t *row_of, void *stream) {
+    w4a16_status st = check_route(T, topk, E);
+    if (st != W4A16_OK) return st;
+    if (!expert_offsets || (T > 0 && (!topk_ids || !sorted_ids || !row_of))) return W4A16_ERR_NULL;
+    if (!aligned(topk_ids, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_ids, 4) || !aligned(row_of, 4))
+        return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_moe_align(topk_ids, T, topk, E, expert_offsets, sorted_ids, row_of,
+                                        (hipStream_t)stream));
+}
+
+w4a16_status w4a16_moe_gather(const void *x, const int32_t *sorted_ids, const int32_t *expert_offsets,
+                              int64_t T, int64_t topk, int64_t E, int64_t H, void *x_sorted, int dt,
+                              void *stream) {
+    if (!dt_ok(dt)) return W4A16_ERR_UNSUPPORTED;
+    w4a16_status st = check_route(T, topk, E);
+    if (st != W4A16_OK) return st;
+    if (H <= 0 || H % 8 != 0 || H > (int64_t(1) << 30)) return W4A16_ERR_SHAPE;
+    if (T == 0) return W4A16_OK;
+    if (!x || !sorted_ids || !expert_offsets || !x_sorted) return W4A16_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(x_sorted, 16) || !aligned(sorted_ids, 4) || !aligned(expert_offsets, 4))
+        return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_moe_gather(x, sorted_ids, expert_offsets, T, topk, E, H, x_sorted,
+                                         (hipStream_t)stream));
+}
+
+w4a16_status w4a16_silu_and_mul(const void *h, const int32_t *row_count, int64_t R, int64_t I, void *a,
+                                int dt, void *stream) {
+    if (!dt_ok(dt)) return W4A16_ERR_UNSUPPORTED;
+    if (R < 0 || I <= 0 || I % 8 != 0 || I > (int64_t(1) << 30) || R > (int64_t(1) << 31)) return W4A16_ERR_SHAPE;
+    if (R == 0) return W4A16_OK;
+    if (!h || !a) return W4A16_ERR_NULL;
+    if (!aligned(h, 16) || !aligned(a, 16) || !aligned(row_count, 4)) return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_silu_and_mul(h, row_count, R, I, a, dt, (hipStream_t)stream));
+}
+
+w4a16_status w4a16_moe_sum(const void *o, const int32_t *row_of, const float *topk_w, int64_t T, int64_t topk,
+                           int64_t N, void *out, int dt, void *stream) {
+    if (!dt_ok(dt)) return W4A16_ERR_UNSUPPORTED;
+    if (T < 0 || topk < 1 || topk > (int64_t(1) << 20) || T > (int64_t(1) << 31) / topk - 1) return W4A16_ERR_SHAPE;
+    if (N <= 0 || N % 8 != 0 || N > (int64_t(1) << 30)) return W4A16_ERR_SHAPE;
+    if (T == 0) return W4A16_OK;
+    if (!o || !row_of || !topk_w || !out) return W4A16_ERR_NULL;
+    if (!aligned(o, 16) || !aligned(out, 16) || !aligned(row_of, 4) || !aligned(topk_w, 4)) return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_moe_sum(o, row_of, topk_w, T, topk, N, out, dt, (hipStream_t)stream));
+}
+
+size_t w4a16_fused_moe_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I) {
+    if (check_route(T, topk, E) != W4A16_OK) return 0;
+    if (check_kn(H, 2 * I, 128) != W4A16_OK || check_kn(I, H, 128) != W4A16_OK) return 0;
+    return w4::moe_plan(T, topk, E, H, I).total;
+}
+
+w4a16_status w4a16_fused_moe(const void *x, const int32_t *topk_ids, const float *topk_w,
+                             const void *w13_packed, const void *s13, const void *z13,
+                             const void *w2_packed, const void *s2, const void *z2, void *out,
+                             int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I, int64_t group_size,
+                             int dt, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!dt_ok(dt)) return W4A16_ERR_UNSUPPORTED;
+    w4a16_status st = check_route(T, topk, E);
+    if (st != W4A16_OK) return st;
+    // gate/up: K = H, N = 2I; down: K = I, N = H
+    if ((st = check_kn(H, 2 * I, group_size)) != W4A16_OK) return st;
+    if ((st = check_kn(I, H, group_size)) != W4A16_OK) return st;
+    if ((z13 == nullptr) != (z2 == nullptr)) return W4A16_ERR_NULL;
+    if (T == 0) return W4A16_OK;
+    if (!x || !topk_ids || !topk_w || !w13_packed || !s13 || !w2_packed || !s2 || !out) return W4A16_ERR_NULL;
+    if (!workspace || workspace_bytes < w4::moe_plan(T, topk, E, H, I).total) return W4A16_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w13_packed, 16) || !aligned(w2_packed, 16) ||
+        !aligned(workspace, 16) || !aligned(s13, 2) || !aligned(s2, 2) || !aligned(topk_ids, 4) ||
+        !aligned(topk_w, 4))
+        return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_fused_moe(x, topk_ids, topk_w, w13_packed, s13, z13, w2_packed, s2, z2, out, T, topk,
+                                        E, H, I, dt, workspace, (hipStream_t)stream));
+}
+
 // ---- test hooks -------------------------------------------------------------
 
 w4a16_status w4a16_test_unpack(const void *w_packed, void *w, int64_t E, int64_t K, int64_t N, int is_signed,

@@ -44,7 +44,7 @@ constexpr int kXcds = 8;
 template <int DT, bool ZERO, int BM, int BN, int WM, int WN, bool GROUPED>
 __global__ void __launch_bounds__(WM * WN * 64, 2)
 gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
-                 const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
+                 const int32_t *__restrict__ row_src, const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
                  const uint8_t *__restrict__ zero, uint16_t *__restrict__ y,
                  int64_t M, int64_t K, int64_t N, int E) {
     constexpr int NT = WM * WN * 64;
@@ -136,14 +136,21 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     // ---- activation staging -------------------------------------------------
     // Rows past the tile's end read the last valid row (finite data whose
     // result rows are never stored).
+    // Each lane stages the same rows in every group: their addresses are
+    // formed once.  With row_src the tile's row r reads x row row_src[r] (the
+    // gather of a routed token folded into the load).
     u32x4_t xr[XP];
+    const uint16_t *xrow[XP];
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+        const int id = p * NT + tid, r = id >> 4, c16 = id & 15;
+        const int64_t grow = row0 + r < row_end ? row0 + r : row_end - 1;
+        const int64_t src = row_src ? (int64_t)row_src[grow] : grow;
+        xrow[p] = x + src * K + c16 * 8;
+    }
     auto load_x = [&](int g) {
 #pragma unroll
-        for (int p = 0; p < XP; ++p) {
-            const int id = p * NT + tid, r = id >> 4, c16 = id & 15;
-            const int64_t grow = row0 + r < row_end ? row0 + r : row_end - 1;
-            xr[p] = ld128(x + grow * K + (int64_t)g * kGroup + c16 * 8);
-        }
+        for (int p = 0; p < XP; ++p) xr[p] = ld128(xrow[p] + (int64_t)g * kGroup);
     };
     // Sum of a value over the 16 lanes of a row (lanes 16i .. 16i+15) with
     // row rotations: every lane ends with the row's sum.
@@ -355,9 +362,9 @@ int tile_config_count() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0]))
 void set_tile_config(int idx) { g_tile_cfg = idx; }
 
 template <int DT, bool ZERO, bool GROUPED, int BM, int BN, int WM, int WN>
-static hipError_t tile_launch(const void *x, const int32_t *offsets, const void *wp, const void *scale,
-                              const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
-                              hipStream_t stream) {
+static hipError_t tile_launch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
+                              const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
+                              int64_t E, hipStream_t stream) {
     // grouped: every expert may end in a partial row tile, hence + E; the
     // items go on a 1-D grid rounded up to whole rounds over the XCDs
     const int64_t ncb = (N + BN - 1) / BN;
@@ -366,15 +373,15 @@ static hipError_t tile_launch(const void *x, const int32_t *offsets, const void 
     if (GROUPED && slots > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid = GROUPED ? dim3((unsigned)slots) : dim3((unsigned)mtiles, (unsigned)ncb);
     hipLaunchKernelGGL((gemm_tile_kernel<DT, ZERO, BM, BN, WM, WN, GROUPED>), grid, dim3(WM * WN * 64), 0,
-                       stream, (const uint16_t *)x, offsets, (const uint8_t *)wp, (const uint16_t *)scale,
+                       stream, (const uint16_t *)x, offsets, row_src, (const uint8_t *)wp, (const uint16_t *)scale,
                        (const uint8_t *)zero, (uint16_t *)y, M, K, N, (int)E);
     return hipGetLastError();
 }
 
 template <int DT, bool ZERO, bool GROUPED>
-static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const void *wp, const void *scale,
-                                const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
-                                hipStream_t stream) {
+static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
+                                const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
+                                int64_t E, hipStream_t stream) {
     int idx = g_tile_cfg;
     if (idx < 0 || idx >= tile_config_count()) {
         idx = 0;
@@ -388,7 +395,8 @@ static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const voi
     const TileCfg c = kTileCfgs[idx];
 #define W4_TILE(BMV, BNV, WMV, WNV)                                                                    \
     if (c.bm == BMV && c.bn == BNV && c.wm == WMV && c.wn == WNV)                                      \
-        return tile_launch<DT, ZERO, GROUPED, BMV, BNV, WMV, WNV>(x, offsets, wp, scale, zero, y, M, K, N, E, stream);
+        return tile_launch<DT, ZERO, GROUPED, BMV, BNV, WMV, WNV>(x, offsets, row_src, wp, scale, zero, y, M, K,   \
+                                                                  N, E, stream);
     W4_TILE(128, 256, 2, 4) W4_TILE(64, 256, 2, 4) W4_TILE(32, 256, 1, 4) W4_TILE(64, 128, 2, 2)
     W4_TILE(32, 128, 1, 4) W4_TILE(128, 128, 2, 2) W4_TILE(64, 256, 1, 4) W4_TILE(64, 128, 1, 2)
 #undef W4_TILE
@@ -396,21 +404,21 @@ static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const voi
 }
 
 template <bool GROUPED>
-static hipError_t tile_dispatch_dt(const void *x, const int32_t *offsets, const void *wp, const void *scale,
-                                   const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
-                                   int dt, hipStream_t stream) {
+static hipError_t tile_dispatch_dt(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
+                                   const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
+                                   int64_t E, int dt, hipStream_t stream) {
     if (dt == DT_BF16)
-        return zero ? tile_dispatch<DT_BF16, true, GROUPED>(x, offsets, wp, scale, zero, y, M, K, N, E, stream)
-                    : tile_dispatch<DT_BF16, false, GROUPED>(x, offsets, wp, scale, zero, y, M, K, N, E, stream);
-    return zero ? tile_dispatch<DT_F16, true, GROUPED>(x, offsets, wp, scale, zero, y, M, K, N, E, stream)
-                : tile_dispatch<DT_F16, false, GROUPED>(x, offsets, wp, scale, zero, y, M, K, N, E, stream);
+        return zero ? tile_dispatch<DT_BF16, true, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, stream)
+                    : tile_dispatch<DT_BF16, false, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, stream);
+    return zero ? tile_dispatch<DT_F16, true, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, stream)
+                : tile_dispatch<DT_F16, false, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, stream);
 }
 
 hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *wp, const void *scale,
                             const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
-                            int dt, hipStream_t stream) {
-    if (offsets) return tile_dispatch_dt<true>(x, offsets, wp, scale, zero, y, M, K, N, E, dt, stream);
-    return tile_dispatch_dt<false>(x, nullptr, wp, scale, zero, y, M, K, N, 1, dt, stream);
+                            int dt, hipStream_t stream, const int32_t *row_src) {
+    if (offsets) return tile_dispatch_dt<true>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, dt, stream);
+    return tile_dispatch_dt<false>(x, nullptr, row_src, wp, scale, zero, y, M, K, N, 1, dt, stream);
 }
 
 }  // namespace w4

@@ -22,11 +22,12 @@ hipError_t launch_gemm_small(const void *x, const void *wp, const void *scale, c
                              int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream);
 
 // LDS-staged tile kernel; grouped when offsets != nullptr (then M = R rows).
+// With row_src, row r of the product reads x row row_src[r] (gathered load).
 int tile_config_count();
 void set_tile_config(int idx);
 hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *wp, const void *scale,
                             const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
-                            int dt, hipStream_t stream);
+                            int dt, hipStream_t stream, const int32_t *row_src = nullptr);
 
 // MSD: decomposition, int8 products + merge, split-K reduction.
 struct MsdPlan {
@@ -48,5 +49,25 @@ hipError_t launch_msd(const void *x, const void *wp, const void *scale, void *y,
 hipError_t launch_msd_intermediates(const void *x, const void *wp, int64_t M, int64_t K, int64_t N,
                                     float *amax, int8_t *layers, int32_t *yint, void *workspace,
                                     hipStream_t stream);
+
+// MoE fused-experts chain: routing prep, gather, SiLU-and-multiply, weighted
+// sum, and the whole chain around two grouped GEMMs.
+constexpr int kMoeMaxExperts = 1024;
+struct MoePlan {
+    size_t off_offsets, off_sorted, off_row_of, off_tok, off_h, off_a, off_o, total;
+};
+MoePlan moe_plan(int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I);
+hipError_t launch_moe_align(const int32_t *ids, int64_t T, int64_t topk, int64_t E, int32_t *offsets,
+                            int32_t *sorted, int32_t *row_of, hipStream_t stream, int32_t *tok_of_row = nullptr);
+hipError_t launch_moe_gather(const void *x, const int32_t *sorted, const int32_t *offsets, int64_t T,
+                             int64_t topk, int64_t E, int64_t H, void *xs, hipStream_t stream);
+hipError_t launch_silu_and_mul(const void *h, const int32_t *row_count, int64_t R, int64_t I, void *a, int dt,
+                               hipStream_t stream);
+hipError_t launch_moe_sum(const void *o, const int32_t *row_of, const float *topk_w, int64_t T, int64_t topk,
+                          int64_t N, void *out, int dt, hipStream_t stream);
+hipError_t launch_fused_moe(const void *x, const int32_t *ids, const float *topk_w, const void *w13, const void *s13,
+                            const void *z13, const void *w2, const void *s2, const void *z2, void *out, int64_t T,
+                            int64_t topk, int64_t E, int64_t H, int64_t I, int dt, void *workspace,
+                            hipStream_t stream);
 
 }  // namespace w4

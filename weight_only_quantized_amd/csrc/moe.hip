@@ -1,0 +1,280 @@
+// moe.hip — the MoE fused-experts chain around the grouped W4A16 GEMM.
+//
+// The pages name the chain and its operators (pwwt.cn notes, §5: an expert
+// GEMM, a fused SiLU-and-multiply, a second expert GEMM; FlagGems-vLLM
+// operator list, MoE and activation tables: moe_align_block_size,
+// silu_and_mul, moe_sum).  Routing entry i = t*topk + k of token t picks
+// expert topk_ids[i] with weight topk_w[i]; ids outside [0, E) are not routed.
+//
+//   moe_align_kernel      routed entries ordered by (expert, i): offsets,
+//                         sorted entry of every row, row of every entry,
+//                         token of every row
+//   gemm_tile_kernel      gate/up projection  h = x[token of row] . W13_e
+//                         (grouped; the gather is folded into its x loads)
+//   silu_and_mul_kernel   a = silu(h[:, :I]) * h[:, I:]
+//   gemm_tile_kernel      down projection     o = a . W2_e          (grouped)
+//   moe_sum_kernel        out[t] = sum_k topk_w[t,k] * o[row of (t,k)]
+//
+// No block padding is needed: the grouped kernel forms its row tiles from the
+// expert offsets on the device, so "alignment" here is only the stable sort.
+// moe_gather_kernel (x rows copied into routed order) is the standalone
+// gather entry point; the chain itself does not need it.
+// Every stage reads the routed row count (offsets[E]) on the device; the host
+// never waits for the routing.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace w4 {
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignCache = 8192;                     // routing ids kept in LDS between the passes
+
+// One workgroup: per-expert counts (LDS atomics), an exclusive scan over the
+// experts, then a stable placement of 1024 entries at a time.  The first
+// kAlignCache ids are read from memory once and kept in LDS for the placement
+// pass.  Inside a wave the lanes holding the same expert are found with one
+// ballot per bit of the expert id; a lane's rank among them is the count of
+// such lanes below it, and the waves' per-expert counts (in LDS) order the
+// waves.
+__global__ void __launch_bounds__(kAlignThreads)
+moe_align_kernel(const int32_t *__restrict__ ids, int64_t n, int E, int topk, int32_t *__restrict__ offsets,
+                 int32_t *__restrict__ sorted, int32_t *__restrict__ row_of, int32_t *__restrict__ tok_of_row) {
+    constexpr int NW = kAlignThreads / 64;
+    __shared__ int idc[kAlignCache];
+    __shared__ int base[kMoeMaxExperts];              // counts, then the running position per expert
+    __shared__ int wcnt[NW][kMoeMaxExperts];          // per-wave counts of the current chunk
+    __shared__ int scan[kAlignThreads];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    for (int e = tid; e < E; e += kAlignThreads) {
+        base[e] = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) wcnt[w][e] = 0;
+    }
+    __syncthreads();
+    for (int64_t i = tid; i < n; i += kAlignThreads) {
+        const int e = ids[i];
+        if (i < kAlignCache) idc[i] = e;
+        if (e >= 0 && e < E) atomicAdd(&base[e], 1);
+    }
+    __syncthreads();
+    // exclusive scan over the experts (E <= kAlignThreads: one per thread)
+    const int cnt = tid < E ? base[tid] : 0;
+    scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kAlignThreads; off <<= 1) {
+        const int v = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) {
+        offsets[tid] = scan[tid] - cnt;
+        base[tid] = scan[tid] - cnt;
+    }
+    if (tid == kAlignThreads - 1) offsets[E] = scan[tid];
+    __syncthreads();
+
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int64_t c0 = 0; c0 < n; c0 += kAlignThreads) {
+        const int64_t i = c0 + tid;
+        const int e = i < n ? (i < kAlignCache ? idc[i] : ids[i]) : -1;
+        const bool valid = e >= 0 && e < E;
+        uint64_t same = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t ones = __ballot(valid && bit);
+            same &= bit ? ones : ~ones;
+        }
+        const int rank = __popcll(same & below);
+        if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
+        __syncthreads();
+        if (valid) {
+            int pos = base[e] + rank;
+            for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+            sorted[pos] = (int32_t)i;
+            row_of[i] = pos;
+            if (tok_of_row) tok_of_row[pos] = (int32_t)(i / topk);
+        } else if (i < n) {
+            row_of[i] = -1;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += kAlignThreads) {
+            int s = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                s += wcnt[w][ee];
+                wcnt[w][ee] = 0;
+            }
+            base[ee] += s;
+        }
+        __syncthreads();
+    }
+}
+
+// x_sorted[r] = x[sorted[r] / topk] for the routed rows r < offsets[E]; one
+// workgroup per row, 16 bytes per lane.
+__global__ void __launch_bounds__(256)
+moe_gather_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ sorted,
+                  const int32_t *__restrict__ offsets, int E, int topk, int64_t H,
+                  uint16_t *__restrict__ xs) {
+    const int64_t r = blockIdx.x;
+    if (r >= offsets[E]) return;                      // uniform: row not routed
+    const int64_t t = sorted[r] / topk;
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + t * H);
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(xs + r * H);
+    for (int64_t c = threadIdx.x; c < H / 8; c += 256) dst[c] = src[c];
+}
+
+// a[r][i] = RNE(silu(g) * u), g = h[r][i], u = h[r][I + i], in fp32, for the
+// first min(*row_count, R) rows (all R when row_count is NULL).
+template <int DT>
+__global__ void __launch_bounds__(256)
+silu_and_mul_kernel(const uint16_t *__restrict__ h, const int32_t *__restrict__ row_count, int64_t R,
+                    int64_t I, uint16_t *__restrict__ a) {
+    int64_t rows = R;
+    if (row_count) rows = *row_count < R ? *row_count : R;
+    const int64_t nv = I / 8;
+    const int64_t total = rows * nv;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+        const int64_t r = idx / nv, v = idx % nv;
+        const u32x4_t g = ld128(h + r * 2 * I + v * 8);
+        const u32x4_t u = ld128(h + r * 2 * I + I + v * 8);
+        u32x4_t out;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t gw = g[q], uw = u[q];
+            uint32_t res = 0;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const float gf = h2f<DT>((uint16_t)(gw >> (16 * half)));
+                const float uf = h2f<DT>((uint16_t)(uw >> (16 * half)));
+                const float s = gf / (1.0f + expf(-gf));
+                res |= (uint32_t)f2h<DT>(s * uf) << (16 * half);
+            }
+            out[q] = res;
+        }
+        *reinterpret_cast<u32x4_t *>(a + r * I + v * 8) = out;
+    }
+}
+
+// out[t][n] = RNE(sum over routed k, ascending, of topk_w[t,k] * o[row][n])
+// in fp32; 8 columns per lane.
+template <int DT>
+__global__ void __launch_bounds__(256)
+moe_sum_kernel(const uint16_t *__restrict__ o, const int32_t *__restrict__ row_of,
+               const float *__restrict__ topk_w, int64_t T, int topk, int64_t N, uint16_t *__restrict__ out) {
+    const int64_t nv = N / 8;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < T * nv; idx += (int64_t)gridDim.x * 256) {
+        const int64_t t = idx / nv, v = idx % nv;
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+        for (int k = 0; k < topk; ++k) {
+            const int32_t r = row_of[t * topk + k];
+            if (r < 0) continue;
+            const float wk = topk_w[t * topk + k];
+            const u32x4_t ov = ld128(o + (int64_t)r * N + v * 8);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t word = ov[q];
+                acc[2 * q] = __builtin_fmaf(wk, h2f<DT>((uint16_t)(word & 0xFFFFu)), acc[2 * q]);
+                acc[2 * q + 1] = __builtin_fmaf(wk, h2f<DT>((uint16_t)(word >> 16)), acc[2 * q + 1]);
+            }
+        }
+        u32x4_t res;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) res[q] = (uint32_t)f2h<DT>(acc[2 * q]) | (uint32_t)f2h<DT>(acc[2 * q + 1]) << 16;
+        *reinterpret_cast<u32x4_t *>(out + t * N + v * 8) = res;
+    }
+}
+
+static unsigned grid_for(int64_t work, int64_t per_block) {
+    int64_t b = (work + per_block - 1) / per_block;
+    if (b < 1) b = 1;
+    if (b > 8192) b = 8192;                           // grid-stride beyond this
+    return (unsigned)b;
+}
+
+hipError_t launch_moe_align(const int32_t *ids, int64_t T, int64_t topk, int64_t E, int32_t *offsets,
+                            int32_t *sorted, int32_t *row_of, hipStream_t stream, int32_t *tok_of_row) {
+    hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(kAlignThreads), 0, stream, ids, T * topk, (int)E,
+                       (int)topk, offsets, sorted, row_of, tok_of_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_gather(const void *x, const int32_t *sorted, const int32_t *offsets, int64_t T,
+                             int64_t topk, int64_t E, int64_t H, void *xs, hipStream_t stream) {
+    if (T * topk == 0) return hipSuccess;
+    hipLaunchKernelGGL(moe_gather_kernel, dim3((unsigned)(T * topk)), dim3(256), 0, stream,
+                       (const uint16_t *)x, sorted, offsets, (int)E, (int)topk, H, (uint16_t *)xs);
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_and_mul(const void *h, const int32_t *row_count, int64_t R, int64_t I, void *a, int dt,
+                               hipStream_t stream) {
+    if (R == 0) return hipSuccess;
+    const dim3 grid(grid_for(R * (I / 8), 256));
+    if (dt == DT_BF16)
+        hipLaunchKernelGGL(silu_and_mul_kernel<DT_BF16>, grid, dim3(256), 0, stream, (const uint16_t *)h, row_count,
+                           R, I, (uint16_t *)a);
+    else
+        hipLaunchKernelGGL(silu_and_mul_kernel<DT_F16>, grid, dim3(256), 0, stream, (const uint16_t *)h, row_count,
+                           R, I, (uint16_t *)a);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_sum(const void *o, const int32_t *row_of, const float *topk_w, int64_t T, int64_t topk,
+                          int64_t N, void *out, int dt, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const dim3 grid(grid_for(T * (N / 8), 256));
+    if (dt == DT_BF16)
+        hipLaunchKernelGGL(moe_sum_kernel<DT_BF16>, grid, dim3(256), 0, stream, (const uint16_t *)o, row_of, topk_w,
+                           T, (int)topk, N, (uint16_t *)out);
+    else
+        hipLaunchKernelGGL(moe_sum_kernel<DT_F16>, grid, dim3(256), 0, stream, (const uint16_t *)o, row_of, topk_w,
+                           T, (int)topk, N, (uint16_t *)out);
+    return hipGetLastError();
+}
+
+static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+MoePlan moe_plan(int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I) {
+    MoePlan p{};
+    const size_t n = (size_t)(T * topk);
+    p.off_offsets = 0;
+    p.off_sorted = align256(p.off_offsets + sizeof(int32_t) * (size_t)(E + 1));
+    p.off_row_of = align256(p.off_sorted + sizeof(int32_t) * n);
+    p.off_tok = align256(p.off_row_of + sizeof(int32_t) * n);
+    p.off_h = align256(p.off_tok + sizeof(int32_t) * n);
+    p.off_a = align256(p.off_h + 2 * n * (size_t)(2 * I));
+    p.off_o = align256(p.off_a + 2 * n * (size_t)I);
+    p.total = align256(p.off_o + 2 * n * (size_t)H);
+    return p;
+}
+
+hipError_t launch_fused_moe(const void *x, const int32_t *ids, const float *topk_w, const void *w13, const void *s13,
+                            const void *z13, const void *w2, const void *s2, const void *z2, void *out, int64_t T,
+                            int64_t topk, int64_t E, int64_t H, int64_t I, int dt, void *workspace,
+                            hipStream_t stream) {
+    const MoePlan p = moe_plan(T, topk, E, H, I);
+    uint8_t *ws = (uint8_t *)workspace;
+    int32_t *offsets = (int32_t *)(ws + p.off_offsets);
+    int32_t *sorted = (int32_t *)(ws + p.off_sorted);
+    int32_t *row_of = (int32_t *)(ws + p.off_row_of);
+    int32_t *tok = (int32_t *)(ws + p.off_tok);
+    void *h = ws + p.off_h, *a = ws + p.off_a, *o = ws + p.off_o;
+    const int64_t n = T * topk;                       // upper bound of the routed rows
+    hipError_t err = launch_moe_align(ids, T, topk, E, offsets, sorted, row_of, stream, tok);
+    // the grouped kernel takes its row tiles from the offsets (offsets[E] <= n)
+    // and reads row r of its x operand from token tok[r]
+    if (err == hipSuccess) err = launch_gemm_tile(x, offsets, w13, s13, z13, h, n, H, 2 * I, E, dt, stream, tok);
+    if (err == hipSuccess) err = launch_silu_and_mul(h, offsets + E, n, I, a, dt, stream);
+    if (err == hipSuccess) err = launch_gemm_tile(a, offsets, w2, s2, z2, o, n, I, H, E, dt, stream);
+    if (err == hipSuccess) err = launch_moe_sum(o, row_of, topk_w, T, topk, H, out, dt, stream);
+    return err;
+}
+
+}  // namespace w4

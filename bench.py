@@ -21,7 +21,10 @@ cpu_baseline = the CPU oracle on the same decode step (host cores).
 per_config adds the same measurement for the other workloads (tiny, prefill,
 MSD, MoE grouped, and the MoE fused-experts chain: routing prep, gather, gate/up
 grouped GEMM, SiLU and multiply, down grouped GEMM, weighted sum); they are
-reported for completeness, the headline is decode.  The chain's algorithmic
+reported for completeness, the headline is decode.  msd_page is the MSD
+page's own example shape (M=1, K=8192, N=12288); msd_page and msd_basic also time
+the page's basic pipeline (integer products written to memory, separate merge)
+next to the fused kernel.  The chain's algorithmic
 bytes: tokens in and out (T*H*2 each), routing ids and weights (T*topk*8), and
 the active experts' gate/up and down weights with their scales.
 
@@ -174,6 +177,46 @@ def msd_workload():
         j = i % len(wps)
         w4.w4a16_msd_gemm(x, wps[j], scs[j], y, p.M, p.K, p.N, 128, ws, nb)
     return [("msd", launch, dense_bytes(p.M, p.K, p.N, False), 2 * p.M * p.N * p.K)], len(wps)
+
+
+def _msd_calls(p, name):
+    """Fused MSD call and the page's basic pipeline (products through memory)
+    on the same problem."""
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    wp = _prepack(p, _dev(p.w.reshape(-1)))
+    x, sc = _dev(p.x), _dev(p.scale)
+    y = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda:0")
+    nb = w4.w4a16_msd_workspace_bytes(p.M, p.K, p.N)
+    nbb = w4.w4a16_test_msd_basic_workspace_bytes(p.M, p.K, p.N)
+    ws = torch.empty(max(nb, nbb), dtype=torch.uint8, device="cuda:0")
+    wps = _copies(wp, wp.numel() + sc.numel() * 2)
+    scs = [sc] + [sc.clone() for _ in range(len(wps) - 1)]
+
+    def fused(i):
+        j = i % len(wps)
+        w4.w4a16_msd_gemm(x, wps[j], scs[j], y, p.M, p.K, p.N, 128, ws, nb)
+
+    def basic(i):
+        j = i % len(wps)
+        w4.w4a16_test_msd_basic(x, wps[j], scs[j], y, p.M, p.K, p.N, 128, ws, nbb)
+    nbytes, flops = dense_bytes(p.M, p.K, p.N, False), 2 * p.M * p.N * p.K
+    return [(name, fused, nbytes, flops), (name + "_basic", basic, nbytes, flops)], len(wps)
+
+
+def msd_page_workload():
+    """The MSD page's own example shape (M=1, K=8192, N=12288), fused and
+    basic pipelines."""
+    import synth
+    return _msd_calls(synth.msd_page_example(), "msd_page")
+
+
+def msd_basic_workload():
+    """The MSD configuration (M=64, K=N=8192) through the basic pipeline, next
+    to the fused kernel."""
+    import synth
+    return _msd_calls(synth.msd(), "msd")
 
 
 def moe_workload():
@@ -362,7 +405,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["decode", "tiny", "prefill", "msd", "moe", "moe_chain"], default=None,
+    ap.add_argument("--only", choices=["decode", "tiny", "prefill", "msd", "moe", "moe_chain", "msd_page",
+                                       "msd_basic"], default=None,
                     help="run only this workload (profiling); no JSON headline unless decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-config extras")
@@ -391,7 +435,8 @@ def main():
         return
 
     builders = {"decode": decode_workload, "tiny": tiny_workload, "prefill": prefill_workload,
-                "msd": msd_workload, "moe": moe_workload, "moe_chain": moe_chain_workload}
+                "msd": msd_workload, "moe": moe_workload, "moe_chain": moe_chain_workload,
+                "msd_page": msd_page_workload, "msd_basic": msd_basic_workload}
     if args.only and args.only != "decode":
         _, out = measure(args.only, builders[args.only], args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **out}), flush=True)
@@ -407,7 +452,7 @@ def main():
 
     extra = {}
     if not args.no_extra and not args.only:
-        for name in ("tiny", "prefill", "msd", "moe", "moe_chain"):
+        for name in ("tiny", "prefill", "msd", "moe", "moe_chain", "msd_page", "msd_basic"):
             print(f"[bench] {name} workload", file=sys.stderr, flush=True)
             _, extra[name] = measure(name, builders[name], max(10, args.steps // 2), args.warmup)
             torch.cuda.empty_cache()

@@ -29,6 +29,20 @@ w4a16_status w4a16_test_msd_intermediates(const void *x, const void *w_packed, i
                                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The MSD page's basic pipeline (§6.1 stage order with the per-group integer
+ * products written to memory, as its Y_int workspace does, then a separate
+ * merge kernel), for comparison with w4a16_msd_gemm, whose merge is fused
+ * into the product kernel so the products never leave registers.  Same
+ * arguments and result definition as w4a16_msd_gemm; the workspace (size from
+ * the query below) also holds Y_int [K/128][3][M][N] int32.  scale and y need
+ * 8-byte alignment.  Benchmarks and tests only.
+ */
+size_t w4a16_test_msd_basic_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
+w4a16_status w4a16_test_msd_basic(const void *x, const void *w_packed, const void *antiquant_scale, void *y,
+                                  int64_t M, int64_t K, int64_t N, int64_t group_size, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
  * Force the dense GEMM kernel family for subsequent calls in this process:
  * 0 = automatic (default), 1 = small-M split-K kernel, 2 = tile kernel.
  * Not thread-safe; tests and benchmarks only.  Returns the previous value.

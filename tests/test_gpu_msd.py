@@ -130,3 +130,23 @@ def test_msd_configs(orc, cfg):
         _check_msd(orc, p, f"msd_cfg{cfg}")
     finally:
         w4.w4a16_test_msd_config(-1)
+
+
+@pytest.mark.parametrize("which", ["page", "shape", "msd"])
+def test_msd_basic_pipeline(orc, which):
+    """The page's basic pipeline (products through memory, separate merge)
+    meets the same bar against the oracle as the fused kernel."""
+    import weight_only_quantized_amd as w4
+    from gpu_helpers import Dev, DEV, check_tol, to_host_u16
+    p = {"page": synth.msd_page_example, "shape": lambda: synth.msd(M=33, K=2048, N=192, seed=4),
+         "msd": synth.msd}[which]()
+    print(f"[case] msd_basic {which} M={p.M} K={p.K} N={p.N}", flush=True)
+    d = Dev(p)
+    nbytes = w4.w4a16_test_msd_basic_workspace_bytes(p.M, p.K, p.N)
+    assert nbytes >= w4.w4a16_msd_workspace_bytes(p.M, p.K, p.N) + 4 * 3 * p.M * p.N * (p.K // 128)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    y = d.new_y()
+    w4.w4a16_test_msd_basic(d.x, d.wp, d.scale, y, p.M, p.K, p.N, 128, ws, nbytes)
+    torch.cuda.synchronize()
+    _, y_ref = orc.msd(p.x, p.w, p.scale, p.M, p.K, p.N)
+    check_tol(to_host_u16(y), y_ref, synth.F16, label=f"msd_basic_{which}")

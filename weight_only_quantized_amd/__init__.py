@@ -50,6 +50,8 @@ _SIGS = {
                          _p, C.c_size_t, _p], C.c_int),
     "w4a16_test_unpack": ([_p, _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
     "w4a16_test_msd_intermediates": ([_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, C.c_size_t, _p], C.c_int),
+    "w4a16_test_msd_basic_workspace_bytes": ([_i64, _i64, _i64, _i64], C.c_size_t),
+    "w4a16_test_msd_basic": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, C.c_size_t, _p], C.c_int),
     "w4a16_test_force_variant": ([C.c_int], C.c_int),
     "w4a16_test_variant_name": ([_i64, _i64, _i64, C.c_int, C.c_int], C.c_char_p),
     "w4a16_test_small_config": ([C.c_int], C.c_int),
@@ -174,6 +176,17 @@ def w4a16_test_msd_intermediates(x, w_packed, M, K, N, amax, layers, yint, works
     _check(lib().w4a16_test_msd_intermediates(_ptr(x), _ptr(w_packed), M, K, N, group_size, _ptr(amax),
                                               _ptr(layers), _ptr(yint), _ptr(workspace), int(workspace_bytes),
                                               _stream(stream)), "w4a16_test_msd_intermediates")
+
+
+def w4a16_test_msd_basic_workspace_bytes(M, K, N, group_size=GROUP_SIZE) -> int:
+    return lib().w4a16_test_msd_basic_workspace_bytes(M, K, N, group_size)
+
+
+def w4a16_test_msd_basic(x, w_packed, antiquant_scale, y, M, K, N, group_size=GROUP_SIZE, workspace=None,
+                         workspace_bytes=0, stream=None):
+    _check(lib().w4a16_test_msd_basic(_ptr(x), _ptr(w_packed), _ptr(antiquant_scale), _ptr(y), M, K, N, group_size,
+                                      _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "w4a16_test_msd_basic")
 
 
 def w4a16_test_force_variant(variant: int) -> int:

@@ -276,6 +276,27 @@ w4a16_status w4a16_test_msd_intermediates(const void *x, const void *w_packed, i
                                                 (hipStream_t)stream));
 }
 
+size_t w4a16_test_msd_basic_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+    if (check_kn(K, N, group_size) != W4A16_OK || M <= 0 || M > (int64_t(1) << 24)) return 0;
+    return w4::msd_basic_workspace_bytes(M, K, N);
+}
+
+w4a16_status w4a16_test_msd_basic(const void *x, const void *w_packed, const void *antiquant_scale, void *y,
+                                  int64_t M, int64_t K, int64_t N, int64_t group_size, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    w4a16_status st = check_kn(K, N, group_size);
+    if (st != W4A16_OK) return st;
+    if (M < 0 || M > (int64_t(1) << 24)) return W4A16_ERR_SHAPE;
+    if (M == 0) return W4A16_OK;
+    if (!x || !w_packed || !antiquant_scale || !y) return W4A16_ERR_NULL;
+    if (!workspace || workspace_bytes < w4::msd_basic_workspace_bytes(M, K, N)) return W4A16_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(antiquant_scale, 8) || !aligned(y, 8) ||
+        !aligned(workspace, 16))
+        return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_msd_basic(x, w_packed, antiquant_scale, y, M, K, N, workspace, (hipStream_t)stream));
+}
+
 int w4a16_test_force_variant(int variant) { return g_force_variant.exchange(variant); }
 
 const char *w4a16_test_variant_name(int64_t M, int64_t K, int64_t N, int dt, int has_zero) {

@@ -46,6 +46,10 @@ int msd_config_count();
 void set_msd_config(int idx);
 hipError_t launch_msd(const void *x, const void *wp, const void *scale, void *y, int64_t M, int64_t K,
                       int64_t N, void *workspace, hipStream_t stream);
+// Basic MSD pipeline (integer products through memory, separate merge).
+size_t msd_basic_workspace_bytes(int64_t M, int64_t K, int64_t N);
+hipError_t launch_msd_basic(const void *x, const void *wp, const void *scale, void *y, int64_t M, int64_t K,
+                            int64_t N, void *workspace, hipStream_t stream);
 hipError_t launch_msd_intermediates(const void *x, const void *wp, int64_t M, int64_t K, int64_t N,
                                     float *amax, int8_t *layers, int32_t *yint, void *workspace,
                                     hipStream_t stream);

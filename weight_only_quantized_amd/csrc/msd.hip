@@ -381,6 +381,43 @@ msd_reduce_kernel(const float *__restrict__ part, uint16_t *__restrict__ y, int6
         if (row0 + r < M) y[(row0 + r) * N + col] = f2h<DT_F16>(acc[r]);
 }
 
+// Basic pipeline (the MSD page's §6.1 stage order with the integer products
+// passed through memory, for comparison with the fused kernel): merge of the
+// per-group products Y_j [G][3][M][N] (signed, eq.9) read back from memory,
+//   y[m][n] = RNE( sum_g s[g][n] * (Y_1 c_1 + Y_2 c_2 + Y_3 c_3) ),
+// c_j = A_max / (7.49 * 14.98^(j-1)) from the decomposition (eqs.10-11), in
+// fp32; 4 columns per lane.
+__global__ void __launch_bounds__(256)
+msd_merge_kernel(const int32_t *__restrict__ yint, const float *__restrict__ coef,
+                 const uint16_t *__restrict__ scale, uint16_t *__restrict__ y, int64_t M, int64_t Mpad,
+                 int64_t N, int64_t G) {
+    const int64_t nv = N / 4;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < M * nv; idx += (int64_t)gridDim.x * 256) {
+        const int64_t m = idx / nv, c0 = (idx % nv) * 4;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int64_t g = 0; g < G; ++g) {
+            const float k0 = coef[(g * 4 + 0) * Mpad + m], k1 = coef[(g * 4 + 1) * Mpad + m],
+                        k2 = coef[(g * 4 + 2) * Mpad + m];
+            const i32x4_t y0 = *reinterpret_cast<const i32x4_t *>(yint + ((g * 3 + 0) * M + m) * N + c0);
+            const i32x4_t y1 = *reinterpret_cast<const i32x4_t *>(yint + ((g * 3 + 1) * M + m) * N + c0);
+            const i32x4_t y2 = *reinterpret_cast<const i32x4_t *>(yint + ((g * 3 + 2) * M + m) * N + c0);
+            const uint2 sv = *reinterpret_cast<const uint2 *>(scale + g * N + c0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float t = (float)y0[j] * k0;
+                t = __builtin_fmaf((float)y1[j], k1, t);
+                t = __builtin_fmaf((float)y2[j], k2, t);
+                const uint32_t sw = j < 2 ? sv.x : sv.y;
+                acc[j] = __builtin_fmaf(h2f<DT_F16>((uint16_t)(sw >> (16 * (j & 1)))), t, acc[j]);
+            }
+        }
+        uint2 out;
+        out.x = (uint32_t)f2h<DT_F16>(acc[0]) | (uint32_t)f2h<DT_F16>(acc[1]) << 16;
+        out.y = (uint32_t)f2h<DT_F16>(acc[2]) | (uint32_t)f2h<DT_F16>(acc[3]) << 16;
+        *reinterpret_cast<uint2 *>(y + m * N + c0) = out;
+    }
+}
+
 // Plain-order copy of the layers for the test hook.
 __global__ void msd_layers_plain_kernel(const int8_t *__restrict__ src, int8_t *__restrict__ dst, int64_t M,
                                         int64_t Mpad, int64_t K) {
@@ -507,6 +544,29 @@ hipError_t launch_msd(const void *x, const void *wp, const void *scale, void *y,
     const int64_t nlanes = slice / 4;
     hipLaunchKernelGGL(msd_reduce_kernel, dim3((unsigned)((nlanes + 255) / 256)), dim3(256), 0, stream,
                        (const float *)(ws + p.off_part), (uint16_t *)y, M, N, p.mt, nlanes, slice, p.ksplit);
+    return hipGetLastError();
+}
+
+size_t msd_basic_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    return align_up(msd_workspace_bytes(M, K, N), 256) + sizeof(int32_t) * (size_t)(K / kGroup) * 3 * (size_t)M * (size_t)N;
+}
+
+hipError_t launch_msd_basic(const void *x, const void *wp, const void *scale, void *y, int64_t M, int64_t K,
+                            int64_t N, void *workspace, hipStream_t stream) {
+    const MsdPlan p = msd_plan(M, K, N);
+    uint8_t *ws = (uint8_t *)workspace;
+    int32_t *yint = (int32_t *)(ws + align_up(msd_workspace_bytes(M, K, N), 256));
+    hipError_t err = msd_pre(p, x, ws, M, K, stream);
+    if (err != hipSuccess) return err;
+    err = msd_gemm_launch<true>(p, (const int8_t *)(ws + p.off_layers), (const float *)(ws + p.off_coef),
+                                (const int32_t *)(ws + p.off_lsum), wp, nullptr, nullptr, nullptr, yint, M, K, N,
+                                p.ksplit, p.gps, stream);
+    if (err != hipSuccess) return err;
+    int64_t blocks = (M * (N / 4) + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(msd_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, yint,
+                       (const float *)(ws + p.off_coef), (const uint16_t *)scale, (uint16_t *)y, M, p.mpad, N,
+                       K / kGroup);
     return hipGetLastError();
 }
 

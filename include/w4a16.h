@@ -5,8 +5,10 @@
  * Computes Y = X . dequant(W) with
  *   X     fp16 or bf16 activations,
  *   W     int4 weights, one scale (same dtype as X) and optionally one uint4
- *         zero point per group of 128 consecutive K rows and per column,
- *   dequant(W)[k][n] = (q[k][n] - z[k/128][n]) * s[k/128][n],
+ *         zero point per group of `group_size` consecutive K rows and per
+ *         column (group_size a multiple of 128; group_size == K gives one
+ *         scale per column),
+ *   dequant(W)[k][n] = (q[k][n] - z[k/gs][n]) * s[k/gs][n], gs = group_size,
  *   fp32 accumulation, Y rounded to the dtype of X.
  * Sources: "Humming: open-source library for quantized inference" (vLLM /
  * Ant Group article), section on the standard quantization descriptor (group
@@ -28,7 +30,10 @@
  *    `zero` is given the weights are unsigned in [0, 15] (prepacked with
  *    is_signed = 0) and zero[G][N/2] holds uint4 zero points packed like w.
  *  - Shape rules: K > 0, K % 128 == 0, N > 0, N % 64 == 0, M (or R) >= 0,
- *    E >= 1, group_size == 128.  M == 0 (or an expert without rows) is a
+ *    E >= 1.  group_size: a multiple of 128 dividing K for w4a16_gemm and
+ *    w4a16_grouped_gemm (else W4A16_ERR_UNSUPPORTED, or W4A16_ERR_SHAPE when
+ *    it does not divide K); exactly 128 for the MSD path (whose page fixes
+ *    the group at 128 rows) and the MoE chain.  M == 0 (or an expert without rows) is a
  *    no-op that returns W4A16_OK.
  *  - Alignment: x, w_packed, workspace 16 bytes; scale, y 2 bytes.
  *  - Errors: every argument is checked on the host before anything is
@@ -89,8 +94,8 @@ w4a16_status w4a16_prepack(const void *w, void *w_packed, int64_t E, int64_t K, 
  * Dense W4A16 GEMM: y[M][N] = x[M][K] . dequant(W).
  *   x        [M][K] fp16/bf16 (dtype dt)
  *   w_packed prepacked weights (E = 1)
- *   scale    [K/128][N], dtype dt
- *   zero     [K/128][N/2] uint4 or NULL (see Signedness)
+ *   scale    [K/group_size][N], dtype dt
+ *   zero     [K/group_size][N/2] uint4 or NULL (see Signedness)
  *   y        [M][N], dtype dt
  * Small M runs a split-K matrix-core kernel whose waves reduce through LDS;
  * large M runs an LDS-staged tile kernel (see the design notes).
@@ -131,8 +136,8 @@ w4a16_status w4a16_msd_gemm(const void *x, const void *w_packed, const void *ant
  *   expert_offsets  DEVICE int32[E+1], offsets[0] = 0, non-decreasing,
  *                   offsets[E] = R (read on the device only: no host sync)
  *   w_packed        prepacked weights of all E experts (E*K*N/2 bytes)
- *   scale           [E][K/128][N], dtype dt
- *   zero            [E][K/128][N/2] or NULL
+ *   scale           [E][K/group_size][N], dtype dt
+ *   zero            [E][K/group_size][N/2] or NULL
  *   y               [R][N], dtype dt; rows of experts without rows: none
  * Experts with no rows cost nothing beyond a skipped tile slot (Humming
  * article: dense and MoE workloads share the kernel components).

@@ -100,6 +100,7 @@ class Problem:
     E: int = 1
     offsets: Optional[np.ndarray] = None   # int32 [E+1] for grouped
     name: str = ""
+    group: int = GROUP                     # K rows per scale group (multiple of 128)
 
     @property
     def signed(self) -> bool:
@@ -107,7 +108,7 @@ class Problem:
 
     @property
     def G(self) -> int:
-        return self.K // GROUP
+        return self.K // self.group
 
 
 def _normal(g: np.random.Generator, shape) -> np.ndarray:
@@ -131,11 +132,12 @@ def _scales(seed, shape, lo, hi, dtype, tag="s"):
 
 def make_dense(M, K, N, dtype, signed=True, scale_range=(0.002, 0.01),
                zero_range=(6, 9), seed=0, outlier_frac=0.0, outlier_mult=20.0,
-               x_scale=1.0, name="") -> Problem:
+               x_scale=1.0, name="", group=GROUP) -> Problem:
     """Dense W4A16 problem: x ~ N(0,1) (optionally with outliers), W int4,
-    scale uniform, zero points uniform integers (unsigned weights only)."""
-    assert K % GROUP == 0 and N % 2 == 0
-    G = K // GROUP
+    scale uniform, zero points uniform integers (unsigned weights only); one
+    scale (and zero) row per ``group`` K rows."""
+    assert K % group == 0 and N % 2 == 0
+    G = K // group
     x = _normal(stream(seed, "x"), (M, K)) * np.float32(x_scale)
     if outlier_frac > 0:
         mask = stream(seed, "mask").random((M, K)) < outlier_frac
@@ -147,7 +149,7 @@ def make_dense(M, K, N, dtype, signed=True, scale_range=(0.002, 0.01),
     if not signed:
         zq = stream(seed, "z").integers(zero_range[0], zero_range[1] + 1, size=(G, N), dtype=np.int8)
         z = pack_nibbles(zq.view(np.uint8))
-    return Problem(x=xb, w=w, scale=s, zero=z, q=q, M=M, K=K, N=N, dtype=dtype, name=name)
+    return Problem(x=xb, w=w, scale=s, zero=z, q=q, M=M, K=K, N=N, dtype=dtype, name=name, group=group)
 
 
 def zipf_routing(tokens, experts, topk, alpha, seed):
@@ -165,11 +167,11 @@ def zipf_routing(tokens, experts, topk, alpha, seed):
 
 def make_grouped(E, tokens, topk, K, N, dtype, alpha=1.1, signed=True,
                  scale_range=(0.002, 0.01), seed=0, name="",
-                 counts: Optional[np.ndarray] = None) -> Problem:
+                 counts: Optional[np.ndarray] = None, group=GROUP) -> Problem:
     """MoE grouped problem.  Rows of ``x`` are token activations gathered and
     sorted by (expert, token); ``offsets[e]..offsets[e+1]`` are expert e's rows.
     If ``counts`` is given it overrides the routing draw (rows per expert)."""
-    G = K // GROUP
+    G = K // group
     if counts is None:
         route = zipf_routing(tokens, E, topk, alpha, seed)
         pairs = sorted((int(e), t) for t in range(tokens) for e in route[t])
@@ -192,7 +194,7 @@ def make_grouped(E, tokens, topk, K, N, dtype, alpha=1.1, signed=True,
         zq = stream(seed, "z").integers(6, 10, size=(E, G, N), dtype=np.int8)
         z = pack_nibbles(zq.view(np.uint8))
     return Problem(x=xb, w=w, scale=s, zero=z, q=q, M=R, K=K, N=N, dtype=dtype,
-                   E=E, offsets=offsets, name=name)
+                   E=E, offsets=offsets, name=name, group=group)
 
 
 # ---------------------------------------------------------------------------

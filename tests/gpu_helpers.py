@@ -50,14 +50,14 @@ class Dev:
     def gemm(self, y=None):
         p = self.p
         y = self.new_y() if y is None else y
-        w4.w4a16_gemm(self.x, self.wp, self.scale, self.zero, y, p.M, p.K, p.N, 128, p.dtype)
+        w4.w4a16_gemm(self.x, self.wp, self.scale, self.zero, y, p.M, p.K, p.N, p.group, p.dtype)
         return y
 
     def grouped(self, y=None):
         p = self.p
         y = self.new_y() if y is None else y
         w4.w4a16_grouped_gemm(self.x, self.offsets, self.wp, self.scale, self.zero, y, p.E, p.M, p.K, p.N,
-                              128, p.dtype)
+                              p.group, p.dtype)
         return y
 
     def msd(self, y=None, ws=None):

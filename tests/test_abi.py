@@ -54,6 +54,8 @@ FAKE = 1 << 40          # never dereferenced: validation fails first
 
 @pytest.mark.parametrize("kw,status", [
     (dict(group_size=64), 3),
+    (dict(group_size=192), 3),            # not a multiple of 128
+    (dict(group_size=512), 2),            # does not divide K = 256
     (dict(dt=7), 3),
     (dict(K=100), 2),
     (dict(K=0), 2),
@@ -166,3 +168,15 @@ def test_moe_chain_validation():
     assert L.w4a16_fused_moe(*a) == 5
     a = list(args); a[17] = FAKE + 8
     assert L.w4a16_fused_moe(*a) == 4
+
+
+def test_group_sizes_accepted_by_gemm_only():
+    """Scale groups that are multiples of 128 dividing K pass validation for the
+    dense and grouped GEMMs (they fail later only on the fake pointers'
+    alignment), while the MSD path keeps group 128."""
+    L = w4.lib()
+    for gs in (128, 256, 512, 1024):
+        assert L.w4a16_gemm(FAKE, FAKE, FAKE + 1, None, FAKE, 4, 1024, 256, gs, 0, None) == 4
+        assert L.w4a16_grouped_gemm(FAKE, FAKE, FAKE, FAKE + 1, None, FAKE, 4, 16, 1024, 256, gs, 1, None) == 4
+    ws = w4.w4a16_msd_workspace_bytes(4, 1024, 256)
+    assert L.w4a16_msd_gemm(FAKE, FAKE, FAKE, FAKE, 4, 1024, 256, 256, FAKE, ws, None) == 3

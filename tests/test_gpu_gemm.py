@@ -21,7 +21,7 @@ def _run_and_check(orc, p, label, variant=0):
         torch.cuda.synchronize()
     finally:
         w4.w4a16_test_force_variant(prev)
-    _, y_ref = orc.w4a16(p.x, p.w, p.scale, p.zero, p.M, p.K, p.N, p.dtype)
+    _, y_ref = orc.w4a16(p.x, p.w, p.scale, p.zero, p.M, p.K, p.N, p.dtype, group=p.group)
     return check_tol(to_host_u16(y), y_ref, p.dtype, label=label), d, y
 
 
@@ -89,7 +89,7 @@ def test_unit_rows_bit_exact(orc, dt, signed, variant):
         y = to_host_u16(d.gemm())
     finally:
         w4.w4a16_test_force_variant(prev)
-    _, y_ref = orc.w4a16(p.x, p.w, p.scale, p.zero, p.M, p.K, p.N, p.dtype)
+    _, y_ref = orc.w4a16(p.x, p.w, p.scale, p.zero, p.M, p.K, p.N, p.dtype, group=p.group)
     assert np.array_equal(y, y_ref)
 
 
@@ -138,3 +138,20 @@ def test_tile_configs(orc, cfg, dt, signed):
         _run_and_check(orc, p, f"tile_cfg{cfg}", variant=2)
     finally:
         w4.w4a16_test_tile_config(-1)
+
+
+@pytest.mark.parametrize("M,K,N,dt,signed,group,variant", [
+    (1, 1024, 256, synth.BF16, False, 256, 0),
+    (4, 2048, 320, synth.F16, True, 2048, 0),          # one scale per column
+    (16, 4096, 512, synth.BF16, False, 512, 0),
+    (4, 4096, 14336, synth.BF16, False, 4096, 0),      # decode shape, per-column scales and zeros
+    (100, 1024, 192, synth.BF16, True, 1024, 0),
+    (300, 512, 256, synth.F16, False, 256, 0),
+    (8, 1024, 256, synth.BF16, True, 512, 2),          # tile kernel forced at small M
+    (40, 768, 128, synth.BF16, False, 384, 0),         # three 128-row groups per scale group
+])
+def test_group_sizes(orc, M, K, N, dt, signed, group, variant):
+    """Scale groups that are multiples of 128 rows (up to one scale per
+    column): both kernel families against the oracle at the same group."""
+    p = synth.make_dense(M, K, N, dt, signed=signed, seed=M + group, group=group)
+    _run_and_check(orc, p, f"group{group}_{M}x{K}x{N}", variant=variant)

@@ -15,7 +15,7 @@ def _check(orc, p, label):
     d = Dev(p)
     y = d.grouped(d.new_y(fill=0))
     torch.cuda.synchronize()
-    _, y_ref = orc.grouped(p.x, p.offsets, p.w, p.scale, p.zero, p.E, p.M, p.K, p.N, p.dtype)
+    _, y_ref = orc.grouped(p.x, p.offsets, p.w, p.scale, p.zero, p.E, p.M, p.K, p.N, p.dtype, group=p.group)
     return check_tol(to_host_u16(y), y_ref, p.dtype, label=label)
 
 
@@ -70,3 +70,12 @@ def test_fewer_items_than_xcds(orc, counts, n):
     p = synth.make_grouped(len(counts), sum(counts), 1, 256, n, synth.BF16, signed=True, counts=counts,
                            seed=sum(counts))
     _check(orc, p, f"grouped_small_{counts[:4]}_{n}")
+
+
+@pytest.mark.parametrize("group,dt,signed", [(256, synth.BF16, True), (1024, synth.F16, False)])
+def test_grouped_group_sizes(orc, group, dt, signed):
+    """Grouped GEMM with scale groups of 256 rows and with one scale per column."""
+    counts = [5, 0, 70, 33, 1, 129]
+    p = synth.make_grouped(len(counts), sum(counts), 1, 1024, 320, dt, signed=signed, counts=counts,
+                           seed=group, group=group)
+    _check(orc, p, f"grouped_group{group}")

@@ -51,6 +51,18 @@ w4a16_status check_kn(int64_t K, int64_t N, int64_t group_size) {
     return W4A16_OK;
 }
 
+// Scale groups for the dense and grouped GEMMs: any multiple of 128 that
+// divides K (group_size == K is one scale per column).  On success *gm is the
+// number of 128-row groups per scale group.
+w4a16_status check_kn_groups(int64_t K, int64_t N, int64_t group_size, int *gm) {
+    if (group_size < 128 || group_size % 128 != 0) return W4A16_ERR_UNSUPPORTED;
+    w4a16_status st = check_kn(K, N, 128);
+    if (st != W4A16_OK) return st;
+    if (K % group_size != 0) return W4A16_ERR_SHAPE;
+    *gm = (int)(group_size / 128);
+    return W4A16_OK;
+}
+
 // Dense dispatch table: decode-sized M goes to the split-K kernel, the rest to
 // the LDS-staged tile kernel.
 int pick_variant(int64_t M, int64_t K) {
@@ -70,7 +82,7 @@ const char *w4a16_status_str(int status) {
         case W4A16_OK: return "W4A16_OK";
         case W4A16_ERR_NULL: return "W4A16_ERR_NULL: a required pointer is NULL";
         case W4A16_ERR_SHAPE: return "W4A16_ERR_SHAPE: sizes violate K>0, K%128==0, N>0, N%64==0, M>=0, E>=1";
-        case W4A16_ERR_UNSUPPORTED: return "W4A16_ERR_UNSUPPORTED: group_size must be 128, dtype F16 or BF16 (MSD: F16)";
+        case W4A16_ERR_UNSUPPORTED: return "W4A16_ERR_UNSUPPORTED: group_size must be a multiple of 128 (MSD and the MoE chain: 128), dtype F16 or BF16 (MSD: F16)";
         case W4A16_ERR_ALIGN: return "W4A16_ERR_ALIGN: x, w_packed, workspace need 16-byte, scale and y 2-byte alignment";
         case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE: MSD workspace is NULL or smaller than w4a16_msd_workspace_bytes()";
         case W4A16_ERR_DEVICE: return "W4A16_ERR_DEVICE: current device is not gfx950 or a launch failed";
@@ -97,7 +109,8 @@ w4a16_status w4a16_prepack(const void *w, void *w_packed, int64_t E, int64_t K, 
 w4a16_status w4a16_gemm(const void *x, const void *w_packed, const void *scale, const void *zero, void *y,
                         int64_t M, int64_t K, int64_t N, int64_t group_size, int dt, void *stream) {
     if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
-    w4a16_status st = check_kn(K, N, group_size);
+    int gm = 1;
+    w4a16_status st = check_kn_groups(K, N, group_size, &gm);
     if (st != W4A16_OK) return st;
     if (M < 0 || M > (int64_t(1) << 31) - 1) return W4A16_ERR_SHAPE;
     if (M == 0) return W4A16_OK;
@@ -106,8 +119,9 @@ w4a16_status w4a16_gemm(const void *x, const void *w_packed, const void *scale, 
         return W4A16_ERR_ALIGN;
     if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
     hipStream_t s = (hipStream_t)stream;
-    if (pick_variant(M, K) == 1) return map_err(w4::launch_gemm_small(x, w_packed, scale, zero, y, M, K, N, dt, s));
-    return map_err(w4::launch_gemm_tile(x, nullptr, w_packed, scale, zero, y, M, K, N, 1, dt, s));
+    if (pick_variant(M, K) == 1)
+        return map_err(w4::launch_gemm_small(x, w_packed, scale, zero, y, M, K, N, dt, s, gm));
+    return map_err(w4::launch_gemm_tile(x, nullptr, w_packed, scale, zero, y, M, K, N, 1, dt, s, nullptr, gm));
 }
 
 size_t w4a16_msd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
@@ -136,7 +150,8 @@ w4a16_status w4a16_grouped_gemm(const void *x, const int32_t *expert_offsets, co
                                 const void *scale, const void *zero, void *y, int64_t E, int64_t R, int64_t K,
                                 int64_t N, int64_t group_size, int dt, void *stream) {
     if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
-    w4a16_status st = check_kn(K, N, group_size);
+    int gm = 1;
+    w4a16_status st = check_kn_groups(K, N, group_size, &gm);
     if (st != W4A16_OK) return st;
     if (E < 1 || E > (int64_t(1) << 20) || R < 0 || R > (int64_t(1) << 31) - 1) return W4A16_ERR_SHAPE;
     if (R == 0) return W4A16_OK;
@@ -146,7 +161,7 @@ w4a16_status w4a16_grouped_gemm(const void *x, const int32_t *expert_offsets, co
         return W4A16_ERR_ALIGN;
     if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
     return map_err(w4::launch_gemm_tile(x, expert_offsets, w_packed, scale, zero, y, R, K, N, E, dt,
-                                        (hipStream_t)stream));
+                                        (hipStream_t)stream, nullptr, gm));
 }
 
 // ---- MoE fused-experts chain -------------------------------------------------

@@ -49,7 +49,7 @@ template <int DT, bool ZERO, int NB, int SG, int D>
 __global__ void __launch_bounds__(kSmallMaxWaves * 64)
 gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp,
                   const uint16_t *__restrict__ scale, const uint8_t *__restrict__ zero,
-                  uint16_t *__restrict__ y, int M, int64_t K, int64_t N) {
+                  uint16_t *__restrict__ y, int M, int64_t K, int64_t N, int gm) {
     static_assert(NB == 1 || NB == 2 || NB == 4, "one 64-lane load covers the scales of <= 4 blocks");
     constexpr int T = NB * SG;                    // tiles per wave, ordered block-major
     const int G = (int)(K / kGroup);
@@ -97,9 +97,10 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
         for (int i = 0; i < SG; ++i) {
             const bool live = g0 + i < G;
             const int g = live ? g0 + i : G - 1;
-            const uint32_t sbits = scale[(int64_t)g * N + col];
+            const int64_t gs = g / gm;                 // scale group (gm 128-row groups each)
+            const uint32_t sbits = scale[gs * N + col];
             uint32_t zb = 8u;
-            if constexpr (ZERO) zb = __builtin_amdgcn_ubfe(zero[((int64_t)g * N + col) >> 1], (uint32_t)(cl & 1) * 4u, 4);
+            if constexpr (ZERO) zb = __builtin_amdgcn_ubfe(zero[(gs * N + col) >> 1], (uint32_t)(cl & 1) * 4u, 4);
             sz[i] = (live ? sbits : 0u) | (kBiasBase + zb) << 16;
         }
     }
@@ -196,19 +197,19 @@ int64_t small_max_k() { return (int64_t)kSmallMaxWaves * 4 * kGroup; }
 
 template <int DT, bool ZERO, int NB, int SG, int D>
 static hipError_t small_launch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
-                               int64_t M, int64_t K, int64_t N, hipStream_t stream) {
+                               int64_t M, int64_t K, int64_t N, int gm, hipStream_t stream) {
     const int64_t G = K / kGroup;
     const int64_t waves = (G + SG - 1) / SG;
     const dim3 grid((unsigned)(N / (16 * NB)));
     hipLaunchKernelGGL((gemm_small_kernel<DT, ZERO, NB, SG, D>), grid, dim3((unsigned)(waves * 64)), 0, stream,
                        (const uint16_t *)x, (const uint8_t *)wp, (const uint16_t *)scale,
-                       (const uint8_t *)zero, (uint16_t *)y, (int)M, K, N);
+                       (const uint8_t *)zero, (uint16_t *)y, (int)M, K, N, gm);
     return hipGetLastError();
 }
 
 template <int DT, bool ZERO>
 static hipError_t small_dispatch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
-                                 int64_t M, int64_t K, int64_t N, hipStream_t stream) {
+                                 int64_t M, int64_t K, int64_t N, int gm, hipStream_t stream) {
     const int64_t G = K / kGroup;
     int idx = g_small_cfg;
     if (idx < 0 || idx >= small_config_count()) idx = M > 4 ? 1 : 0;
@@ -224,7 +225,7 @@ static hipError_t small_dispatch(const void *x, const void *wp, const void *scal
     while ((N / 16) % c.nb != 0) c.nb /= 2;
 #define W4_SMALL(NBV, SGV, DV)                                                                  \
     if (c.nb == NBV && c.sg == SGV && c.d == DV)                                                \
-        return small_launch<DT, ZERO, NBV, SGV, DV>(x, wp, scale, zero, y, M, K, N, stream);
+        return small_launch<DT, ZERO, NBV, SGV, DV>(x, wp, scale, zero, y, M, K, N, gm, stream);
     W4_SMALL(4, 2, 4) W4_SMALL(4, 2, 8) W4_SMALL(4, 2, 2) W4_SMALL(2, 4, 4) W4_SMALL(2, 2, 4)
     W4_SMALL(2, 4, 8) W4_SMALL(1, 2, 2) W4_SMALL(1, 4, 4) W4_SMALL(2, 2, 2) W4_SMALL(2, 4, 2)
     W4_SMALL(1, 4, 2) W4_SMALL(1, 2, 4) W4_SMALL(4, 1, 4) W4_SMALL(2, 1, 4) W4_SMALL(1, 1, 4)
@@ -235,12 +236,12 @@ static hipError_t small_dispatch(const void *x, const void *wp, const void *scal
 }
 
 hipError_t launch_gemm_small(const void *x, const void *wp, const void *scale, const void *zero, void *y,
-                             int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream) {
+                             int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream, int gm) {
     if (dt == DT_BF16)
-        return zero ? small_dispatch<DT_BF16, true>(x, wp, scale, zero, y, M, K, N, stream)
-                    : small_dispatch<DT_BF16, false>(x, wp, scale, zero, y, M, K, N, stream);
-    return zero ? small_dispatch<DT_F16, true>(x, wp, scale, zero, y, M, K, N, stream)
-                : small_dispatch<DT_F16, false>(x, wp, scale, zero, y, M, K, N, stream);
+        return zero ? small_dispatch<DT_BF16, true>(x, wp, scale, zero, y, M, K, N, gm, stream)
+                    : small_dispatch<DT_BF16, false>(x, wp, scale, zero, y, M, K, N, gm, stream);
+    return zero ? small_dispatch<DT_F16, true>(x, wp, scale, zero, y, M, K, N, gm, stream)
+                : small_dispatch<DT_F16, false>(x, wp, scale, zero, y, M, K, N, gm, stream);
 }
 
 }  // namespace w4

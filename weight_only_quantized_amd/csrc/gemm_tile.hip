@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 2)
 gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
                  const int32_t *__restrict__ row_src, const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
                  const uint8_t *__restrict__ zero, uint16_t *__restrict__ y,
-                 int64_t M, int64_t K, int64_t N, int E) {
+                 int64_t M, int64_t K, int64_t N, int E, int gm) {
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int RT = TM / 32, CT = TN / 32;
@@ -129,8 +129,10 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     const bool wave_cols = n0 + (int64_t)wn * TN < N;
     const int64_t wcol0 = wave_cols ? n0 + (int64_t)wn * TN : N - TN;
 
-    const uint16_t *sc = scale + e * (int64_t)G * N;
-    const uint8_t *zp = ZERO ? zero + e * (int64_t)G * (N / 2) : nullptr;
+    // one scale (and zero) row per gm consecutive 128-row groups
+    const int64_t GS = G / gm;
+    const uint16_t *sc = scale + e * GS * N;
+    const uint8_t *zp = ZERO ? zero + e * GS * (N / 2) : nullptr;
     const uint8_t *we = wp + e * NBLK * (int64_t)G * kTileBytes;
 
     // ---- activation staging -------------------------------------------------
@@ -225,8 +227,9 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             const int64_t n = wcol0 + ct * 32 + lj;
-            sdst[ct] = sc[(int64_t)g * N + n];
-            zdst[ct] = ZERO ? zp[((int64_t)g * N + n) >> 1] : (uint8_t)0;
+            const int64_t gs = g / gm;
+            sdst[ct] = sc[gs * N + n];
+            zdst[ct] = ZERO ? zp[(gs * N + n) >> 1] : (uint8_t)0;
         }
     };
 
@@ -364,7 +367,7 @@ void set_tile_config(int idx) { g_tile_cfg = idx; }
 template <int DT, bool ZERO, bool GROUPED, int BM, int BN, int WM, int WN>
 static hipError_t tile_launch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
                               const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
-                              int64_t E, hipStream_t stream) {
+                              int64_t E, int gm, hipStream_t stream) {
     // grouped: every expert may end in a partial row tile, hence + E; the
     // items go on a 1-D grid rounded up to whole rounds over the XCDs
     const int64_t ncb = (N + BN - 1) / BN;
@@ -374,14 +377,14 @@ static hipError_t tile_launch(const void *x, const int32_t *offsets, const int32
     const dim3 grid = GROUPED ? dim3((unsigned)slots) : dim3((unsigned)mtiles, (unsigned)ncb);
     hipLaunchKernelGGL((gemm_tile_kernel<DT, ZERO, BM, BN, WM, WN, GROUPED>), grid, dim3(WM * WN * 64), 0,
                        stream, (const uint16_t *)x, offsets, row_src, (const uint8_t *)wp, (const uint16_t *)scale,
-                       (const uint8_t *)zero, (uint16_t *)y, M, K, N, (int)E);
+                       (const uint8_t *)zero, (uint16_t *)y, M, K, N, (int)E, gm);
     return hipGetLastError();
 }
 
 template <int DT, bool ZERO, bool GROUPED>
 static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
                                 const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
-                                int64_t E, hipStream_t stream) {
+                                int64_t E, int gm, hipStream_t stream) {
     int idx = g_tile_cfg;
     if (idx < 0 || idx >= tile_config_count()) {
         idx = 0;
@@ -396,7 +399,7 @@ static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const int
 #define W4_TILE(BMV, BNV, WMV, WNV)                                                                    \
     if (c.bm == BMV && c.bn == BNV && c.wm == WMV && c.wn == WNV)                                      \
         return tile_launch<DT, ZERO, GROUPED, BMV, BNV, WMV, WNV>(x, offsets, row_src, wp, scale, zero, y, M, K,   \
-                                                                  N, E, stream);
+                                                                  N, E, gm, stream);
     W4_TILE(128, 256, 2, 4) W4_TILE(64, 256, 2, 4) W4_TILE(32, 256, 1, 4) W4_TILE(64, 128, 2, 2)
     W4_TILE(32, 128, 1, 4) W4_TILE(128, 128, 2, 2) W4_TILE(64, 256, 1, 4) W4_TILE(64, 128, 1, 2)
 #undef W4_TILE
@@ -406,19 +409,19 @@ static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const int
 template <bool GROUPED>
 static hipError_t tile_dispatch_dt(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
                                    const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
-                                   int64_t E, int dt, hipStream_t stream) {
+                                   int64_t E, int gm, int dt, hipStream_t stream) {
     if (dt == DT_BF16)
-        return zero ? tile_dispatch<DT_BF16, true, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, stream)
-                    : tile_dispatch<DT_BF16, false, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, stream);
-    return zero ? tile_dispatch<DT_F16, true, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, stream)
-                : tile_dispatch<DT_F16, false, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, stream);
+        return zero ? tile_dispatch<DT_BF16, true, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, stream)
+                    : tile_dispatch<DT_BF16, false, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, stream);
+    return zero ? tile_dispatch<DT_F16, true, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, stream)
+                : tile_dispatch<DT_F16, false, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, stream);
 }
 
 hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *wp, const void *scale,
                             const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
-                            int dt, hipStream_t stream, const int32_t *row_src) {
-    if (offsets) return tile_dispatch_dt<true>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, dt, stream);
-    return tile_dispatch_dt<false>(x, nullptr, row_src, wp, scale, zero, y, M, K, N, 1, dt, stream);
+                            int dt, hipStream_t stream, const int32_t *row_src, int gm) {
+    if (offsets) return tile_dispatch_dt<true>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, dt, stream);
+    return tile_dispatch_dt<false>(x, nullptr, row_src, wp, scale, zero, y, M, K, N, 1, gm, dt, stream);
 }
 
 }  // namespace w4

@@ -18,8 +18,9 @@ hipError_t launch_unpack(const void *in, void *w, int64_t E, int64_t K, int64_t 
 int small_config_count();
 void set_small_config(int idx);
 int64_t small_max_k();
+// gm: 128-row groups per scale group (scale and zero have K/(128*gm) rows).
 hipError_t launch_gemm_small(const void *x, const void *wp, const void *scale, const void *zero, void *y,
-                             int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream);
+                             int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream, int gm = 1);
 
 // LDS-staged tile kernel; grouped when offsets != nullptr (then M = R rows).
 // With row_src, row r of the product reads x row row_src[r] (gathered load).
@@ -27,7 +28,7 @@ int tile_config_count();
 void set_tile_config(int idx);
 hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *wp, const void *scale,
                             const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
-                            int dt, hipStream_t stream, const int32_t *row_src = nullptr);
+                            int dt, hipStream_t stream, const int32_t *row_src = nullptr, int gm = 1);
 
 // MSD: decomposition, int8 products + merge, split-K reduction.
 struct MsdPlan {

@@ -66,6 +66,11 @@ def lib():
             "oracle_moe_sum": ([_p, _p, _p, _i64, _i64, _i64, C.c_int, _p], None),
             "oracle_fused_moe": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
                                   C.c_int, _p, _i64, _p], None),
+            "oracle_e4m3_to_double": ([C.c_uint8], C.c_double),
+            "oracle_e2m1_to_double": ([C.c_uint8], C.c_double),
+            "oracle_e8m0_to_double": ([C.c_uint8], C.c_double),
+            "oracle_mxfp8_quantize": ([_p, _i64, _i64, C.c_int, _p, _p], None),
+            "oracle_w4a8_mxfp4": ([_p, _p, _p, _p, _i64, _i64, _i64, C.c_int, _p, _p], None),
             "oracle_prepack": ([_p, _p, _i64, _i64, _i64, C.c_int], None),
             "oracle_unpack": ([_p, _p, _i64, _i64, _i64, C.c_int], None),
         }
@@ -209,6 +214,24 @@ def fused_moe(c, tokens=None):
                            _ptr(c.z13), _ptr(c.w2), _ptr(c.s2), _ptr(c.z2), c.T, c.topk, c.E, c.H, c.I,
                            128, c.dtype, _ptr(tok), tok.shape[0], _ptr(out))
     return out
+
+
+def mxfp8_quantize(x, M, K, dtype):
+    """x bits [M][K] -> (E4M3 codes [M][K] uint8, E8M0 scales [M][K/32] uint8)."""
+    qx = np.empty((M, K), dtype=np.uint8)
+    sx = np.empty((M, K // 32), dtype=np.uint8)
+    lib().oracle_mxfp8_quantize(_ptr(np.ascontiguousarray(x, np.uint16)), M, K, dtype, _ptr(qx), _ptr(sx))
+    return qx, sx
+
+
+def w4a8_mxfp4(qx, sx, w, sw, M, K, N, dtype):
+    """Return (y64 [M,N], y [M,N] bits) of the MXFP8 x MXFP4 product."""
+    y64 = np.empty((M, N), dtype=np.float64)
+    y = np.empty((M, N), dtype=np.uint16)
+    lib().oracle_w4a8_mxfp4(_ptr(np.ascontiguousarray(qx, np.uint8)), _ptr(np.ascontiguousarray(sx, np.uint8)),
+                            _ptr(np.ascontiguousarray(w, np.uint8)), _ptr(np.ascontiguousarray(sw, np.uint8)),
+                            M, K, N, dtype, _ptr(y64), _ptr(y))
+    return y64, y
 
 
 def prepack(w, E, K, N, is_signed):

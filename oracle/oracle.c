@@ -482,3 +482,84 @@ void oracle_fused_moe(const uint16_t *x, const int32_t *topk_ids, const float *t
     }
     free(h); free(a); free(ob); free(acc);
 }
+
+/* ------------------------------------------------------------------------- */
+/* W4A8-MXFP4 (OCP MX formats)                                                */
+/* ------------------------------------------------------------------------- */
+
+double oracle_e4m3_to_double(uint8_t v) {
+    int s = v >> 7, e = (v >> 3) & 15, m = v & 7;
+    if (e == 15 && m == 7) return NAN;
+    double x = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -x : x;
+}
+
+double oracle_e2m1_to_double(uint8_t v) {
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double x = mag[v & 7];
+    return (v & 8) ? -x : x;
+}
+
+double oracle_e8m0_to_double(uint8_t v) { return v == 255 ? NAN : ldexp(1.0, (int)v - 127); }
+
+/* E4M3 code of a finite double, round to nearest even over the representable
+ * values, saturated to +-448.  Written as a search over the 127 non-negative
+ * finite codes (monotone in the code), so it is plainly the nearest-value
+ * rounding of the definition. */
+static uint8_t e4m3_rne_sat(double v) {
+    int neg = signbit(v) != 0;
+    double a = fabs(v);
+    if (a >= 448.0) return (uint8_t)((neg << 7) | 0x7E);
+    int best = 0;
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs(oracle_e4m3_to_double((uint8_t)c) - a), db = fabs(oracle_e4m3_to_double((uint8_t)best) - a);
+        if (d < db || (d == db && (c & 1) == 0 && (best & 1) == 1)) best = c;
+    }
+    return (uint8_t)((neg << 7) | best);
+}
+
+void oracle_mxfp8_quantize(const uint16_t *x, int64_t M, int64_t K, int dtype, uint8_t *qx, uint8_t *sx) {
+    int64_t B = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t b = 0; b < B; ++b) {
+            double amax = 0.0;
+            for (int64_t k = 32 * b; k < 32 * b + 32; ++k) {
+                double a = fabs(to_double(x[m * K + k], dtype));
+                if (a > amax) amax = a;
+            }
+            int e = -127;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);          /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+                e = ex - 1 - 8;
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            sx[m * B + b] = (uint8_t)(e + 127);
+            for (int64_t k = 32 * b; k < 32 * b + 32; ++k)
+                qx[m * K + k] = e4m3_rne_sat(ldexp(to_double(x[m * K + k], dtype), -e));
+        }
+}
+
+void oracle_w4a8_mxfp4(const uint8_t *qx, const uint8_t *sx, const uint8_t *w, const uint8_t *sw,
+                       int64_t M, int64_t K, int64_t N, int dtype, double *y64, uint16_t *y) {
+    int64_t B = K / 32;
+    double *acc = y64 ? y64 : (double *)malloc(sizeof(double) * (size_t)(M * N));
+    assert(acc);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double a = oracle_e4m3_to_double(qx[m * K + k]) * oracle_e8m0_to_double(sx[m * B + k / 32]);
+                uint8_t byte = w[k * (N / 2) + n / 2];
+                uint8_t code = (n & 1) ? (byte >> 4) : (byte & 0xF);
+                double b = oracle_e2m1_to_double(code) * oracle_e8m0_to_double(sw[(k / 32) * N + n]);
+                s += a * b;
+            }
+            acc[m * N + n] = s;
+        }
+    if (y) oracle_round_array(acc, y, M * N, dtype);
+    if (!y64) free(acc);
+}

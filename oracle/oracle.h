@@ -117,6 +117,26 @@ void oracle_fused_moe(const uint16_t *x, const int32_t *topk_ids, const float *t
                       int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I,
                       int64_t group, int dtype, const int64_t *tok, int64_t P, uint16_t *out);
 
+/* ---- W4A8-MXFP4 (Humming article: W4A8-MXFP4 path; formats per the OCP
+ * Microscaling (MX) specification v1.0: blocks of 32 elements along K sharing
+ * one power-of-two E8M0 scale).  Weights: E2M1 codes w[K][N/2] (two per byte
+ * along N, low nibble = even n) with scales sw[K/32][N]; activations:
+ * quantized to MXFP8 (E4M3 codes qx[M][K], scales sx[M][K/32]). ---- */
+double oracle_e4m3_to_double(uint8_t v);     /* OCP E4M3 (bias 7, no infinities, 0x7F/0xFF NaN) */
+double oracle_e2m1_to_double(uint8_t v);     /* OCP E2M1: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6} */
+double oracle_e8m0_to_double(uint8_t v);     /* 2^(v - 127), 0xFF NaN */
+
+/* MXFP8 quantization of one row-block set: for each row m and 32-block b,
+ * shared exponent e = floor(log2(max |x|)) - 8 (8 = largest E4M3 exponent),
+ * clamped to [-127, 127] (an all-zero block gets e = -127); scale byte e + 127;
+ * element = E4M3 round-to-nearest-even of x / 2^e, saturated to +-448. */
+void oracle_mxfp8_quantize(const uint16_t *x, int64_t M, int64_t K, int dtype, uint8_t *qx, uint8_t *sx);
+
+/* y64[m][n] = sum_k E4M3(qx[m][k]) 2^(sx[m][k/32]-127) * E2M1(w[k][n]) 2^(sw[k/32][n]-127)
+ * in fp64 (every product exact), y = RNE(y64) in dtype (y64 or y may be NULL). */
+void oracle_w4a8_mxfp4(const uint8_t *qx, const uint8_t *sx, const uint8_t *w, const uint8_t *sw,
+                       int64_t M, int64_t K, int64_t N, int dtype, double *y64, uint16_t *y);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,9 @@ page's own example shape (M=1, K=8192, N=12288); msd_page and msd_basic also tim
 the page's basic pipeline (integer products written to memory, separate merge)
 next to the fused kernel.  The chain's algorithmic
 bytes: tokens in and out (T*H*2 each), routing ids and weights (T*topk*8), and
-the active experts' gate/up and down weights with their scales.
+the active experts' gate/up and down weights with their scales.  mx_decode is
+W4A8-MXFP4 at the decode shape (bf16 x quantized to MXFP8 inside the GEMM,
+MXFP4 weights); its bytes: x + E2M1 codes (K*N/2) + E8M0 scales (K/32*N) + y.
 
 Algorithmic bytes of one dense call: x (M*K*2) + packed weights (K*N/2) +
 scales (K/128*N*2) + zero points (K/128*N/2, if any) + y (M*N*2).
@@ -283,6 +285,34 @@ def moe_chain_workload():
 # timing
 # ---------------------------------------------------------------------------
 
+def mx_bytes(M, K, N):
+    """Algorithmic bytes of one W4A8-MXFP4 call: x (16-bit) + E2M1 codes + E8M0
+    scales (one per 32 rows and column) + y."""
+    return M * K * 2 + K * N // 2 + K // 32 * N + M * N * 2
+
+
+def mx_decode_workload():
+    """W4A8-MXFP4 at the decode shape: M in {1, 4, 16}, K=4096, N=14336, bf16 x
+    quantized to MXFP8 inside the GEMM, MXFP4 weights."""
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    ps = {M: synth.mx_decode(M) for M in (1, 4, 16)}
+    p1 = ps[1]
+    K, N = p1.K, p1.N
+    wp = torch.empty(w4.w4a8_mxfp4_prepacked_bytes(1, K, N), dtype=torch.uint8, device="cuda:0")
+    w4.w4a8_mxfp4_prepack(_dev(p1.w), _dev(p1.sw), wp, 1, K, N)
+    wps = _copies(wp, wp.numel())
+    xs = {M: _dev(ps[M].x) for M in ps}
+    ys = {M: torch.empty((M, N), dtype=torch.int16, device="cuda:0") for M in ps}
+    calls = []
+    for M in (1, 4, 16):
+        def launch(i, M=M):
+            w4.w4a8_mxfp4_gemm(xs[M], wps[i % len(wps)], ys[M], M, K, N, synth.BF16, None, 0)
+        calls.append((f"mx_decode_m{M}", launch, mx_bytes(M, K, N), 2 * M * N * K))
+    return calls, len(wps)
+
+
 def _capture(calls, first, count):
     """One HIP graph holding `count` steps (every call once per step, buffer set
     first + i for step i), captured on a side stream.  Replaying it launches the
@@ -406,7 +436,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["decode", "tiny", "prefill", "msd", "moe", "moe_chain", "msd_page",
-                                       "msd_basic"], default=None,
+                                       "msd_basic", "mx_decode"], default=None,
                     help="run only this workload (profiling); no JSON headline unless decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-config extras")
@@ -436,7 +466,7 @@ def main():
 
     builders = {"decode": decode_workload, "tiny": tiny_workload, "prefill": prefill_workload,
                 "msd": msd_workload, "moe": moe_workload, "moe_chain": moe_chain_workload,
-                "msd_page": msd_page_workload, "msd_basic": msd_basic_workload}
+                "msd_page": msd_page_workload, "msd_basic": msd_basic_workload, "mx_decode": mx_decode_workload}
     if args.only and args.only != "decode":
         _, out = measure(args.only, builders[args.only], args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **out}), flush=True)
@@ -452,7 +482,7 @@ def main():
 
     extra = {}
     if not args.no_extra and not args.only:
-        for name in ("tiny", "prefill", "msd", "moe", "moe_chain", "msd_page", "msd_basic"):
+        for name in ("tiny", "prefill", "msd", "moe", "moe_chain", "msd_page", "msd_basic", "mx_decode"):
             print(f"[bench] {name} workload", file=sys.stderr, flush=True)
             _, extra[name] = measure(name, builders[name], max(10, args.steps // 2), args.warmup)
             torch.cuda.empty_cache()

@@ -227,6 +227,65 @@ w4a16_status w4a16_fused_moe(const void *x, const int32_t *topk_ids, const float
                              int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I, int64_t group_size,
                              int dt, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * W4A8-MXFP4 ("Humming: open-source library for quantized inference", the
+ * W4A8-MXFP4 path: MXFP4 weights with 8-bit activations, aimed at small-M
+ * speed; the W4A8 configuration in its list of supported weight/activation
+ * settings).  Formats follow the OCP Microscaling (MX) v1.0 specification:
+ *   weights      E2M1 codes w[E][K][N/2] (two per byte along N, low nibble =
+ *                even n, the plain layout above) with E8M0 scales
+ *                w_scale[E][K/32][N]: value = e2m1(code) * 2^(scale - 127);
+ *   activations  MXFP8: E4M3 codes qx[M][K] with E8M0 scales sx[M][K/32]; a
+ *                block's shared exponent is floor(log2 max|x|) - 8, clamped to
+ *                [-127, 127], and each element is x / 2^e rounded to nearest
+ *                even and saturated to +-448 (finite inputs only);
+ *   y[m][n] = sum_k qx * 2^(sx - 127) * w * 2^(w_scale - 127), fp32
+ *   accumulation, rounded to dt (fp16 or bf16).
+ * gfx950's block-scaled matrix-core instruction takes both formats and both
+ * scales directly; the article's in-kernel weight conversion (needed on GPUs
+ * without MXFP4 matrix cores) is not needed here.
+ * Shape rules: K % 128 == 0, N % 64 == 0, K <= 8192, M >= 0, E >= 1.
+ * Alignment: x, qx, w, w_packed, workspace 16 bytes; y 2 bytes.
+ */
+
+/* Bytes of the prepacked MXFP4 buffer: E * (K/128) * (N/16) * 1088. */
+size_t w4a8_mxfp4_prepacked_bytes(int64_t E, int64_t K, int64_t N);
+
+/*
+ * Offline repack of MXFP4 weights and their scales into 1088-byte tiles
+ * ordered (expert, 16-column block, 128-row group): bytes 16L..16L+15 of a
+ * tile hold column 16*nb + L%16, rows 128*g + 32*(L/16) + r (r = 0..31) as
+ * nibble r (low nibble first); byte 1024 + L holds the scale of that column
+ * for rows 128*g + 32*(L/16) .. +31.  This is the block-scaled instruction's
+ * own operand order, so one 128-bit and one 8-bit load per lane feed it.
+ * w: E*K*N/2 bytes, w_scale: E*(K/32)*N bytes, w_packed:
+ * w4a8_mxfp4_prepacked_bytes() bytes; device pointers, no overlap.
+ */
+w4a16_status w4a8_mxfp4_prepack(const void *w, const void *w_scale, void *w_packed, int64_t E, int64_t K,
+                                int64_t N, void *stream);
+
+/* MXFP8 quantization of activations x[M][K] (dtype dt) into qx[M][K] (E4M3)
+ * and sx[M][K/32] (E8M0), as defined above.  Bit-exact by construction. */
+w4a16_status w4a8_mxfp8_quantize(const void *x, void *qx, void *sx, int64_t M, int64_t K, int dt, void *stream);
+
+/* y[M][N] (dtype dt) from prequantized MXFP8 activations and prepacked
+ * MXFP4 weights (E = 1). */
+w4a16_status w4a8_mxfp4_gemm_prequant(const void *qx, const void *sx, const void *w_packed, void *y, int64_t M,
+                                      int64_t K, int64_t N, int dt, void *stream);
+
+/* Scratch for w4a8_mxfp4_gemm: 0 when M <= 16 (activations are quantized in
+ * the GEMM's registers), else room for qx and sx. */
+size_t w4a8_mxfp4_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * y[M][N] = MXFP8(x) . MXFP4(W): quantizes x (dtype dt) and multiplies.  For
+ * M <= 16 one kernel does both (each wave quantizes its K slice in registers);
+ * otherwise x is quantized into the workspace first.  workspace: device,
+ * >= w4a8_mxfp4_workspace_bytes(M, K) bytes (may be NULL when that is 0).
+ */
+w4a16_status w4a8_mxfp4_gemm(const void *x, const void *w_packed, void *y, int64_t M, int64_t K, int64_t N,
+                             int dt, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

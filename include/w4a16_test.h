@@ -72,6 +72,10 @@ int w4a16_test_tile_config(int idx);
  */
 int w4a16_test_msd_config(int idx);
 
+/* Select the W4A8-MXFP4 small-M kernel variant (-1 = automatic); returns the
+ * number of variants. */
+int w4a16_test_mx_small_config(int idx);
+
 /* Name of the kernel variant the dispatcher picks for a dense call. */
 const char *w4a16_test_variant_name(int64_t M, int64_t K, int64_t N, int dt, int has_zero);
 

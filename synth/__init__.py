@@ -308,3 +308,38 @@ def moe_chain(seed=0) -> MoeChain:
     grouped GEMM's K and N); x bf16 N(0,1); signed int4; scales bf16
     U[0.002,0.01]."""
     return make_moe_chain(512, 8, 64, 2048, 1408, BF16, alpha=1.1, signed=True, seed=seed, name="moe_chain")
+
+
+@dataclasses.dataclass
+class MxProblem:
+    """W4A8-MXFP4 problem in the plain layout: 16-bit activations ``x [M][K]``,
+    E2M1 weight codes ``w [K][N/2]`` (low nibble = even n) and E8M0 weight
+    scale bytes ``sw [K/32][N]``."""
+    x: np.ndarray
+    w: np.ndarray
+    sw: np.ndarray
+    M: int
+    K: int
+    N: int
+    dtype: int
+    name: str = ""
+
+
+def make_mx(M, K, N, dtype=BF16, seed=0, scale_exp=(-9, -6), x_scale=1.0, outlier_frac=0.0,
+            outlier_mult=20.0, name="") -> MxProblem:
+    """x ~ N(0,1) * x_scale (optionally with outliers); weight codes uniform
+    over the 16 E2M1 patterns; weight scale exponents uniform integers in
+    ``scale_exp`` (stored as exponent + 127)."""
+    assert K % 32 == 0 and N % 2 == 0
+    x = _normal(stream(seed, "x"), (M, K)) * np.float32(x_scale)
+    if outlier_frac > 0:
+        mask = stream(seed, "mask").random((M, K)) < outlier_frac
+        x = np.where(mask, x * np.float32(outlier_mult), x).astype(np.float32)
+    codes = stream(seed, "w").integers(0, 16, size=(K, N), dtype=np.uint8)
+    sw = (127 + stream(seed, "s").integers(scale_exp[0], scale_exp[1] + 1, size=(K // 32, N))).astype(np.uint8)
+    return MxProblem(x=to_bits(x, dtype), w=pack_nibbles(codes), sw=sw, M=M, K=K, N=N, dtype=dtype, name=name)
+
+
+def mx_decode(M, seed=0, N=14336, K=4096) -> MxProblem:
+    """W4A8-MXFP4 decode: the decode shape (K=4096, N=14336), x bf16 N(0,1)."""
+    return make_mx(M, K, N, BF16, seed=seed, name=f"mx_decode_m{M}")

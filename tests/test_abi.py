@@ -17,7 +17,7 @@ def _declared():
     for h in ("w4a16.h", "w4a16_test.h"):
         src = open(os.path.join(ROOT, "include", h)).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        names |= set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", src))
+        names |= set(re.findall(r"\b(w4a(?:16|8)_[a-z0-9_]+)\s*\(", src))
     return names
 
 
@@ -180,3 +180,35 @@ def test_group_sizes_accepted_by_gemm_only():
         assert L.w4a16_grouped_gemm(FAKE, FAKE, FAKE, FAKE + 1, None, FAKE, 4, 16, 1024, 256, gs, 1, None) == 4
     ws = w4.w4a16_msd_workspace_bytes(4, 1024, 256)
     assert L.w4a16_msd_gemm(FAKE, FAKE, FAKE, FAKE, 4, 1024, 256, 256, FAKE, ws, None) == 3
+
+
+def test_mxfp4_sizes_and_validation():
+    assert w4.w4a8_mxfp4_prepacked_bytes(1, 4096, 14336) == 32 * 896 * 1088
+    assert w4.w4a8_mxfp4_prepacked_bytes(0, 128, 64) == 0
+    assert w4.w4a8_mxfp4_workspace_bytes(16, 4096) == 0               # quantized in registers
+    ws = w4.w4a8_mxfp4_workspace_bytes(17, 4096)
+    assert ws >= 17 * 4096 + 17 * 128 and (17 * 4096 + 255) // 256 * 256 <= ws
+    L = w4.lib()
+    F = FAKE
+    # (call, expected status): shapes, dtype, nulls, alignment, workspace; all
+    # rejected on the host before any device call
+    cases = [
+        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 1, 100, 64, 1, None, 0, None), 2),        # K % 128
+        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 1, 128, 32, 1, None, 0, None), 2),        # N % 64
+        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 1, 16384, 64, 1, None, 0, None), 2),      # K > 8192
+        (lambda: L.w4a8_mxfp4_gemm(F, F, F, -1, 128, 64, 1, None, 0, None), 2),
+        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 1, 128, 64, 5, None, 0, None), 3),        # dtype
+        (lambda: L.w4a8_mxfp4_gemm(None, F, F, 1, 128, 64, 1, None, 0, None), 1),
+        (lambda: L.w4a8_mxfp4_gemm(F + 8, F, F, 1, 128, 64, 1, None, 0, None), 4),    # x alignment
+        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 17, 128, 64, 1, None, 0, None), 5),       # workspace
+        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 17, 128, 64, 1, F, 16, None), 5),
+        (lambda: L.w4a8_mxfp4_gemm_prequant(F, F, F, F, 1, 128, 48, 1, None), 2),
+        (lambda: L.w4a8_mxfp4_gemm_prequant(F, None, F, F, 1, 128, 64, 1, None), 1),
+        (lambda: L.w4a8_mxfp8_quantize(F, F, F, 1, 96, 1, None), 2),
+        (lambda: L.w4a8_mxfp8_quantize(F, F + 4, F, 1, 128, 1, None), 4),
+        (lambda: L.w4a8_mxfp4_prepack(F, F, F, 0, 128, 64, None), 2),
+        (lambda: L.w4a8_mxfp4_prepack(F, None, F, 1, 128, 64, None), 1),
+    ]
+    for i, (call, st) in enumerate(cases):
+        assert call() == st, i
+    assert L.w4a8_mxfp4_gemm(F, F, F, 0, 128, 64, 1, None, 0, None) == 0              # M == 0: no-op

@@ -48,6 +48,12 @@ _SIGS = {
     "w4a16_fused_moe_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64], C.c_size_t),
     "w4a16_fused_moe": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, C.c_int,
                          _p, C.c_size_t, _p], C.c_int),
+    "w4a8_mxfp4_prepacked_bytes": ([_i64, _i64, _i64], C.c_size_t),
+    "w4a8_mxfp4_prepack": ([_p, _p, _p, _i64, _i64, _i64, _p], C.c_int),
+    "w4a8_mxfp8_quantize": ([_p, _p, _p, _i64, _i64, C.c_int, _p], C.c_int),
+    "w4a8_mxfp4_gemm_prequant": ([_p, _p, _p, _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
+    "w4a8_mxfp4_workspace_bytes": ([_i64, _i64], C.c_size_t),
+    "w4a8_mxfp4_gemm": ([_p, _p, _p, _i64, _i64, _i64, C.c_int, _p, C.c_size_t, _p], C.c_int),
     "w4a16_test_unpack": ([_p, _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
     "w4a16_test_msd_intermediates": ([_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, C.c_size_t, _p], C.c_int),
     "w4a16_test_msd_basic_workspace_bytes": ([_i64, _i64, _i64, _i64], C.c_size_t),
@@ -57,6 +63,7 @@ _SIGS = {
     "w4a16_test_small_config": ([C.c_int], C.c_int),
     "w4a16_test_tile_config": ([C.c_int], C.c_int),
     "w4a16_test_msd_config": ([C.c_int], C.c_int),
+    "w4a16_test_mx_small_config": ([C.c_int], C.c_int),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -164,6 +171,34 @@ def w4a16_fused_moe(x, topk_ids, topk_w, w13_packed, s13, z13, w2_packed, s2, z2
            "w4a16_fused_moe")
 
 
+def w4a8_mxfp4_prepacked_bytes(E: int, K: int, N: int) -> int:
+    return lib().w4a8_mxfp4_prepacked_bytes(E, K, N)
+
+
+def w4a8_mxfp4_prepack(w, w_scale, w_packed, E, K, N, stream=None):
+    _check(lib().w4a8_mxfp4_prepack(_ptr(w), _ptr(w_scale), _ptr(w_packed), E, K, N, _stream(stream)),
+           "w4a8_mxfp4_prepack")
+
+
+def w4a8_mxfp8_quantize(x, qx, sx, M, K, dt=W4A16_BF16, stream=None):
+    _check(lib().w4a8_mxfp8_quantize(_ptr(x), _ptr(qx), _ptr(sx), M, K, int(dt), _stream(stream)),
+           "w4a8_mxfp8_quantize")
+
+
+def w4a8_mxfp4_gemm_prequant(qx, sx, w_packed, y, M, K, N, dt=W4A16_BF16, stream=None):
+    _check(lib().w4a8_mxfp4_gemm_prequant(_ptr(qx), _ptr(sx), _ptr(w_packed), _ptr(y), M, K, N, int(dt),
+                                          _stream(stream)), "w4a8_mxfp4_gemm_prequant")
+
+
+def w4a8_mxfp4_workspace_bytes(M: int, K: int) -> int:
+    return lib().w4a8_mxfp4_workspace_bytes(M, K)
+
+
+def w4a8_mxfp4_gemm(x, w_packed, y, M, K, N, dt=W4A16_BF16, workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().w4a8_mxfp4_gemm(_ptr(x), _ptr(w_packed), _ptr(y), M, K, N, int(dt), _ptr(workspace),
+                                 int(workspace_bytes), _stream(stream)), "w4a8_mxfp4_gemm")
+
+
 # ---- test hooks (include/w4a16_test.h) ----------------------------------------
 
 def w4a16_test_unpack(w_packed, w, E, K, N, is_signed, stream=None):
@@ -207,3 +242,7 @@ def w4a16_test_tile_config(idx: int) -> int:
 
 def w4a16_test_msd_config(idx: int) -> int:
     return lib().w4a16_test_msd_config(int(idx))
+
+
+def w4a16_test_mx_small_config(idx: int) -> int:
+    return lib().w4a16_test_mx_small_config(int(idx))

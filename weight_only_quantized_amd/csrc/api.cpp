@@ -63,6 +63,20 @@ w4a16_status check_kn_groups(int64_t K, int64_t N, int64_t group_size, int *gm) 
     return W4A16_OK;
 }
 
+// W4A8-MXFP4 shapes: K a multiple of 128 up to the small kernel's K limit,
+// N a multiple of 64.
+w4a16_status check_mx_kn(int64_t K, int64_t N) {
+    if (K <= 0 || N <= 0 || K % 128 != 0 || N % 64 != 0) return W4A16_ERR_SHAPE;
+    if (K > w4::mx_small_max_k() || N > (int64_t(1) << 30)) return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+// Row limit of the MXFP4 GEMM (16-row chunks on the second grid axis).
+constexpr int64_t kMxMaxM = 65535 * 16;
+
+// Offset of sx behind qx in the W4A8-MXFP4 workspace (256-byte aligned).
+size_t mx_ws_sx_offset(int64_t M, int64_t K) { return ((size_t)M * (size_t)K + 255) & ~(size_t)255; }
+
 // Dense dispatch table: decode-sized M goes to the split-K kernel, the rest to
 // the LDS-staged tile kernel.
 int pick_variant(int64_t M, int64_t K) {
@@ -332,6 +346,80 @@ int w4a16_test_tile_config(int idx) {
 int w4a16_test_msd_config(int idx) {
     w4::set_msd_config(idx);
     return w4::msd_config_count();
+}
+
+int w4a16_test_mx_small_config(int idx) {
+    w4::set_mx_small_config(idx);
+    return w4::mx_small_config_count();
+}
+
+// ---- W4A8-MXFP4 -------------------------------------------------------------
+
+size_t w4a8_mxfp4_prepacked_bytes(int64_t E, int64_t K, int64_t N) {
+    if (E < 1 || K <= 0 || N <= 0) return 0;
+    return w4::mx_prepacked_bytes(E, K, N);
+}
+
+w4a16_status w4a8_mxfp4_prepack(const void *w, const void *w_scale, void *w_packed, int64_t E, int64_t K,
+                                int64_t N, void *stream) {
+    if (E < 1) return W4A16_ERR_SHAPE;
+    w4a16_status st = check_mx_kn(K, N);
+    if (st != W4A16_OK) return st;
+    if (!w || !w_scale || !w_packed) return W4A16_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(w_packed, 16)) return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_mx_prepack(w, w_scale, w_packed, E, K, N, (hipStream_t)stream));
+}
+
+w4a16_status w4a8_mxfp8_quantize(const void *x, void *qx, void *sx, int64_t M, int64_t K, int dt, void *stream) {
+    if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
+    if (M < 0 || K <= 0 || K % 128 != 0 || M > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 30))
+        return W4A16_ERR_SHAPE;
+    if (M == 0) return W4A16_OK;
+    if (!x || !qx || !sx) return W4A16_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(qx, 16)) return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_mx_quantize(x, qx, sx, M, K, dt, (hipStream_t)stream));
+}
+
+w4a16_status w4a8_mxfp4_gemm_prequant(const void *qx, const void *sx, const void *w_packed, void *y, int64_t M,
+                                      int64_t K, int64_t N, int dt, void *stream) {
+    if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
+    w4a16_status st = check_mx_kn(K, N);
+    if (st != W4A16_OK) return st;
+    if (M < 0 || M > kMxMaxM) return W4A16_ERR_SHAPE;
+    if (M == 0) return W4A16_OK;
+    if (!qx || !sx || !w_packed || !y) return W4A16_ERR_NULL;
+    if (!aligned(qx, 16) || !aligned(w_packed, 16) || !aligned(y, 2)) return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_mx_gemm_small(nullptr, qx, sx, w_packed, y, M, K, N, dt, (hipStream_t)stream));
+}
+
+size_t w4a8_mxfp4_workspace_bytes(int64_t M, int64_t K) {
+    if (M <= 16 || K <= 0) return 0;
+    return mx_ws_sx_offset(M, K) + (size_t)M * (size_t)(K / 32);
+}
+
+w4a16_status w4a8_mxfp4_gemm(const void *x, const void *w_packed, void *y, int64_t M, int64_t K, int64_t N,
+                             int dt, void *workspace, size_t workspace_bytes, void *stream) {
+    if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
+    w4a16_status st = check_mx_kn(K, N);
+    if (st != W4A16_OK) return st;
+    if (M < 0 || M > kMxMaxM) return W4A16_ERR_SHAPE;
+    if (M == 0) return W4A16_OK;
+    if (!x || !w_packed || !y) return W4A16_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 2)) return W4A16_ERR_ALIGN;
+    const size_t need = w4a8_mxfp4_workspace_bytes(M, K);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return W4A16_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    const hipStream_t s = (hipStream_t)stream;
+    if (M <= 16) return map_err(w4::launch_mx_gemm_small(x, nullptr, nullptr, w_packed, y, M, K, N, dt, s));
+    uint8_t *qx = (uint8_t *)workspace;
+    uint8_t *sx = qx + mx_ws_sx_offset(M, K);
+    hipError_t e = w4::launch_mx_quantize(x, qx, sx, M, K, dt, s);
+    if (e != hipSuccess) return map_err(e);
+    return map_err(w4::launch_mx_gemm_small(nullptr, qx, sx, w_packed, y, M, K, N, dt, s));
 }
 
 }  // extern "C"

@@ -75,4 +75,17 @@ hipError_t launch_fused_moe(const void *x, const int32_t *ids, const float *topk
                             int64_t topk, int64_t E, int64_t H, int64_t I, int dt, void *workspace,
                             hipStream_t stream);
 
+// W4A8-MXFP4: weight prepack (1088-byte tiles), MXFP8 activation
+// quantization, and the small-M GEMM (x != nullptr: activations quantized in
+// registers; else read prequantized from qx / sx).
+size_t mx_prepacked_bytes(int64_t E, int64_t K, int64_t N);
+hipError_t launch_mx_prepack(const void *w, const void *sw, void *out, int64_t E, int64_t K, int64_t N,
+                             hipStream_t stream);
+hipError_t launch_mx_quantize(const void *x, void *qx, void *sx, int64_t M, int64_t K, int dt, hipStream_t stream);
+int mx_small_config_count();
+void set_mx_small_config(int idx);
+int64_t mx_small_max_k();
+hipError_t launch_mx_gemm_small(const void *x, const void *qx, const void *sx, const void *wp, void *y, int64_t M,
+                                int64_t K, int64_t N, int dt, hipStream_t stream);
+
 }  // namespace w4

@@ -1,0 +1,360 @@
+// mxfp4.hip — W4A8-MXFP4: MXFP4 weights (E2M1 codes with one E8M0 scale per
+// 32 K rows and column) times MXFP8 activations (E4M3 codes with one E8M0
+// scale per row and 32 K elements), formats as in the OCP Microscaling (MX)
+// v1.0 specification; the path itself is the Humming article's W4A8-MXFP4
+// route.  The article converts MXFP4 weights inside the kernel because the
+// GPUs it targets have no MXFP4 matrix cores; gfx950 has them: the
+// block-scaled instruction v_mfma_scale_f32_16x16x128_f8f6f4 takes E4M3 A,
+// E2M1 B and both E8M0 scales directly, so the weights go from memory into
+// the matrix core untouched and no vector-ALU dequantization is left.
+//
+// Operand layout of that instruction (16 x 16 x 128, fp8 A, fp4 B):
+//   A (8 registers): lane l feeds row l % 16; with h = l / 16, bytes 0..15
+//     hold k = 16h + i and bytes 16..31 hold k = 64 + 16h + i (i = 0..15);
+//   B (4 registers): lane l feeds column l % 16 and rows k = 32h + r,
+//     r = 0..31, as nibble r of its 16 bytes (low nibble first);
+//   scales: lane l's A scale belongs to row l % 16, k-block h (32 rows); its B
+//     scale to column l % 16, k-block h (E8M0 in the low byte);
+//   D: register r of lane l is row 4h + r, column l % 16.
+//
+// Prepacked weight tile (1088 bytes per 16-column block and 128-row group):
+// bytes 0..1023 are the 64 lanes' B operands (16 bytes each, lane-major), bytes
+// 1024..1087 the 64 lanes' B scales.  One 128-bit and one 8-bit load per lane
+// deliver a whole instruction's weight operand.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace w4 {
+
+constexpr int kMxTileBytes = 1088;
+constexpr int kMxCodeBytes = 1024;
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma_mx(const i32x8_t &a, const i32x8_t &b, const f32x4_t &c, int sa, int sb) {
+    // cbsz = 0: A is E4M3; blgp = 4: B is E2M1 (only the low 4 registers read)
+    f32x4_t r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
+    keep_live(r, a, b);
+    return r;
+}
+
+// Shared exponent of an MXFP8 block (OCP MX: floor(log2 max|x|) minus the
+// largest E4M3 exponent, 8), clamped to the E8M0 range.  For a zero or
+// subnormal maximum the exponent field gives -127 and the clamp the smallest
+// scale, which is what the exact floor(log2) would give as well.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+    const int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 8;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Four values scaled by 2^-e (exact), clamped to the largest E4M3 magnitude
+// and converted with round-to-nearest-even, packed into one word (byte i =
+// value i).
+__device__ __forceinline__ uint32_t mx_e4m3x4(float a, float b, float c, float d, int e) {
+    a = __builtin_amdgcn_fmed3f(__builtin_amdgcn_ldexpf(a, -e), -448.f, 448.f);
+    b = __builtin_amdgcn_fmed3f(__builtin_amdgcn_ldexpf(b, -e), -448.f, 448.f);
+    c = __builtin_amdgcn_fmed3f(__builtin_amdgcn_ldexpf(c, -e), -448.f, 448.f);
+    d = __builtin_amdgcn_fmed3f(__builtin_amdgcn_ldexpf(d, -e), -448.f, 448.f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// Eight 16-bit values (one 128-bit load) as fp32.
+template <int DT>
+__device__ __forceinline__ void unpack8(const u32x4_t &v, float (&f)[8]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t w = v[t];
+        f[2 * t] = h2f<DT>((uint16_t)(w & 0xFFFFu));
+        f[2 * t + 1] = h2f<DT>((uint16_t)(w >> 16));
+    }
+}
+
+__device__ __forceinline__ float amax8(const float (&f)[8]) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+    return m;
+}
+
+// ---------------------------------------------------------------------------
+// Weight prepack: w[E][K][N/2] E2M1 codes (low nibble = even column) and
+// sw[E][K/32][N] E8M0 scales into 1088-byte tiles ordered (expert, 16-column
+// block, 128-row group).  One 64-thread workgroup per tile.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) mx_prepack_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ sw,
+                                                        uint8_t *__restrict__ out, int64_t K, int64_t N) {
+    const int64_t G = K / kGroup, NB = N / 16;
+    const int64_t tile = blockIdx.x;                 // (e * NB + nb) * G + g
+    const int64_t g = tile % G;
+    const int64_t nb = (tile / G) % NB;
+    const int64_t e = tile / (G * NB);
+    const int L = threadIdx.x;
+
+    __shared__ uint64_t rows[kGroup];                 // 16 codes of each row
+    const uint8_t *src = w + e * K * (N / 2) + (g * kGroup) * (N / 2) + nb * 8;
+    for (int r = L; r < kGroup; r += 64) rows[r] = *reinterpret_cast<const uint64_t *>(src + (int64_t)r * (N / 2));
+    __syncthreads();
+
+    const int h = L >> 4, j = L & 15;
+    u32x4_t slot;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= ((uint32_t)(rows[32 * h + 8 * t + i] >> (4 * j)) & 0xFu) << (4 * i);
+        slot[t] = word;
+    }
+    uint8_t *dst = out + tile * kMxTileBytes;
+    *reinterpret_cast<u32x4_t *>(dst + L * 16) = slot;
+    dst[kMxCodeBytes + L] = sw[e * (K / 32) * N + (4 * g + h) * N + nb * 16 + j];
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 quantization of activations: x[M][K] -> qx[M][K] E4M3 codes and
+// sx[M][K/32] E8M0 scales.  Four consecutive lanes own one 32-element block
+// (8 elements each, one 128-bit load) and agree on its maximum with two
+// cross-lane exchanges.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ void __launch_bounds__(256) mx_quantize_kernel(const uint16_t *__restrict__ x, uint8_t *__restrict__ qx,
+                                                          uint8_t *__restrict__ sx, int64_t n8) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // n8 is a multiple of 4 and quads are lane-aligned: a quad is all in or all out
+    if (t >= n8) return;
+    float f[8];
+    unpack8<DT>(ld128(x + t * 8), f);
+    float m = amax8(f);
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    const int e = mx_shared_exp(m);
+    u32x2_t q;
+    q[0] = mx_e4m3x4(f[0], f[1], f[2], f[3], e);
+    q[1] = mx_e4m3x4(f[4], f[5], f[6], f[7], e);
+    *reinterpret_cast<u32x2_t *>(qx + t * 8) = q;
+    if ((t & 3) == 0) sx[t >> 2] = (uint8_t)(e + 127);
+}
+
+// ---------------------------------------------------------------------------
+// Small-M GEMM: split-K over the waves of a workgroup, reduced through LDS
+// (the structure of the W4A16 decode kernel).  A workgroup owns NB 16-column
+// blocks and a 16-row chunk of the output (blockIdx.y); wave w owns the SG
+// 128-row groups w*SG .. w*SG+SG-1 for all NB blocks.
+//
+// FUSED: the wave reads its slice of the 16-bit activations and quantizes it
+// to MXFP8 in registers, straight into the A operand: lane l holds for row
+// l % 16 the 16 elements k = 16h + i (block h/2 of the group) and the 16
+// elements 64 + 16h + i (block 2 + h/2); its partner lane l ^ 16 holds the
+// other halves of the same two blocks, so one exchange gives both block
+// maxima.  Lane l's A scale (block h) then sits in lane 32*(h & 1) + l % 16,
+// low half for h < 2, high half otherwise.  Every workgroup repeats this for
+// its slice (a few hundred vector instructions per wave, from L2), which
+// saves the separate quantization launch.
+// Otherwise (prequantized) the A operand is two 128-bit loads of qx and one
+// byte of sx per group.
+//
+// Per weight tile a wave then issues one 128-bit and one 8-bit buffer load and
+// one block-scaled matrix-core instruction, chained on the block's
+// accumulator across groups (the scales are applied inside the instruction).
+// ---------------------------------------------------------------------------
+constexpr int kMxSmallMaxWaves = 16;
+
+template <int DT, bool FUSED, int NB, int SG, int D>
+__global__ void __launch_bounds__(kMxSmallMaxWaves * 64)
+mx_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx,
+                const uint8_t *__restrict__ wp, uint16_t *__restrict__ y, int M, int64_t K, int64_t N) {
+    static_assert(NB * SG <= 16, "tile pipeline fits in registers");
+    constexpr int T = NB * SG;
+    const int G = (int)(K / kGroup);
+    const int W = blockDim.x >> 6;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 15;
+    const int h = lane >> 4;
+    const int64_t nb0 = (int64_t)blockIdx.x * NB;
+    const int m0 = blockIdx.y * 16;
+    const int g0 = wave * SG;
+
+    // rows past M read row M - 1 (finite, in bounds); their results are dropped
+    const int64_t row = m0 + j < M ? m0 + j : M - 1;
+
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(wp + nb0 * G * kMxTileBytes), (short)0, NB * G * kMxTileBytes, 0x00020000);
+    u32x4_t raw[T];
+    int sb[T];
+    auto issue = [&](int q) {
+        const int b = q / SG, i = q % SG;
+        const int g = g0 + i < G ? g0 + i : G - 1;
+        const int toff = (b * G + g) * kMxTileBytes;
+        raw[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, lane * 16, toff, 0));
+        sb[q] = __builtin_amdgcn_raw_buffer_load_b8(wrsrc, kMxCodeBytes + lane, toff, 0);
+    };
+    // the first D weight tiles go out before the activation slice is read
+    // and quantized, so the two memory latencies overlap
+#pragma unroll
+    for (int q = 0; q < D && q < T; ++q) issue(q);
+    __builtin_amdgcn_sched_barrier(0);
+
+    i32x8_t a[SG];
+    int sa[SG];
+#pragma unroll
+    for (int i = 0; i < SG; ++i) {
+        const bool live = g0 + i < G;
+        const int64_t g = live ? g0 + i : G - 1;
+        if constexpr (FUSED) {
+            const uint16_t *xb = x + row * K + g * kGroup + 16 * h;
+            float lo0[8], lo1[8], hi0[8], hi1[8];
+            unpack8<DT>(ld128(xb), lo0);
+            unpack8<DT>(ld128(xb + 8), lo1);
+            unpack8<DT>(ld128(xb + 64), hi0);
+            unpack8<DT>(ld128(xb + 72), hi1);
+            float mlo = fmaxf(amax8(lo0), amax8(lo1));
+            float mhi = fmaxf(amax8(hi0), amax8(hi1));
+            mlo = fmaxf(mlo, __shfl_xor(mlo, 16));
+            mhi = fmaxf(mhi, __shfl_xor(mhi, 16));
+            const int elo = mx_shared_exp(mlo), ehi = mx_shared_exp(mhi);
+            a[i][0] = (int)mx_e4m3x4(lo0[0], lo0[1], lo0[2], lo0[3], elo);
+            a[i][1] = (int)mx_e4m3x4(lo0[4], lo0[5], lo0[6], lo0[7], elo);
+            a[i][2] = (int)mx_e4m3x4(lo1[0], lo1[1], lo1[2], lo1[3], elo);
+            a[i][3] = (int)mx_e4m3x4(lo1[4], lo1[5], lo1[6], lo1[7], elo);
+            a[i][4] = (int)mx_e4m3x4(hi0[0], hi0[1], hi0[2], hi0[3], ehi);
+            a[i][5] = (int)mx_e4m3x4(hi0[4], hi0[5], hi0[6], hi0[7], ehi);
+            a[i][6] = (int)mx_e4m3x4(hi1[0], hi1[1], hi1[2], hi1[3], ehi);
+            a[i][7] = (int)mx_e4m3x4(hi1[4], hi1[5], hi1[6], hi1[7], ehi);
+            const int packed = (elo + 127) | (ehi + 127) << 8;
+            const int v = __builtin_amdgcn_ds_bpermute((32 * (h & 1) + j) << 2, packed);
+            sa[i] = (v >> (8 * (h >> 1))) & 0xFF;
+        } else {
+            const uint8_t *qb = qx + row * K + g * kGroup + 16 * h;
+            const u32x4_t q0 = ld128(qb), q1 = ld128(qb + 64);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                a[i][t] = (int)q0[t];
+                a[i][4 + t] = (int)q1[t];
+            }
+            sa[i] = sx[row * (K / 32) + 4 * g + h];
+        }
+        // a group past the end of K (G not a multiple of SG) contributes zero
+        if (!live) a[i] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < T; ++q) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (q + D < T) issue(q + D);
+        __builtin_amdgcn_sched_barrier(0);
+        const int b = q / SG, i = q % SG;
+        const i32x8_t bv = {(int)raw[q][0], (int)raw[q][1], (int)raw[q][2], (int)raw[q][3], 0, 0, 0, 0};
+        acc[b] = mfma_mx(a[i], bv, acc[b], sa[i], sb[q]);
+    }
+
+    __shared__ float red[kMxSmallMaxWaves][NB][16][17];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][b][4 * h + r][j] = acc[b][r];
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < NB * 256; idx += W * 64) {
+        const int b = idx >> 8, r = (idx >> 4) & 15, col = idx & 15;
+        if (m0 + r < M) {
+            float sum = 0.f;
+            for (int w = 0; w < W; ++w) sum += red[w][b][r][col];
+            y[(int64_t)(m0 + r) * N + (nb0 + b) * 16 + col] = f2h<DT>(sum);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+size_t mx_prepacked_bytes(int64_t E, int64_t K, int64_t N) {
+    return (size_t)E * (size_t)(K / kGroup) * (size_t)(N / 16) * kMxTileBytes;
+}
+
+hipError_t launch_mx_prepack(const void *w, const void *sw, void *out, int64_t E, int64_t K, int64_t N,
+                             hipStream_t stream) {
+    const int64_t tiles = E * (K / kGroup) * (N / 16);
+    for (int64_t e = 0; e < E; ++e) {
+        // one launch per expert keeps the grid within 2^31 workgroups for any size
+        const int64_t per = tiles / E;
+        hipLaunchKernelGGL(mx_prepack_kernel, dim3((unsigned)per), dim3(64), 0, stream,
+                           (const uint8_t *)w + e * K * (N / 2), (const uint8_t *)sw + e * (K / 32) * N,
+                           (uint8_t *)out + e * per * kMxTileBytes, K, N);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize(const void *x, void *qx, void *sx, int64_t M, int64_t K, int dt, hipStream_t stream) {
+    const int64_t n8 = M * K / 8;
+    if (n8 == 0) return hipSuccess;
+    const dim3 grid((unsigned)((n8 + 255) / 256));
+    if (dt == DT_BF16)
+        hipLaunchKernelGGL(mx_quantize_kernel<DT_BF16>, grid, dim3(256), 0, stream, (const uint16_t *)x,
+                           (uint8_t *)qx, (uint8_t *)sx, n8);
+    else
+        hipLaunchKernelGGL(mx_quantize_kernel<DT_F16>, grid, dim3(256), 0, stream, (const uint16_t *)x,
+                           (uint8_t *)qx, (uint8_t *)sx, n8);
+    return hipGetLastError();
+}
+
+// Small-kernel variants (NB, SG, D); index 0 is the default.
+struct MxSmallCfg { int nb, sg, d; };
+static constexpr MxSmallCfg kMxSmallCfgs[] = {{4, 2, 4}, {4, 2, 8}, {2, 2, 4}, {4, 1, 4}, {2, 4, 8}, {1, 2, 2}};
+static int g_mx_small_cfg = -1;
+
+int mx_small_config_count() { return (int)(sizeof(kMxSmallCfgs) / sizeof(kMxSmallCfgs[0])); }
+void set_mx_small_config(int idx) { g_mx_small_cfg = idx; }
+int64_t mx_small_max_k() { return (int64_t)kMxSmallMaxWaves * 4 * kGroup; }
+
+template <int DT, bool FUSED, int NB, int SG, int D>
+static hipError_t mx_small_launch(const void *x, const void *qx, const void *sx, const void *wp, void *y, int64_t M,
+                                  int64_t K, int64_t N, hipStream_t stream) {
+    const int64_t G = K / kGroup;
+    const int64_t waves = (G + SG - 1) / SG;
+    const dim3 grid((unsigned)(N / (16 * NB)), (unsigned)((M + 15) / 16));
+    hipLaunchKernelGGL((mx_small_kernel<DT, FUSED, NB, SG, D>), grid, dim3((unsigned)(waves * 64)), 0, stream,
+                       (const uint16_t *)x, (const uint8_t *)qx, (const uint8_t *)sx, (const uint8_t *)wp,
+                       (uint16_t *)y, (int)M, K, N);
+    return hipGetLastError();
+}
+
+template <int DT, bool FUSED>
+static hipError_t mx_small_dispatch(const void *x, const void *qx, const void *sx, const void *wp, void *y,
+                                    int64_t M, int64_t K, int64_t N, hipStream_t stream) {
+    const int64_t G = K / kGroup;
+    int idx = g_mx_small_cfg;
+    if (idx < 0 || idx >= mx_small_config_count()) idx = 0;
+    MxSmallCfg c = kMxSmallCfgs[idx];
+    while ((G + c.sg - 1) / c.sg > kMxSmallMaxWaves && c.sg < 4) c.sg *= 2;
+    if ((G + c.sg - 1) / c.sg > kMxSmallMaxWaves) return hipErrorInvalidValue;   // K > mx_small_max_k()
+    while (c.nb * c.sg > 16) c.nb /= 2;
+    if (c.d > c.nb * c.sg) c.d = c.nb * c.sg;
+    while ((N / 16) % c.nb != 0) c.nb /= 2;
+#define W4_MX(NBV, SGV, DV)                                                                                   \
+    if (c.nb == NBV && c.sg == SGV && c.d == DV)                                                              \
+        return mx_small_launch<DT, FUSED, NBV, SGV, DV>(x, qx, sx, wp, y, M, K, N, stream);
+    W4_MX(4, 2, 8) W4_MX(4, 2, 4) W4_MX(2, 2, 4) W4_MX(4, 1, 4) W4_MX(2, 4, 8) W4_MX(1, 2, 2)
+    W4_MX(4, 4, 8) W4_MX(2, 2, 2) W4_MX(1, 4, 4) W4_MX(2, 1, 2) W4_MX(1, 1, 1) W4_MX(1, 2, 1)
+    W4_MX(2, 1, 1) W4_MX(4, 1, 2) W4_MX(1, 4, 2) W4_MX(2, 4, 4) W4_MX(4, 2, 2) W4_MX(4, 4, 4)
+    W4_MX(4, 1, 1) W4_MX(2, 2, 1) W4_MX(1, 4, 1) W4_MX(2, 4, 2) W4_MX(1, 2, 4)
+#undef W4_MX
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mx_gemm_small(const void *x, const void *qx, const void *sx, const void *wp, void *y, int64_t M,
+                                int64_t K, int64_t N, int dt, hipStream_t stream) {
+    if (M == 0) return hipSuccess;
+    const bool fused = x != nullptr;
+    if (dt == DT_BF16)
+        return fused ? mx_small_dispatch<DT_BF16, true>(x, qx, sx, wp, y, M, K, N, stream)
+                     : mx_small_dispatch<DT_BF16, false>(x, qx, sx, wp, y, M, K, N, stream);
+    return fused ? mx_small_dispatch<DT_F16, true>(x, qx, sx, wp, y, M, K, N, stream)
+                 : mx_small_dispatch<DT_F16, false>(x, qx, sx, wp, y, M, K, N, stream);
+}
+
+}  // namespace w4

@@ -29,6 +29,9 @@ bytes: tokens in and out (T*H*2 each), routing ids and weights (T*topk*8), and
 the active experts' gate/up and down weights with their scales.  mx_decode is
 W4A8-MXFP4 at the decode shape (bf16 x quantized to MXFP8 inside the GEMM,
 MXFP4 weights); its bytes: x + E2M1 codes (K*N/2) + E8M0 scales (K/32*N) + y.
+mx_prefill is W4A8-MXFP4 at M=N=K=4096 (activation quantization into a
+workspace, then the LDS-staged tile kernel); judged on flops against the
+5.0 PFLOP/s dense fp8 peak.
 
 Algorithmic bytes of one dense call: x (M*K*2) + packed weights (K*N/2) +
 scales (K/128*N*2) + zero points (K/128*N/2, if any) + y (M*N*2).
@@ -313,6 +316,26 @@ def mx_decode_workload():
     return calls, len(wps)
 
 
+def mx_prefill_workload():
+    """W4A8-MXFP4 at the prefill shape (M=N=K=4096): bf16 x quantized to MXFP8
+    into a workspace, then the tile kernel; one call = both launches."""
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    M = K = N = 4096
+    p = synth.make_mx(M, K, N, synth.BF16, name="mx_prefill")
+    wp = torch.empty(w4.w4a8_mxfp4_prepacked_bytes(1, K, N), dtype=torch.uint8, device="cuda:0")
+    w4.w4a8_mxfp4_prepack(_dev(p.w), _dev(p.sw), wp, 1, K, N)
+    x = _dev(p.x)
+    y = torch.empty((M, N), dtype=torch.int16, device="cuda:0")
+    nb = w4.w4a8_mxfp4_workspace_bytes(M, K)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+
+    def launch(i):
+        w4.w4a8_mxfp4_gemm(x, wp, y, M, K, N, synth.BF16, ws, nb)
+    return [("mx_prefill", launch, mx_bytes(M, K, N), 2 * M * N * K)], 1
+
+
 def _capture(calls, first, count):
     """One HIP graph holding `count` steps (every call once per step, buffer set
     first + i for step i), captured on a side stream.  Replaying it launches the
@@ -436,7 +459,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["decode", "tiny", "prefill", "msd", "moe", "moe_chain", "msd_page",
-                                       "msd_basic", "mx_decode"], default=None,
+                                       "msd_basic", "mx_decode", "mx_prefill"], default=None,
                     help="run only this workload (profiling); no JSON headline unless decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-config extras")
@@ -466,7 +489,8 @@ def main():
 
     builders = {"decode": decode_workload, "tiny": tiny_workload, "prefill": prefill_workload,
                 "msd": msd_workload, "moe": moe_workload, "moe_chain": moe_chain_workload,
-                "msd_page": msd_page_workload, "msd_basic": msd_basic_workload, "mx_decode": mx_decode_workload}
+                "msd_page": msd_page_workload, "msd_basic": msd_basic_workload, "mx_decode": mx_decode_workload,
+                "mx_prefill": mx_prefill_workload}
     if args.only and args.only != "decode":
         _, out = measure(args.only, builders[args.only], args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **out}), flush=True)
@@ -482,7 +506,8 @@ def main():
 
     extra = {}
     if not args.no_extra and not args.only:
-        for name in ("tiny", "prefill", "msd", "moe", "moe_chain", "msd_page", "msd_basic", "mx_decode"):
+        for name in ("tiny", "prefill", "msd", "moe", "moe_chain", "msd_page", "msd_basic", "mx_decode",
+                     "mx_prefill"):
             print(f"[bench] {name} workload", file=sys.stderr, flush=True)
             _, extra[name] = measure(name, builders[name], max(10, args.steps // 2), args.warmup)
             torch.cuda.empty_cache()

@@ -244,8 +244,11 @@ w4a16_status w4a16_fused_moe(const void *x, const int32_t *topk_ids, const float
  * gfx950's block-scaled matrix-core instruction takes both formats and both
  * scales directly; the article's in-kernel weight conversion (needed on GPUs
  * without MXFP4 matrix cores) is not needed here.
- * Shape rules: K % 128 == 0, N % 64 == 0, K <= 8192, M >= 0, E >= 1.
- * Alignment: x, qx, w, w_packed, workspace 16 bytes; y 2 bytes.
+ * Shape rules: K % 128 == 0, N % 64 == 0, M >= 0, E >= 1, and one expert's
+ * packed weights below 2 GiB ((K/128) * (N/16) * 1088 < 2^31).
+ * Alignment: x, qx, w, w_packed, workspace 16 bytes; sx 4 bytes; y 2 bytes.
+ * Kernels: M <= 16 with K <= 8192 runs a split-K kernel; everything else a
+ * tile kernel that stages the quantized activations in LDS.
  */
 
 /* Bytes of the prepacked MXFP4 buffer: E * (K/128) * (N/16) * 1088. */
@@ -273,15 +276,18 @@ w4a16_status w4a8_mxfp8_quantize(const void *x, void *qx, void *sx, int64_t M, i
 w4a16_status w4a8_mxfp4_gemm_prequant(const void *qx, const void *sx, const void *w_packed, void *y, int64_t M,
                                       int64_t K, int64_t N, int dt, void *stream);
 
-/* Scratch for w4a8_mxfp4_gemm: 0 when M <= 16 (activations are quantized in
- * the GEMM's registers), else room for qx and sx. */
+/* Scratch for w4a8_mxfp4_gemm: 0 when the split-K kernel runs (M <= 16,
+ * K <= 8192: activations are quantized in its registers), else room for qx
+ * and sx. */
 size_t w4a8_mxfp4_workspace_bytes(int64_t M, int64_t K);
 
 /*
  * y[M][N] = MXFP8(x) . MXFP4(W): quantizes x (dtype dt) and multiplies.  For
- * M <= 16 one kernel does both (each wave quantizes its K slice in registers);
- * otherwise x is quantized into the workspace first.  workspace: device,
- * >= w4a8_mxfp4_workspace_bytes(M, K) bytes (may be NULL when that is 0).
+ * M <= 16 (K <= 8192) one kernel does both (each wave quantizes its K slice
+ * in registers); otherwise x is quantized into the workspace first.
+ * workspace: device, >= w4a8_mxfp4_workspace_bytes(M, K) bytes (may be NULL
+ * when that is 0); contents on return unspecified; calls sharing one
+ * workspace must be ordered on one stream.
  */
 w4a16_status w4a8_mxfp4_gemm(const void *x, const void *w_packed, void *y, int64_t M, int64_t K, int64_t N,
                              int dt, void *workspace, size_t workspace_bytes, void *stream);

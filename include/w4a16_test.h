@@ -76,6 +76,12 @@ int w4a16_test_msd_config(int idx);
  * number of variants. */
 int w4a16_test_mx_small_config(int idx);
 
+/* Select the W4A8-MXFP4 tile kernel variant (-1 = automatic); returns the
+ * number of variants.  w4a16_test_force_variant(2) also forces the W4A8-MXFP4
+ * calls onto the tile kernel (and then w4a8_mxfp4_workspace_bytes asks for
+ * a workspace at every M). */
+int w4a16_test_mx_tile_config(int idx);
+
 /* Name of the kernel variant the dispatcher picks for a dense call. */
 const char *w4a16_test_variant_name(int64_t M, int64_t K, int64_t N, int dt, int has_zero);
 

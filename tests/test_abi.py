@@ -186,6 +186,7 @@ def test_mxfp4_sizes_and_validation():
     assert w4.w4a8_mxfp4_prepacked_bytes(1, 4096, 14336) == 32 * 896 * 1088
     assert w4.w4a8_mxfp4_prepacked_bytes(0, 128, 64) == 0
     assert w4.w4a8_mxfp4_workspace_bytes(16, 4096) == 0               # quantized in registers
+    assert w4.w4a8_mxfp4_workspace_bytes(16, 16384) >= 16 * 16384     # K beyond the split-K kernel
     ws = w4.w4a8_mxfp4_workspace_bytes(17, 4096)
     assert ws >= 17 * 4096 + 17 * 128 and (17 * 4096 + 255) // 256 * 256 <= ws
     L = w4.lib()
@@ -195,7 +196,8 @@ def test_mxfp4_sizes_and_validation():
     cases = [
         (lambda: L.w4a8_mxfp4_gemm(F, F, F, 1, 100, 64, 1, None, 0, None), 2),        # K % 128
         (lambda: L.w4a8_mxfp4_gemm(F, F, F, 1, 128, 32, 1, None, 0, None), 2),        # N % 64
-        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 1, 16384, 64, 1, None, 0, None), 2),      # K > 8192
+        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 1, 16384, 64, 1, None, 0, None), 5),      # K > 8192: tile kernel
+        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 1, 8192, 1 << 20, 1, None, 0, None), 2),  # packed > 2 GiB
         (lambda: L.w4a8_mxfp4_gemm(F, F, F, -1, 128, 64, 1, None, 0, None), 2),
         (lambda: L.w4a8_mxfp4_gemm(F, F, F, 1, 128, 64, 5, None, 0, None), 3),        # dtype
         (lambda: L.w4a8_mxfp4_gemm(None, F, F, 1, 128, 64, 1, None, 0, None), 1),

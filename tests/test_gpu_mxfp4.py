@@ -178,6 +178,51 @@ def test_gemm_prequant(orc, M):
     _check_bound(orc, got, qx, sx, p, f"mx_prequant_m{M}")
 
 
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F16])
+@pytest.mark.parametrize("M,K,N", [(300, 2048, 512), (1000, 1024, 1088), (129, 16384, 192)])
+def test_gemm_tile(orc, dtype, M, K, N):
+    """The tile kernel: several row and column tiles with ragged tails, and a K
+    beyond the split-K kernel's reach."""
+    print(f"[case] mx tile dtype={dtype} M={M} K={K} N={N}", flush=True)
+    from gpu_helpers import to_host_u16
+    p = synth.make_mx(M, K, N, dtype, seed=M + K + N, outlier_frac=0.01)
+    got = to_host_u16(DevMx(p).gemm())
+    qx, sx = orc.mxfp8_quantize(p.x, M, K, dtype)
+    _check_bound(orc, got, qx, sx, p, f"mx_tile_{M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_tile_forced_small_m(orc, M):
+    import weight_only_quantized_amd as w4
+    from gpu_helpers import to_host_u16
+    p = synth.make_mx(M, 1024, 320, synth.BF16, seed=40 + M)
+    d = DevMx(p)
+    old = w4.w4a16_test_force_variant(2)
+    try:
+        print(f"[case] mx tile forced M={M}", flush=True)
+        got = to_host_u16(d.gemm())
+    finally:
+        w4.w4a16_test_force_variant(old)
+    qx, sx = orc.mxfp8_quantize(p.x, M, p.K, p.dtype)
+    _check_bound(orc, got, qx, sx, p, f"mx_tile_forced_m{M}")
+
+
+def test_tile_configs(orc):
+    import weight_only_quantized_amd as w4
+    from gpu_helpers import to_host_u16
+    p = synth.make_mx(200, 1024, 576, synth.F16, seed=8)
+    d = DevMx(p)
+    qx, sx = orc.mxfp8_quantize(p.x, p.M, p.K, p.dtype)
+    n = w4.w4a16_test_mx_tile_config(-1)
+    try:
+        for c in range(n):
+            w4.w4a16_test_mx_tile_config(c)
+            print(f"[case] mx tile config {c}", flush=True)
+            _check_bound(orc, to_host_u16(d.gemm()), qx, sx, p, f"mx_tile_cfg{c}")
+    finally:
+        w4.w4a16_test_mx_tile_config(-1)
+
+
 def test_small_configs(orc):
     import weight_only_quantized_amd as w4
     from gpu_helpers import to_host_u16

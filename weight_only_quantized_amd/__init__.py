@@ -64,6 +64,7 @@ _SIGS = {
     "w4a16_test_tile_config": ([C.c_int], C.c_int),
     "w4a16_test_msd_config": ([C.c_int], C.c_int),
     "w4a16_test_mx_small_config": ([C.c_int], C.c_int),
+    "w4a16_test_mx_tile_config": ([C.c_int], C.c_int),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -246,3 +247,7 @@ def w4a16_test_msd_config(idx: int) -> int:
 
 def w4a16_test_mx_small_config(idx: int) -> int:
     return lib().w4a16_test_mx_small_config(int(idx))
+
+
+def w4a16_test_mx_tile_config(idx: int) -> int:
+    return lib().w4a16_test_mx_tile_config(int(idx))

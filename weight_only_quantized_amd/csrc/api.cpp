@@ -65,14 +65,25 @@ w4a16_status check_kn_groups(int64_t K, int64_t N, int64_t group_size, int *gm) 
 
 // W4A8-MXFP4 shapes: K a multiple of 128 up to the small kernel's K limit,
 // N a multiple of 64.
+// The packed weights of one expert are addressed with 32-bit byte offsets.
 w4a16_status check_mx_kn(int64_t K, int64_t N) {
     if (K <= 0 || N <= 0 || K % 128 != 0 || N % 64 != 0) return W4A16_ERR_SHAPE;
-    if (K > w4::mx_small_max_k() || N > (int64_t(1) << 30)) return W4A16_ERR_SHAPE;
+    if (K > (int64_t(1) << 30) || N > (int64_t(1) << 30)) return W4A16_ERR_SHAPE;
+    if ((K / 128) * (N / 16) * 1088 > (int64_t(1) << 31) - 1) return W4A16_ERR_SHAPE;
     return W4A16_OK;
 }
 
-// Row limit of the MXFP4 GEMM (16-row chunks on the second grid axis).
-constexpr int64_t kMxMaxM = 65535 * 16;
+// Row limit of the MXFP4 GEMM (32-bit row tiles on the first grid axis).
+constexpr int64_t kMxMaxM = (int64_t(1) << 31) - 1;
+
+// MXFP4 dispatch: M <= 16 (and K within the split-K kernel's reach) runs the
+// split-K kernel, everything else the tile kernel; the test hook can force
+// the tile kernel.
+bool mx_use_small(int64_t M, int64_t K) {
+    const int forced = g_force_variant.load(std::memory_order_relaxed);
+    if (forced == 2) return false;
+    return M <= 16 && K <= w4::mx_small_max_k();
+}
 
 // Offset of sx behind qx in the W4A8-MXFP4 workspace (256-byte aligned).
 size_t mx_ws_sx_offset(int64_t M, int64_t K) { return ((size_t)M * (size_t)K + 255) & ~(size_t)255; }
@@ -353,6 +364,11 @@ int w4a16_test_mx_small_config(int idx) {
     return w4::mx_small_config_count();
 }
 
+int w4a16_test_mx_tile_config(int idx) {
+    w4::set_mx_tile_config(idx);
+    return w4::mx_tile_config_count();
+}
+
 // ---- W4A8-MXFP4 -------------------------------------------------------------
 
 size_t w4a8_mxfp4_prepacked_bytes(int64_t E, int64_t K, int64_t N) {
@@ -390,13 +406,15 @@ w4a16_status w4a8_mxfp4_gemm_prequant(const void *qx, const void *sx, const void
     if (M < 0 || M > kMxMaxM) return W4A16_ERR_SHAPE;
     if (M == 0) return W4A16_OK;
     if (!qx || !sx || !w_packed || !y) return W4A16_ERR_NULL;
-    if (!aligned(qx, 16) || !aligned(w_packed, 16) || !aligned(y, 2)) return W4A16_ERR_ALIGN;
+    if (!aligned(qx, 16) || !aligned(sx, 4) || !aligned(w_packed, 16) || !aligned(y, 2)) return W4A16_ERR_ALIGN;
     if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
-    return map_err(w4::launch_mx_gemm_small(nullptr, qx, sx, w_packed, y, M, K, N, dt, (hipStream_t)stream));
+    const hipStream_t s = (hipStream_t)stream;
+    if (mx_use_small(M, K)) return map_err(w4::launch_mx_gemm_small(nullptr, qx, sx, w_packed, y, M, K, N, dt, s));
+    return map_err(w4::launch_mx_gemm_tile(qx, sx, w_packed, y, M, K, N, dt, s));
 }
 
 size_t w4a8_mxfp4_workspace_bytes(int64_t M, int64_t K) {
-    if (M <= 16 || K <= 0) return 0;
+    if (M <= 0 || K <= 0 || mx_use_small(M, K)) return 0;
     return mx_ws_sx_offset(M, K) + (size_t)M * (size_t)(K / 32);
 }
 
@@ -414,12 +432,12 @@ w4a16_status w4a8_mxfp4_gemm(const void *x, const void *w_packed, void *y, int64
     if (need > 0 && !aligned(workspace, 16)) return W4A16_ERR_ALIGN;
     if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
     const hipStream_t s = (hipStream_t)stream;
-    if (M <= 16) return map_err(w4::launch_mx_gemm_small(x, nullptr, nullptr, w_packed, y, M, K, N, dt, s));
+    if (mx_use_small(M, K)) return map_err(w4::launch_mx_gemm_small(x, nullptr, nullptr, w_packed, y, M, K, N, dt, s));
     uint8_t *qx = (uint8_t *)workspace;
     uint8_t *sx = qx + mx_ws_sx_offset(M, K);
     hipError_t e = w4::launch_mx_quantize(x, qx, sx, M, K, dt, s);
     if (e != hipSuccess) return map_err(e);
-    return map_err(w4::launch_mx_gemm_small(nullptr, qx, sx, w_packed, y, M, K, N, dt, s));
+    return map_err(w4::launch_mx_gemm_tile(qx, sx, w_packed, y, M, K, N, dt, s));
 }
 
 }  // extern "C"

@@ -87,5 +87,10 @@ void set_mx_small_config(int idx);
 int64_t mx_small_max_k();
 hipError_t launch_mx_gemm_small(const void *x, const void *qx, const void *sx, const void *wp, void *y, int64_t M,
                                 int64_t K, int64_t N, int dt, hipStream_t stream);
+// Large-M tile kernel from prequantized activations (sx 4-byte aligned).
+int mx_tile_config_count();
+void set_mx_tile_config(int idx);
+hipError_t launch_mx_gemm_tile(const void *qx, const void *sx, const void *wp, void *y, int64_t M, int64_t K,
+                               int64_t N, int dt, hipStream_t stream);
 
 }  // namespace w4

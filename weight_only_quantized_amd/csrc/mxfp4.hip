@@ -300,7 +300,11 @@ mx_tile_kernel(const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx, c
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BM * kMxRowB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform: readfirstlane lets the compiler keep every
+    // value derived from it (the weight-tile offsets) in scalar registers, as
+    // the buffer loads' scalar offset operand requires
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int j = lane & 15, h = lane >> 4;
     const int G = (int)(K / kGroup);
@@ -372,20 +376,35 @@ mx_tile_kernel(const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx, c
         const int gn = g + 1 < G ? g + 1 : g;     // the last step re-reads: no branch around loads
         load_a(gn);
         load_b(gn, bnx, snx);
-        const uint8_t *abase = lds + buf * BM * kMxRowB;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const uint8_t *ap = abase + (arow0 + rt * 16) * kMxRowB;
+        const uint8_t *abase = lds + buf * BM * kMxRowB + arow0 * kMxRowB;
+        // A operands are read from LDS one 16-row block ahead of their use
+        auto read_a = [&](int rt, i32x8_t &av, int &sa) {
+            const uint8_t *ap = abase + rt * 16 * kMxRowB;
             const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(ap + 16 * h);
             const u32x4_t a1 = *reinterpret_cast<const u32x4_t *>(ap + 64 + 16 * h);
-            const int sa = ap[128 + h];
-            const i32x8_t av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                                (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            sa = ap[128 + h];
+            av = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        };
+        i32x8_t avs[2];
+        int sas[2];
+        read_a(0, avs[0], sas[0]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            // the scheduling barriers keep the next block's LDS reads ahead of
+            // this block's products (left alone, the compiler issues them after
+            // the products and waits at once, draining the matrix pipe)
+            if (rt + 1 < RT) read_a(rt + 1, avs[(rt + 1) & 1], sas[(rt + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            const i32x8_t &av = avs[rt & 1];
+            const int sa = sas[rt & 1];
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                const i32x8_t bv = {(int)bw[ct][0], (int)bw[ct][1], (int)bw[ct][2], (int)bw[ct][3], 0, 0, 0, 0};
+                // an fp4 B operand occupies the low four registers only
+                const u32x4_t b4 = bw[ct];
+                const i32x8_t bv = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(b4, b4, 0, 1, 2, 3, -1, -1, -1, -1));
                 acc[rt][ct] = mfma_mx(av, bv, acc[rt][ct], sa, sw[ct]);
             }
+            __builtin_amdgcn_sched_barrier(0);
             // stage the next slice halfway through the products; the buffer
             // written was last read in the previous step, before its barrier
             if (rt == RT / 2) store_a(buf ^ 1);
@@ -501,14 +520,16 @@ hipError_t launch_mx_gemm_small(const void *x, const void *qx, const void *sx, c
 }
 
 
-// Tile-kernel variants (BM, BN, WM, WN).  Index 0 (128 x 64 wave tiles, four
-// waves, two workgroups per compute unit) is the default; index 5 (32-row
-// tiles) serves M <= 64, where a 128-row tile would mostly multiply padding.
-// Measured on 4096^3 (quantization included): 86 us for index 0 against
-// 96-117 us for the others.
+// Tile-kernel variants (BM, BN, WM, WN).  Defaults: index 7 (128 x 512, eight
+// 128 x 64-column waves, one workgroup per compute unit: the fewest bytes per
+// product) for N >= 2048, index 0 (128 x 256, four such waves, two workgroups
+// per compute unit) for smaller N, index 5 (32-row tiles) for M <= 64, where a
+// 128-row tile would mostly multiply padding.  Measured on 4096^3
+// (quantization included): 77 us for index 7, 81 us for index 0, 82-104 us
+// for the others.
 struct MxTileCfg { int bm, bn, wm, wn; };
 static constexpr MxTileCfg kMxTileCfgs[] = {{128, 256, 1, 4}, {128, 256, 2, 4}, {128, 128, 2, 2}, {64, 128, 1, 2},
-                                            {64, 256, 1, 4}, {32, 256, 1, 4}};
+                                            {64, 256, 1, 4}, {32, 256, 1, 4}, {256, 256, 2, 4}, {128, 512, 1, 8}};
 static int g_mx_tile_cfg = -1;
 
 int mx_tile_config_count() { return (int)(sizeof(kMxTileCfgs) / sizeof(kMxTileCfgs[0])); }
@@ -527,7 +548,7 @@ template <int DT>
 static hipError_t mx_tile_dispatch(const void *qx, const void *sx, const void *wp, void *y, int64_t M, int64_t K,
                                    int64_t N, hipStream_t stream) {
     int idx = g_mx_tile_cfg;
-    if (idx < 0 || idx >= mx_tile_config_count()) idx = M <= 64 ? 5 : 0;
+    if (idx < 0 || idx >= mx_tile_config_count()) idx = M <= 64 ? 5 : (N >= 2048 ? 7 : 0);
     // a wave's columns must be all in or all out of N
     if (N % (kMxTileCfgs[idx].bn / kMxTileCfgs[idx].wn) != 0) idx = 0;
     const MxTileCfg c = kMxTileCfgs[idx];
@@ -535,7 +556,7 @@ static hipError_t mx_tile_dispatch(const void *qx, const void *sx, const void *w
     if (c.bm == BMV && c.bn == BNV && c.wm == WMV && c.wn == WNV)                                      \
         return mx_tile_launch<DT, BMV, BNV, WMV, WNV>(qx, sx, wp, y, M, K, N, stream);
     W4_MXT(64, 256, 1, 4) W4_MXT(128, 256, 2, 4) W4_MXT(128, 128, 2, 2) W4_MXT(64, 128, 1, 2)
-    W4_MXT(128, 256, 1, 4) W4_MXT(32, 256, 1, 4)
+    W4_MXT(128, 256, 1, 4) W4_MXT(32, 256, 1, 4) W4_MXT(256, 256, 2, 4) W4_MXT(128, 512, 1, 8)
 #undef W4_MXT
     return hipErrorInvalidValue;
 }

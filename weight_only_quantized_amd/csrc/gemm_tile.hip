@@ -59,7 +59,10 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BM * ROWB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform (readfirstlane: values derived from it stay
+    // in scalar registers)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int G = (int)(K / kGroup);
     const int64_t NBLK = N / 16;

@@ -66,6 +66,7 @@ def lib():
             "oracle_moe_sum": ([_p, _p, _p, _i64, _i64, _i64, C.c_int, _p], None),
             "oracle_fused_moe": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
                                   C.c_int, _p, _i64, _p], None),
+            "oracle_w8a16": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p, _p], None),
             "oracle_e4m3_to_double": ([C.c_uint8], C.c_double),
             "oracle_e2m1_to_double": ([C.c_uint8], C.c_double),
             "oracle_e8m0_to_double": ([C.c_uint8], C.c_double),
@@ -143,7 +144,8 @@ def msd_amax(x, M, K, group=128):
 
 def msd_layers(x, amax, M, K, group=128):
     out = np.empty((3, M, K), dtype=np.int8)
-    lib().oracle_msd_layers(_ptr(x), _ptr(np.ascontiguousarray(amax, np.float32)), M, K, group, _ptr(out))
+    am = np.ascontiguousarray(amax, np.float32)        # bound: outlives the call
+    lib().oracle_msd_layers(_ptr(x), _ptr(am), M, K, group, _ptr(out))
     return out
 
 
@@ -156,7 +158,8 @@ def msd_decompose_one(a: float, amax: float):
 
 def msd_yint(layers, w, M, K, N, group=128):
     out = np.empty((K // group, 3, M, N), dtype=np.int32)
-    lib().oracle_msd_yint(_ptr(np.ascontiguousarray(layers, np.int8)), _ptr(w), M, K, N, group, _ptr(out))
+    ly = np.ascontiguousarray(layers, np.int8)
+    lib().oracle_msd_yint(_ptr(ly), _ptr(w), M, K, N, group, _ptr(out))
     return out
 
 
@@ -199,8 +202,8 @@ def moe_sum(o, row_of, topk_w, dtype):
     T, topk = w.shape
     N = o.shape[1]
     out = np.empty((T, N), dtype=np.uint16)
-    lib().oracle_moe_sum(_ptr(o), _ptr(np.ascontiguousarray(row_of, np.int32)), _ptr(w), T, topk, N,
-                         dtype, _ptr(out))
+    ro = np.ascontiguousarray(row_of, np.int32)
+    lib().oracle_moe_sum(_ptr(o), _ptr(ro), _ptr(w), T, topk, N, dtype, _ptr(out))
     return out
 
 
@@ -209,18 +212,33 @@ def fused_moe(c, tokens=None):
     (default: all); returns [P][H] bits."""
     tok = np.arange(c.T, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, np.int64)
     out = np.empty((tok.shape[0], c.H), dtype=np.uint16)
-    lib().oracle_fused_moe(_ptr(c.x), _ptr(np.ascontiguousarray(c.topk_ids, np.int32)),
-                           _ptr(np.ascontiguousarray(c.topk_w, np.float32)), _ptr(c.w13), _ptr(c.s13),
+    ids = np.ascontiguousarray(c.topk_ids, np.int32)
+    tw = np.ascontiguousarray(c.topk_w, np.float32)
+    lib().oracle_fused_moe(_ptr(c.x), _ptr(ids), _ptr(tw), _ptr(c.w13), _ptr(c.s13),
                            _ptr(c.z13), _ptr(c.w2), _ptr(c.s2), _ptr(c.z2), c.T, c.topk, c.E, c.H, c.I,
                            128, c.dtype, _ptr(tok), tok.shape[0], _ptr(out))
     return out
+
+
+def w8a16(x, w, scale, zero, M, K, N, dtype, group=128):
+    """W8A16: w [K][N] bytes (int8, or uint8 with zero [K/group][N]); returns
+    (y64 [M,N] float64, y [M,N] uint16 bits)."""
+    y64 = np.empty((M, N), dtype=np.float64)
+    y = np.empty((M, N), dtype=np.uint16)
+    # contiguous copies are bound to names so they outlive the call
+    xc, wc, sc = (np.ascontiguousarray(x, np.uint16), np.ascontiguousarray(w, np.uint8),
+                  np.ascontiguousarray(scale, np.uint16))
+    zc = None if zero is None else np.ascontiguousarray(zero, np.uint8)
+    lib().oracle_w8a16(_ptr(xc), _ptr(wc), _ptr(sc), _ptr(zc), M, K, N, group, dtype, _ptr(y64), _ptr(y))
+    return y64, y
 
 
 def mxfp8_quantize(x, M, K, dtype):
     """x bits [M][K] -> (E4M3 codes [M][K] uint8, E8M0 scales [M][K/32] uint8)."""
     qx = np.empty((M, K), dtype=np.uint8)
     sx = np.empty((M, K // 32), dtype=np.uint8)
-    lib().oracle_mxfp8_quantize(_ptr(np.ascontiguousarray(x, np.uint16)), M, K, dtype, _ptr(qx), _ptr(sx))
+    xc = np.ascontiguousarray(x, np.uint16)
+    lib().oracle_mxfp8_quantize(_ptr(xc), M, K, dtype, _ptr(qx), _ptr(sx))
     return qx, sx
 
 
@@ -228,21 +246,22 @@ def w4a8_mxfp4(qx, sx, w, sw, M, K, N, dtype):
     """Return (y64 [M,N], y [M,N] bits) of the MXFP8 x MXFP4 product."""
     y64 = np.empty((M, N), dtype=np.float64)
     y = np.empty((M, N), dtype=np.uint16)
-    lib().oracle_w4a8_mxfp4(_ptr(np.ascontiguousarray(qx, np.uint8)), _ptr(np.ascontiguousarray(sx, np.uint8)),
-                            _ptr(np.ascontiguousarray(w, np.uint8)), _ptr(np.ascontiguousarray(sw, np.uint8)),
-                            M, K, N, dtype, _ptr(y64), _ptr(y))
+    qc, sc, wc, swc = (np.ascontiguousarray(a, np.uint8) for a in (qx, sx, w, sw))
+    lib().oracle_w4a8_mxfp4(_ptr(qc), _ptr(sc), _ptr(wc), _ptr(swc), M, K, N, dtype, _ptr(y64), _ptr(y))
     return y64, y
 
 
 def prepack(w, E, K, N, is_signed):
     out = np.empty(E * K * N // 2, dtype=np.uint8)
-    lib().oracle_prepack(_ptr(np.ascontiguousarray(w, np.uint8)), _ptr(out), E, K, N, int(is_signed))
+    wc = np.ascontiguousarray(w, np.uint8)
+    lib().oracle_prepack(_ptr(wc), _ptr(out), E, K, N, int(is_signed))
     return out
 
 
 def unpack(packed, E, K, N, is_signed):
     out = np.empty(E * K * N // 2, dtype=np.uint8)
-    lib().oracle_unpack(_ptr(np.ascontiguousarray(packed, np.uint8)), _ptr(out), E, K, N, int(is_signed))
+    pc = np.ascontiguousarray(packed, np.uint8)
+    lib().oracle_unpack(_ptr(pc), _ptr(out), E, K, N, int(is_signed))
     return out
 
 

@@ -117,6 +117,14 @@ void oracle_fused_moe(const uint16_t *x, const int32_t *topk_ids, const float *t
                       int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I,
                       int64_t group, int dtype, const int64_t *tok, int64_t P, uint16_t *out);
 
+/* ---- W8A16 (Humming article: the WNA16 setting with N = 8, i.e. 8-bit integer
+ * weights with 16-bit activations, group scales and optional zero points).
+ * w[K][N] one byte per weight: two's complement int8 when zero == NULL, else
+ * uint8 with uint8 zero points zero[K/group][N]; scale[K/group][N] in dtype.
+ * y64 = x . ((q - z) * s) in fp64 (every product exact), y = RNE(y64). ---- */
+void oracle_w8a16(const uint16_t *x, const uint8_t *w, const uint16_t *scale, const uint8_t *zero,
+                  int64_t M, int64_t K, int64_t N, int64_t group, int dtype, double *y64, uint16_t *y);
+
 /* ---- W4A8-MXFP4 (Humming article: W4A8-MXFP4 path; formats per the OCP
  * Microscaling (MX) specification v1.0: blocks of 32 elements along K sharing
  * one power-of-two E8M0 scale).  Weights: E2M1 codes w[K][N/2] (two per byte

@@ -31,7 +31,9 @@ W4A8-MXFP4 at the decode shape (bf16 x quantized to MXFP8 inside the GEMM,
 MXFP4 weights); its bytes: x + E2M1 codes (K*N/2) + E8M0 scales (K/32*N) + y.
 mx_prefill is W4A8-MXFP4 at M=N=K=4096 (activation quantization into a
 workspace, then the LDS-staged tile kernel); judged on flops against the
-5.0 PFLOP/s dense fp8 peak.
+5.0 PFLOP/s dense fp8 peak.  w8_decode / w8_prefill are W8A16 (8-bit integer
+weights) at the decode shape (uint8 with zero points) and at 4096^3 (int8);
+bytes: x + K*N weight bytes + scales (+ zero points, one byte each) + y.
 
 Algorithmic bytes of one dense call: x (M*K*2) + packed weights (K*N/2) +
 scales (K/128*N*2) + zero points (K/128*N/2, if any) + y (M*N*2).
@@ -336,6 +338,53 @@ def mx_prefill_workload():
     return [("mx_prefill", launch, mx_bytes(M, K, N), 2 * M * N * K)], 1
 
 
+def w8_bytes(M, K, N, zero):
+    """Algorithmic bytes of one W8A16 call: x + 8-bit weights + scales (+ zero
+    points, one byte each) + y."""
+    G = K // 128
+    return M * K * 2 + K * N + G * N * 2 + (G * N if zero else 0) + M * N * 2
+
+
+def w8_decode_workload():
+    """W8A16 at the decode shape: M in {1, 4, 16}, K=4096, N=14336, bf16 x,
+    uint8 weights with uint8 zero points, bf16 scales, group 128."""
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    ps = {M: synth.make_w8(M, 4096, 14336, synth.BF16, signed=False, seed=0) for M in (1, 4, 16)}
+    p1 = ps[1]
+    K, N = p1.K, p1.N
+    wp = torch.empty(w4.w8a16_prepacked_bytes(1, K, N), dtype=torch.uint8, device="cuda:0")
+    w4.w8a16_prepack(_dev(p1.w), wp, 1, K, N, 0)
+    sc, zr = _dev(p1.scale), _dev(p1.zero)
+    wps = _copies(wp, wp.numel())
+    xs = {M: _dev(ps[M].x) for M in ps}
+    ys = {M: torch.empty((M, N), dtype=torch.int16, device="cuda:0") for M in ps}
+    calls = []
+    for M in (1, 4, 16):
+        def launch(i, M=M):
+            w4.w8a16_gemm(xs[M], wps[i % len(wps)], sc, zr, ys[M], M, K, N, 128, synth.BF16)
+        calls.append((f"w8_decode_m{M}", launch, w8_bytes(M, K, N, True), 2 * M * N * K))
+    return calls, len(wps)
+
+
+def w8_prefill_workload():
+    """W8A16 at the prefill shape (M=N=K=4096), bf16 x, int8 weights."""
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    M = K = N = 4096
+    p = synth.make_w8(M, K, N, synth.BF16, signed=True, seed=0)
+    wp = torch.empty(w4.w8a16_prepacked_bytes(1, K, N), dtype=torch.uint8, device="cuda:0")
+    w4.w8a16_prepack(_dev(p.w), wp, 1, K, N, 1)
+    x, sc = _dev(p.x), _dev(p.scale)
+    y = torch.empty((M, N), dtype=torch.int16, device="cuda:0")
+
+    def launch(i):
+        w4.w8a16_gemm(x, wp, sc, None, y, M, K, N, 128, synth.BF16)
+    return [("w8_prefill", launch, w8_bytes(M, K, N, False), 2 * M * N * K)], 1
+
+
 def _capture(calls, first, count):
     """One HIP graph holding `count` steps (every call once per step, buffer set
     first + i for step i), captured on a side stream.  Replaying it launches the
@@ -459,7 +508,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["decode", "tiny", "prefill", "msd", "moe", "moe_chain", "msd_page",
-                                       "msd_basic", "mx_decode", "mx_prefill"], default=None,
+                                       "msd_basic", "mx_decode", "mx_prefill", "w8_decode", "w8_prefill"],
+                    default=None,
                     help="run only this workload (profiling); no JSON headline unless decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-config extras")
@@ -490,7 +540,8 @@ def main():
     builders = {"decode": decode_workload, "tiny": tiny_workload, "prefill": prefill_workload,
                 "msd": msd_workload, "moe": moe_workload, "moe_chain": moe_chain_workload,
                 "msd_page": msd_page_workload, "msd_basic": msd_basic_workload, "mx_decode": mx_decode_workload,
-                "mx_prefill": mx_prefill_workload}
+                "mx_prefill": mx_prefill_workload, "w8_decode": w8_decode_workload,
+                "w8_prefill": w8_prefill_workload}
     if args.only and args.only != "decode":
         _, out = measure(args.only, builders[args.only], args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **out}), flush=True)
@@ -507,7 +558,7 @@ def main():
     extra = {}
     if not args.no_extra and not args.only:
         for name in ("tiny", "prefill", "msd", "moe", "moe_chain", "msd_page", "msd_basic", "mx_decode",
-                     "mx_prefill"):
+                     "mx_prefill", "w8_decode", "w8_prefill"):
             print(f"[bench] {name} workload", file=sys.stderr, flush=True)
             _, extra[name] = measure(name, builders[name], max(10, args.steps // 2), args.warmup)
             torch.cuda.empty_cache()

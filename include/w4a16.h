@@ -228,6 +228,35 @@ w4a16_status w4a16_fused_moe(const void *x, const int32_t *topk_ids, const float
                              int dt, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * W8A16 ("Humming: open-source library for quantized inference", the WNA16
+ * setting of its quantization descriptor with 8-bit weights): as the W4A16
+ * GEMM with 8-bit codes,
+ *   dequant(W)[k][n] = (q[k][n] - z[k/gs][n]) * s[k/gs][n],
+ *   w[E][K][N] one byte per weight: two's complement int8 q (zero == NULL,
+ *   prepacked with is_signed = 1) or uint8 q with uint8 zero points
+ *   zero[K/gs][N] (one byte each; is_signed = 0); scale[K/gs][N] in dt.
+ * Shape, group and alignment rules as for w4a16_gemm (group_size a multiple
+ * of 128 dividing K).  M <= 16 with K <= 8192 runs a split-K kernel, larger M
+ * an LDS-staged tile kernel.
+ */
+
+/* Bytes of the prepacked 8-bit buffer: E*K*N. */
+size_t w8a16_prepacked_bytes(int64_t E, int64_t K, int64_t N);
+
+/*
+ * Offline repack of w[E][K][N] into 2048-byte tiles ordered (expert, 16-column
+ * block nb, 128-row group g): bytes 32L..32L+31 of a tile hold column
+ * 16*nb + L%16, rows 128*g + 32*(L/16) + r as byte r, the code being q + 128
+ * (is_signed = 1) or q.  Device pointers, E*K*N bytes each, no overlap.
+ */
+w4a16_status w8a16_prepack(const void *w, void *w_packed, int64_t E, int64_t K, int64_t N, int is_signed,
+                           void *stream);
+
+/* y[M][N] = x[M][K] . dequant(W) for 8-bit weights (E = 1); see above. */
+w4a16_status w8a16_gemm(const void *x, const void *w_packed, const void *scale, const void *zero, void *y,
+                        int64_t M, int64_t K, int64_t N, int64_t group_size, int dt, void *stream);
+
+/*
  * W4A8-MXFP4 ("Humming: open-source library for quantized inference", the
  * W4A8-MXFP4 path: MXFP4 weights with 8-bit activations, aimed at small-M
  * speed; the W4A8 configuration in its list of supported weight/activation

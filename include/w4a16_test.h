@@ -76,6 +76,11 @@ int w4a16_test_msd_config(int idx);
  * number of variants. */
 int w4a16_test_mx_small_config(int idx);
 
+/* Select the W8A16 small-M and tile kernel variants (-1 = automatic);
+ * returns 100 * (small variants) + (tile variants).  w4a16_test_force_variant(2)
+ * also forces W8A16 calls onto the tile kernel. */
+int w4a16_test_w8_config(int small_idx, int tile_idx);
+
 /* Select the W4A8-MXFP4 tile kernel variant (-1 = automatic); returns the
  * number of variants.  w4a16_test_force_variant(2) also forces the W4A8-MXFP4
  * calls onto the tile kernel (and then w4a8_mxfp4_workspace_bytes asks for

@@ -343,3 +343,34 @@ def make_mx(M, K, N, dtype=BF16, seed=0, scale_exp=(-9, -6), x_scale=1.0, outlie
 def mx_decode(M, seed=0, N=14336, K=4096) -> MxProblem:
     """W4A8-MXFP4 decode: the decode shape (K=4096, N=14336), x bf16 N(0,1)."""
     return make_mx(M, K, N, BF16, seed=seed, name=f"mx_decode_m{M}")
+
+
+@dataclasses.dataclass
+class W8Problem:
+    """W8A16 problem in the plain layout: 16-bit activations ``x [M][K]``, one
+    byte per weight ``w [K][N]`` (int8 when ``zero`` is None, else uint8),
+    ``scale [K/group][N]`` 16-bit patterns, ``zero [K/group][N]`` uint8."""
+    x: np.ndarray
+    w: np.ndarray
+    scale: np.ndarray
+    zero: Optional[np.ndarray]
+    M: int
+    K: int
+    N: int
+    dtype: int
+    group: int = GROUP
+    name: str = ""
+
+
+def make_w8(M, K, N, dtype=BF16, signed=True, scale_range=(1e-4, 5e-4), zero_range=(100, 156), seed=0,
+            group=GROUP, name="") -> W8Problem:
+    """x ~ N(0,1); weight bytes uniform over [0, 255] (read as int8 when signed);
+    scales uniform in ``scale_range``; zero points uniform integers in
+    ``zero_range`` (unsigned weights only)."""
+    assert K % group == 0
+    G = K // group
+    x = to_bits(_normal(stream(seed, "x"), (M, K)), dtype)
+    w = stream(seed, "w").integers(0, 256, size=(K, N), dtype=np.uint8)
+    s = _scales(seed, (G, N), scale_range[0], scale_range[1], dtype)
+    z = None if signed else stream(seed, "z").integers(zero_range[0], zero_range[1] + 1, size=(G, N)).astype(np.uint8)
+    return W8Problem(x=x, w=w, scale=s, zero=z, M=M, K=K, N=N, dtype=dtype, group=group, name=name)

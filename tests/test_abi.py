@@ -17,7 +17,7 @@ def _declared():
     for h in ("w4a16.h", "w4a16_test.h"):
         src = open(os.path.join(ROOT, "include", h)).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        names |= set(re.findall(r"\b(w4a(?:16|8)_[a-z0-9_]+)\s*\(", src))
+        names |= set(re.findall(r"\b(w[48]a(?:16|8)_[a-z0-9_]+)\s*\(", src))
     return names
 
 

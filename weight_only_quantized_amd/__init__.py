@@ -48,6 +48,9 @@ _SIGS = {
     "w4a16_fused_moe_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64], C.c_size_t),
     "w4a16_fused_moe": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, C.c_int,
                          _p, C.c_size_t, _p], C.c_int),
+    "w8a16_prepacked_bytes": ([_i64, _i64, _i64], C.c_size_t),
+    "w8a16_prepack": ([_p, _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
+    "w8a16_gemm": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p], C.c_int),
     "w4a8_mxfp4_prepacked_bytes": ([_i64, _i64, _i64], C.c_size_t),
     "w4a8_mxfp4_prepack": ([_p, _p, _p, _i64, _i64, _i64, _p], C.c_int),
     "w4a8_mxfp8_quantize": ([_p, _p, _p, _i64, _i64, C.c_int, _p], C.c_int),
@@ -65,6 +68,7 @@ _SIGS = {
     "w4a16_test_msd_config": ([C.c_int], C.c_int),
     "w4a16_test_mx_small_config": ([C.c_int], C.c_int),
     "w4a16_test_mx_tile_config": ([C.c_int], C.c_int),
+    "w4a16_test_w8_config": ([C.c_int, C.c_int], C.c_int),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -172,6 +176,19 @@ def w4a16_fused_moe(x, topk_ids, topk_w, w13_packed, s13, z13, w2_packed, s2, z2
            "w4a16_fused_moe")
 
 
+def w8a16_prepacked_bytes(E: int, K: int, N: int) -> int:
+    return lib().w8a16_prepacked_bytes(E, K, N)
+
+
+def w8a16_prepack(w, w_packed, E, K, N, is_signed, stream=None):
+    _check(lib().w8a16_prepack(_ptr(w), _ptr(w_packed), E, K, N, int(is_signed), _stream(stream)), "w8a16_prepack")
+
+
+def w8a16_gemm(x, w_packed, scale, zero, y, M, K, N, group_size=GROUP_SIZE, dt=W4A16_BF16, stream=None):
+    _check(lib().w8a16_gemm(_ptr(x), _ptr(w_packed), _ptr(scale), _ptr(zero), _ptr(y), M, K, N, group_size,
+                            int(dt), _stream(stream)), "w8a16_gemm")
+
+
 def w4a8_mxfp4_prepacked_bytes(E: int, K: int, N: int) -> int:
     return lib().w4a8_mxfp4_prepacked_bytes(E, K, N)
 
@@ -251,3 +268,7 @@ def w4a16_test_mx_small_config(idx: int) -> int:
 
 def w4a16_test_mx_tile_config(idx: int) -> int:
     return lib().w4a16_test_mx_tile_config(int(idx))
+
+
+def w4a16_test_w8_config(small_idx: int, tile_idx: int) -> int:
+    return lib().w4a16_test_w8_config(int(small_idx), int(tile_idx))

@@ -364,6 +364,47 @@ int w4a16_test_mx_small_config(int idx) {
     return w4::mx_small_config_count();
 }
 
+int w4a16_test_w8_config(int small_idx, int tile_idx) {
+    w4::set_w8_small_config(small_idx);
+    w4::set_w8_tile_config(tile_idx);
+    return w4::w8_small_config_count() * 100 + w4::w8_tile_config_count();
+}
+
+// ---- W8A16 ------------------------------------------------------------------
+
+size_t w8a16_prepacked_bytes(int64_t E, int64_t K, int64_t N) {
+    if (E < 1 || K <= 0 || N <= 0) return 0;
+    return w4::w8_prepacked_bytes(E, K, N);
+}
+
+w4a16_status w8a16_prepack(const void *w, void *w_packed, int64_t E, int64_t K, int64_t N, int is_signed,
+                           void *stream) {
+    if (E < 1) return W4A16_ERR_SHAPE;
+    w4a16_status st = check_kn(K, N, 128);
+    if (st != W4A16_OK) return st;
+    if (!w || !w_packed) return W4A16_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(w_packed, 16)) return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_w8_prepack(w, w_packed, E, K, N, is_signed ? 1 : 0, (hipStream_t)stream));
+}
+
+w4a16_status w8a16_gemm(const void *x, const void *w_packed, const void *scale, const void *zero, void *y,
+                        int64_t M, int64_t K, int64_t N, int64_t group_size, int dt, void *stream) {
+    if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
+    int gm = 1;
+    w4a16_status st = check_kn_groups(K, N, group_size, &gm);
+    if (st != W4A16_OK) return st;
+    if (M < 0 || M > (int64_t(1) << 31) - 1) return W4A16_ERR_SHAPE;
+    if (M == 0) return W4A16_OK;
+    if (!x || !w_packed || !scale || !y) return W4A16_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(scale, 2) || !aligned(y, 2))
+        return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    const int forced = g_force_variant.load(std::memory_order_relaxed);
+    const bool small = forced != 2 && M <= 16 && K <= w4::w8_small_max_k();
+    return map_err(w4::launch_w8_gemm(x, w_packed, scale, zero, y, M, K, N, dt, gm, small, (hipStream_t)stream));
+}
+
 int w4a16_test_mx_tile_config(int idx) {
     w4::set_mx_tile_config(idx);
     return w4::mx_tile_config_count();

@@ -93,4 +93,17 @@ void set_mx_tile_config(int idx);
 hipError_t launch_mx_gemm_tile(const void *qx, const void *sx, const void *wp, void *y, int64_t M, int64_t K,
                                int64_t N, int dt, hipStream_t stream);
 
+// W8A16: 8-bit weight prepack (2048-byte tiles) and the dense GEMM (small:
+// split-K kernel for M <= 16 and K <= w8_small_max_k(); else the tile kernel).
+size_t w8_prepacked_bytes(int64_t E, int64_t K, int64_t N);
+hipError_t launch_w8_prepack(const void *w, void *out, int64_t E, int64_t K, int64_t N, int is_signed,
+                             hipStream_t stream);
+int64_t w8_small_max_k();
+int w8_small_config_count();
+void set_w8_small_config(int idx);
+int w8_tile_config_count();
+void set_w8_tile_config(int idx);
+hipError_t launch_w8_gemm(const void *x, const void *wp, const void *scale, const void *zero, void *y, int64_t M,
+                          int64_t K, int64_t N, int dt, int gm, bool small, hipStream_t stream);
+
 }  // namespace w4

@@ -484,7 +484,7 @@ static hipError_t w8_small_dispatch(const void *x, const void *wp, const void *s
                                     int64_t M, int64_t K, int64_t N, int gm, hipStream_t stream) {
     const int64_t G = K / kGroup;
     int idx = g_w8_small_cfg;
-    if (idx < 0 || idx >= w8_small_config_count()) idx = M > 4 ? 1 : 0;
+    if (idx < 0 || idx >= w8_small_config_count()) idx = 0;
     W8SmallCfg c = kW8SmallCfgs[idx];
     while ((G + c.sg - 1) / c.sg > kW8SmallMaxWaves && c.sg < 4) c.sg *= 2;
     if ((G + c.sg - 1) / c.sg > kW8SmallMaxWaves) return hipErrorInvalidValue;
@@ -503,10 +503,11 @@ static hipError_t w8_small_dispatch(const void *x, const void *wp, const void *s
     return hipErrorInvalidValue;
 }
 
-// Tile variants (BM, BN, WM, WN).  Defaults: 64 x 256 with four 64 x 64 waves
-// for fp16, 64 x 128 with four 32 x 64... waves for bf16 (whose row-sum
-// correction needs more registers: 64 x 256 spills there), 32 x 256 for
-// M <= 64.
+// Tile variants (BM, BN, WM, WN).  Defaults: 32 x 256 with four 32 x 64 waves
+// for bf16 (the byte-to-bf16 conversion makes the kernel vector-ALU bound;
+// measured on 4096^3: 238 us against 258 us for 64 x 128; 64 x 256 spills
+// there and is not built) and for fp16 at M <= 64, 64 x 256 with four 64 x 64
+// waves for fp16 otherwise.
 struct W8TileCfg { int bm, bn, wm, wn; };
 static constexpr W8TileCfg kW8TileCfgs[] = {{64, 256, 1, 4}, {32, 256, 1, 4}, {64, 128, 2, 2}};
 static int g_w8_tile_cfg = -1;
@@ -531,7 +532,7 @@ template <int DT, bool ZERO>
 static hipError_t w8_tile_dispatch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
                                    int64_t M, int64_t K, int64_t N, int gm, hipStream_t stream) {
     int idx = g_w8_tile_cfg;
-    if (idx < 0 || idx >= w8_tile_config_count()) idx = M <= 64 ? 1 : 0;
+    if (idx < 0 || idx >= w8_tile_config_count()) idx = (DT == DT_BF16 || M <= 64) ? 1 : 0;
     if (DT == DT_BF16 && idx == 0) idx = 2;
     const W8TileCfg c = kW8TileCfgs[idx];
 #define W4_W8T(BMV, BNV, WMV, WNV)                                                              \

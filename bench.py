@@ -19,6 +19,7 @@ roofline = the dominant kernel (the small-M split-K kernel): algorithmic
 cpu_baseline = the CPU oracle on the same decode step (host cores).
 
 per_config adds the same measurement for the other workloads (tiny, prefill,
+mrange = W4A16 at M = 32..2048 on the decode weights,
 MSD, MoE grouped, and the MoE fused-experts chain: routing prep, gather, gate/up
 grouped GEMM, SiLU and multiply, down grouped GEMM, weighted sum); they are
 reported for completeness, the headline is decode.  msd_page is the MSD
@@ -133,6 +134,30 @@ def decode_workload():
             w4.w4a16_gemm(xs[M], wps[j], scs[j], zrs[j], ys[M], M, K, N, 128, synth.BF16)
         calls.append((f"decode_m{M}", launch, dense_bytes(M, K, N, True), 2 * M * N * K))
     return calls, len(wps)
+
+
+def mrange_workload():
+    """W4A16 over the middle of the M range on the decode weights (K=4096,
+    N=14336, uint4 + zero points, bf16): M in {32, 64, 128, 256, 512, 1024,
+    2048}, each with the kernel variant the dispatcher picks for it."""
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    Ms = (32, 64, 128, 256, 512, 1024, 2048)
+    p = synth.make_dense(max(Ms), 4096, 14336, synth.BF16, signed=False, scale_range=(0.002, 0.01),
+                         zero_range=(6, 9), seed=0, name="mrange")
+    K, N = p.K, p.N
+    wp = _prepack(p, _dev(p.w.reshape(-1)))
+    sc, zr = _dev(p.scale), _dev(p.zero)
+    xfull = _dev(p.x)
+    xs = {M: xfull[:M].contiguous() for M in Ms}
+    ys = {M: torch.empty((M, N), dtype=torch.int16, device="cuda:0") for M in Ms}
+    calls = []
+    for M in Ms:
+        def launch(i, M=M):
+            w4.w4a16_gemm(xs[M], wp, sc, zr, ys[M], M, K, N, 128, synth.BF16)
+        calls.append((f"mrange_m{M}", launch, dense_bytes(M, K, N, True), 2 * M * N * K))
+    return calls, 1
 
 
 def tiny_workload():
@@ -508,7 +533,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["decode", "tiny", "prefill", "msd", "moe", "moe_chain", "msd_page",
-                                       "msd_basic", "mx_decode", "mx_prefill", "w8_decode", "w8_prefill"],
+                                       "msd_basic", "mx_decode", "mx_prefill", "w8_decode", "w8_prefill", "mrange"],
                     default=None,
                     help="run only this workload (profiling); no JSON headline unless decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -541,7 +566,7 @@ def main():
                 "msd": msd_workload, "moe": moe_workload, "moe_chain": moe_chain_workload,
                 "msd_page": msd_page_workload, "msd_basic": msd_basic_workload, "mx_decode": mx_decode_workload,
                 "mx_prefill": mx_prefill_workload, "w8_decode": w8_decode_workload,
-                "w8_prefill": w8_prefill_workload}
+                "w8_prefill": w8_prefill_workload, "mrange": mrange_workload}
     if args.only and args.only != "decode":
         _, out = measure(args.only, builders[args.only], args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **out}), flush=True)
@@ -557,8 +582,8 @@ def main():
 
     extra = {}
     if not args.no_extra and not args.only:
-        for name in ("tiny", "prefill", "msd", "moe", "moe_chain", "msd_page", "msd_basic", "mx_decode",
-                     "mx_prefill", "w8_decode", "w8_prefill"):
+        for name in ("tiny", "prefill", "mrange", "msd", "moe", "moe_chain", "msd_page", "msd_basic",
+                     "mx_decode", "mx_prefill", "w8_decode", "w8_prefill"):
             print(f"[bench] {name} workload", file=sys.stderr, flush=True)
             _, extra[name] = measure(name, builders[name], max(10, args.steps // 2), args.warmup)
             torch.cuda.empty_cache()

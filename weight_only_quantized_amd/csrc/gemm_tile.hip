@@ -350,14 +350,15 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
 }
 
 // Workgroup tile configurations (BM x BN rows x columns, WM x WN waves).
-// Index 0 is the dense default: 64 x 64 wave tiles in workgroups of four
-// waves, two resident per compute unit, so that one workgroup's matrix-core
-// steps overlap the other's vector work across their separate per-group
-// barriers (measured ~5% faster on 4096^3 than one eight-wave 128 x 256
-// workgroup with the same wave tile).  The grouped default follows the
-// average row count per expert (small row tiles waste less of the matrix
-// core on experts with few rows).  The others are kept for tuning through
-// the test hook.
+// Index 0 is the dense default for large M: 64 x 64 wave tiles in workgroups
+// of four waves, two resident per compute unit, so that one workgroup's
+// matrix-core steps overlap the other's vector work across their separate
+// per-group barriers (measured ~5% faster on 4096^3 than one eight-wave
+// 128 x 256 workgroup with the same wave tile).  Smaller M takes indices 4
+// and 2 by workgroup count (see the dispatcher).  The grouped default follows
+// the average row count per expert (small row tiles waste less of the matrix
+// core on experts with few rows).  The others are kept for tuning through the
+// test hook.
 struct TileCfg { int bm, bn, wm, wn; };
 static constexpr TileCfg kTileCfgs[] = {{64, 256, 1, 4}, {64, 256, 2, 4}, {32, 256, 1, 4},
                                         {64, 128, 2, 2}, {32, 128, 1, 4}, {128, 128, 2, 2},
@@ -396,6 +397,15 @@ static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const int
             // resident workgroups per compute unit, little padding)
             const int64_t avg = M / E;          // mean rows per expert
             idx = avg <= 96 ? 4 : 0;
+        } else {
+            // M ranges by workgroup count (measured over M = 17..4096 at
+            // K = 4096, N = 4096 and 14336): while 32 x 128 tiles give at most
+            // 672 workgroups they win (up to 2x against 64 x 256, which would
+            // leave most compute units idle); then 32 x 256 while 64 x 256
+            // would give fewer than 448; 64 x 256 beyond
+            const int64_t items4 = (M + 31) / 32 * ((N + 127) / 128);
+            const int64_t items0 = (M + 63) / 64 * ((N + 255) / 256);
+            idx = items4 <= 672 ? 4 : (items0 < 448 ? 2 : 0);
         }
     }
     const TileCfg c = kTileCfgs[idx];

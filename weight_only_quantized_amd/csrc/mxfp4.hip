@@ -520,13 +520,14 @@ hipError_t launch_mx_gemm_small(const void *x, const void *qx, const void *sx, c
 }
 
 
-// Tile-kernel variants (BM, BN, WM, WN).  Defaults: index 7 (128 x 512, eight
-// 128 x 64-column waves, one workgroup per compute unit: the fewest bytes per
-// product) for N >= 2048, index 0 (128 x 256, four such waves, two workgroups
-// per compute unit) for smaller N, index 5 (32-row tiles) for M <= 64, where a
-// 128-row tile would mostly multiply padding.  Measured on 4096^3
-// (quantization included): 77 us for index 7, 81 us for index 0, 82-104 us
-// for the others.
+// Tile-kernel variants (BM, BN, WM, WN).  The default follows the workgroup
+// count (measured over M = 17..4096 at K = 4096, N = 4096 and 14336): the
+// smallest tiles that still give at most 512 workgroups, in the order 32 x 256
+// (index 5), 64 x 256 (index 4), 128 x 512 with eight 128 x 64-column waves
+// (index 7, the fewest bytes per product), else 128 x 256 with four such waves
+// (index 0).  Larger tiles at small M leave most compute units idle (M = 128,
+// N = 14336: 24.6 us for index 5 against 53.5 us for index 7); on 4096^3
+// index 7 takes 64-77 us against 68-81 us for index 0.
 struct MxTileCfg { int bm, bn, wm, wn; };
 static constexpr MxTileCfg kMxTileCfgs[] = {{128, 256, 1, 4}, {128, 256, 2, 4}, {128, 128, 2, 2}, {64, 128, 1, 2},
                                             {64, 256, 1, 4}, {32, 256, 1, 4}, {256, 256, 2, 4}, {128, 512, 1, 8}};
@@ -548,7 +549,10 @@ template <int DT>
 static hipError_t mx_tile_dispatch(const void *qx, const void *sx, const void *wp, void *y, int64_t M, int64_t K,
                                    int64_t N, hipStream_t stream) {
     int idx = g_mx_tile_cfg;
-    if (idx < 0 || idx >= mx_tile_config_count()) idx = M <= 64 ? 5 : (N >= 2048 ? 7 : 0);
+    if (idx < 0 || idx >= mx_tile_config_count()) {
+        const auto items = [&](int bm, int bn) { return (M + bm - 1) / bm * ((N + bn - 1) / bn); };
+        idx = items(32, 256) <= 512 ? 5 : items(64, 256) <= 512 ? 4 : items(128, 512) <= 512 ? 7 : 0;
+    }
     // a wave's columns must be all in or all out of N
     if (N % (kMxTileCfgs[idx].bn / kMxTileCfgs[idx].wn) != 0) idx = 0;
     const MxTileCfg c = kMxTileCfgs[idx];

@@ -32,7 +32,8 @@ W4A8-MXFP4 at the decode shape (bf16 x quantized to MXFP8 inside the GEMM,
 MXFP4 weights); its bytes: x + E2M1 codes (K*N/2) + E8M0 scales (K/32*N) + y.
 mx_prefill is W4A8-MXFP4 at M=N=K=4096 (activation quantization into a
 workspace, then the LDS-staged tile kernel); judged on flops against the
-5.0 PFLOP/s dense fp8 peak.  w8_decode / w8_prefill are W8A16 (8-bit integer
+5.0 PFLOP/s dense fp8 peak.  mx_moe is W4A8-MXFP4 at the MoE grouped shape
+(quantization of the routed rows, then the grouped tile kernel).  w8_decode / w8_prefill are W8A16 (8-bit integer
 weights) at the decode shape (uint8 with zero points) and at 4096^3 (int8);
 bytes: x + K*N weight bytes + scales (+ zero points, one byte each) + y.
 
@@ -363,6 +364,30 @@ def mx_prefill_workload():
     return [("mx_prefill", launch, mx_bytes(M, K, N), 2 * M * N * K)], 1
 
 
+def mx_moe_workload():
+    """W4A8-MXFP4 at the MoE grouped shape (64 experts, 512 tokens, top-8
+    Zipf(1.1), K=2048, N=1408, bf16 x): quantization of the 4096 routed rows
+    into a workspace, then the grouped tile kernel; one call = both launches."""
+    import numpy as np
+    import torch
+    import synth
+    import weight_only_quantized_amd as w4
+    p = synth.mx_moe()
+    wp = torch.empty(w4.w4a8_mxfp4_prepacked_bytes(p.E, p.K, p.N), dtype=torch.uint8, device="cuda:0")
+    w4.w4a8_mxfp4_prepack(_dev(p.w.reshape(-1)), _dev(p.sw.reshape(-1)), wp, p.E, p.K, p.N)
+    x = _dev(p.x)
+    off = _dev(np.ascontiguousarray(p.offsets, np.int32))
+    y = torch.empty((p.R, p.N), dtype=torch.int16, device="cuda:0")
+    nb = w4.w4a8_mxfp4_grouped_workspace_bytes(p.R, p.K)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    active = int(np.count_nonzero(np.diff(p.offsets)))
+    nbytes = p.R * p.K * 2 + active * (p.K * p.N // 2 + p.K // 32 * p.N) + p.R * p.N * 2
+
+    def launch(i):
+        w4.w4a8_mxfp4_grouped_gemm(x, off, wp, y, p.E, p.R, p.K, p.N, synth.BF16, ws, nb)
+    return [("mx_moe", launch, nbytes, 2 * p.R * p.N * p.K)], 1
+
+
 def w8_bytes(M, K, N, zero):
     """Algorithmic bytes of one W8A16 call: x + 8-bit weights + scales (+ zero
     points, one byte each) + y."""
@@ -533,7 +558,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["decode", "tiny", "prefill", "msd", "moe", "moe_chain", "msd_page",
-                                       "msd_basic", "mx_decode", "mx_prefill", "w8_decode", "w8_prefill", "mrange"],
+                                       "msd_basic", "mx_decode", "mx_prefill", "w8_decode", "w8_prefill", "mrange", "mx_moe"],
                     default=None,
                     help="run only this workload (profiling); no JSON headline unless decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -566,7 +591,8 @@ def main():
                 "msd": msd_workload, "moe": moe_workload, "moe_chain": moe_chain_workload,
                 "msd_page": msd_page_workload, "msd_basic": msd_basic_workload, "mx_decode": mx_decode_workload,
                 "mx_prefill": mx_prefill_workload, "w8_decode": w8_decode_workload,
-                "w8_prefill": w8_prefill_workload, "mrange": mrange_workload}
+                "w8_prefill": w8_prefill_workload, "mrange": mrange_workload,
+                "mx_moe": mx_moe_workload}
     if args.only and args.only != "decode":
         _, out = measure(args.only, builders[args.only], args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **out}), flush=True)
@@ -583,7 +609,7 @@ def main():
     extra = {}
     if not args.no_extra and not args.only:
         for name in ("tiny", "prefill", "mrange", "msd", "moe", "moe_chain", "msd_page", "msd_basic",
-                     "mx_decode", "mx_prefill", "w8_decode", "w8_prefill"):
+                     "mx_decode", "mx_prefill", "mx_moe", "w8_decode", "w8_prefill"):
             print(f"[bench] {name} workload", file=sys.stderr, flush=True)
             _, extra[name] = measure(name, builders[name], max(10, args.steps // 2), args.warmup)
             torch.cuda.empty_cache()

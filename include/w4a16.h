@@ -321,6 +321,25 @@ size_t w4a8_mxfp4_workspace_bytes(int64_t M, int64_t K);
 w4a16_status w4a8_mxfp4_gemm(const void *x, const void *w_packed, void *y, int64_t M, int64_t K, int64_t N,
                              int dt, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Scratch for w4a8_mxfp4_grouped_gemm: room for the MXFP8 codes and scales of
+ * all R rows. */
+size_t w4a8_mxfp4_grouped_workspace_bytes(int64_t R, int64_t K);
+
+/*
+ * Grouped (MoE) W4A8-MXFP4: rows expert_offsets[e] .. expert_offsets[e+1]-1
+ * of x are multiplied by expert e's MXFP4 weights (the Humming article runs
+ * dense and MoE layers on the same kernel components).  x [R][K] (dtype dt),
+ * rows already gathered and sorted by expert; expert_offsets DEVICE
+ * int32[E+1] as for w4a16_grouped_gemm (read on the device only); w_packed
+ * the E experts' prepacked weights; y [R][N].  The R rows are quantized to
+ * MXFP8 into the workspace (>= w4a8_mxfp4_grouped_workspace_bytes(R, K),
+ * 16-byte aligned; contents on return unspecified; calls sharing it must be
+ * ordered on one stream), then one grouped tile kernel runs.
+ */
+w4a16_status w4a8_mxfp4_grouped_gemm(const void *x, const int32_t *expert_offsets, const void *w_packed, void *y,
+                                     int64_t E, int64_t R, int64_t K, int64_t N, int dt, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

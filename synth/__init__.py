@@ -165,13 +165,9 @@ def zipf_routing(tokens, experts, topk, alpha, seed):
     return out
 
 
-def make_grouped(E, tokens, topk, K, N, dtype, alpha=1.1, signed=True,
-                 scale_range=(0.002, 0.01), seed=0, name="",
-                 counts: Optional[np.ndarray] = None, group=GROUP) -> Problem:
-    """MoE grouped problem.  Rows of ``x`` are token activations gathered and
-    sorted by (expert, token); ``offsets[e]..offsets[e+1]`` are expert e's rows.
-    If ``counts`` is given it overrides the routing draw (rows per expert)."""
-    G = K // group
+def _routed_rows(E, tokens, topk, K, dtype, alpha, seed, counts=None):
+    """Rows of token activations gathered and sorted by (expert, token) under
+    Zipf routing (or the given rows per expert); returns (offsets [E+1], x bits)."""
     if counts is None:
         route = zipf_routing(tokens, E, topk, alpha, seed)
         pairs = sorted((int(e), t) for t in range(tokens) for e in route[t])
@@ -186,7 +182,18 @@ def make_grouped(E, tokens, topk, K, N, dtype, alpha=1.1, signed=True,
     R = int(offsets[-1])
     xt = _normal(stream(seed, "tokens"), (max(tokens, 1), K))
     x = xt[tok_of_row] if R else np.zeros((0, K), np.float32)
-    xb = to_bits(x, dtype)
+    return offsets, to_bits(x, dtype)
+
+
+def make_grouped(E, tokens, topk, K, N, dtype, alpha=1.1, signed=True,
+                 scale_range=(0.002, 0.01), seed=0, name="",
+                 counts: Optional[np.ndarray] = None, group=GROUP) -> Problem:
+    """MoE grouped problem.  Rows of ``x`` are token activations gathered and
+    sorted by (expert, token); ``offsets[e]..offsets[e+1]`` are expert e's rows.
+    If ``counts`` is given it overrides the routing draw (rows per expert)."""
+    G = K // group
+    offsets, xb = _routed_rows(E, tokens, topk, K, dtype, alpha, seed, counts)
+    R = int(offsets[-1])
     q, w = _weights(seed, (E, K, N), signed)
     s = _scales(seed, (E, G, N), scale_range[0], scale_range[1], dtype)
     z = None
@@ -374,3 +381,37 @@ def make_w8(M, K, N, dtype=BF16, signed=True, scale_range=(1e-4, 5e-4), zero_ran
     s = _scales(seed, (G, N), scale_range[0], scale_range[1], dtype)
     z = None if signed else stream(seed, "z").integers(zero_range[0], zero_range[1] + 1, size=(G, N)).astype(np.uint8)
     return W8Problem(x=x, w=w, scale=s, zero=z, M=M, K=K, N=N, dtype=dtype, group=group, name=name)
+
+
+@dataclasses.dataclass
+class MxGrouped:
+    """Grouped W4A8-MXFP4 problem: routed rows ``x [R][K]`` sorted by expert,
+    ``offsets [E+1]``, E2M1 codes ``w [E][K][N/2]``, E8M0 scales
+    ``sw [E][K/32][N]``."""
+    x: np.ndarray
+    offsets: np.ndarray
+    w: np.ndarray
+    sw: np.ndarray
+    E: int
+    R: int
+    K: int
+    N: int
+    dtype: int
+    name: str = ""
+
+
+def make_mx_grouped(E, tokens, topk, K, N, dtype=BF16, alpha=1.1, seed=0, counts=None, scale_exp=(-9, -6),
+                    name="") -> MxGrouped:
+    """Routing as for the W4A16 grouped problems; weight codes uniform over the
+    16 E2M1 patterns, scale exponents uniform in ``scale_exp``."""
+    offsets, x = _routed_rows(E, tokens, topk, K, dtype, alpha, seed, counts)
+    codes = stream(seed, "w").integers(0, 16, size=(E, K, N), dtype=np.uint8)
+    sw = (127 + stream(seed, "s").integers(scale_exp[0], scale_exp[1] + 1, size=(E, K // 32, N))).astype(np.uint8)
+    return MxGrouped(x=x, offsets=offsets, w=pack_nibbles(codes), sw=sw, E=E, R=int(offsets[-1]), K=K, N=N,
+                     dtype=dtype, name=name)
+
+
+def mx_moe(seed=0) -> MxGrouped:
+    """W4A8-MXFP4 at the MoE grouped shape: 64 experts, 512 tokens, top-8
+    Zipf(1.1), K=2048, N=1408, bf16 x."""
+    return make_mx_grouped(64, 512, 8, 2048, 1408, BF16, alpha=1.1, seed=seed, name="mx_moe")

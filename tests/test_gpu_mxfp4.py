@@ -265,3 +265,77 @@ def test_decode_full_size_sampled(orc, M):
         sub = synth.MxProblem(x=p.x, w=np.ascontiguousarray(p.w[:, c0 // 2:(c0 + 256) // 2]),
                               sw=np.ascontiguousarray(p.sw[:, c0:c0 + 256]), M=M, K=p.K, N=256, dtype=p.dtype)
         _check_bound(orc, np.ascontiguousarray(got[:, c0:c0 + 256]), qx, sx, sub, f"mx_decode_m{M}_c{c0}")
+
+
+class DevMxGrouped:
+    def __init__(self, p):
+        import weight_only_quantized_amd as w4
+        from gpu_helpers import to_dev
+        self.p = p
+        self.x = to_dev(p.x) if p.R else torch.zeros((1, p.K), dtype=torch.int16, device=DEV)
+        self.off = torch.from_numpy(np.ascontiguousarray(p.offsets, np.int32)).to(DEV)
+        self.wp = torch.empty(w4.w4a8_mxfp4_prepacked_bytes(p.E, p.K, p.N), dtype=torch.uint8, device=DEV)
+        w4.w4a8_mxfp4_prepack(_u8(p.w.reshape(-1)), _u8(p.sw.reshape(-1)), self.wp, p.E, p.K, p.N)
+        self.nb = w4.w4a8_mxfp4_grouped_workspace_bytes(p.R, p.K)
+        self.ws = torch.empty(max(self.nb, 16), dtype=torch.uint8, device=DEV)
+
+    def run(self):
+        import weight_only_quantized_amd as w4
+        p = self.p
+        y = torch.full((max(p.R, 1), p.N), 0x1234, dtype=torch.int16, device=DEV)
+        w4.w4a8_mxfp4_grouped_gemm(self.x, self.off, self.wp, y, p.E, p.R, p.K, p.N, p.dtype, self.ws, self.nb)
+        return y
+
+
+def _check_grouped(orc, got, p, label, experts=None):
+    qx, sx = orc.mxfp8_quantize(p.x, p.R, p.K, p.dtype)
+    for e in (range(p.E) if experts is None else experts):
+        r0, r1 = int(p.offsets[e]), int(p.offsets[e + 1])
+        if r1 == r0:
+            continue
+        sub = synth.MxProblem(x=p.x[r0:r1], w=p.w[e], sw=p.sw[e], M=r1 - r0, K=p.K, N=p.N, dtype=p.dtype)
+        _check_bound(orc, np.ascontiguousarray(got[r0:r1]), np.ascontiguousarray(qx[r0:r1]),
+                     np.ascontiguousarray(sx[r0:r1]), sub, f"{label}_e{e}")
+
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F16])
+@pytest.mark.parametrize("E,tokens,topk,K,N,counts", [
+    (4, 40, 2, 256, 128, None),
+    (8, 100, 3, 512, 192, None),
+    (6, 0, 1, 256, 64, [0, 37, 0, 1, 130, 5]),          # experts without rows, ragged tiles
+    (3, 0, 1, 1024, 320, [300, 0, 64]),
+])
+def test_grouped(orc, dtype, E, tokens, topk, K, N, counts):
+    from gpu_helpers import to_host_u16
+    print(f"[case] mx grouped E={E} tokens={tokens} K={K} N={N} counts={counts} dtype={dtype}", flush=True)
+    p = synth.make_mx_grouped(E, tokens, topk, K, N, dtype, seed=E + K, counts=counts)
+    got = to_host_u16(DevMxGrouped(p).run())
+    _check_grouped(orc, got, p, f"mx_grouped_E{E}")
+
+
+def test_grouped_tile_configs(orc):
+    import weight_only_quantized_amd as w4
+    from gpu_helpers import to_host_u16
+    p = synth.make_mx_grouped(5, 0, 1, 512, 576, synth.BF16, seed=3, counts=[70, 0, 1, 200, 33])
+    d = DevMxGrouped(p)
+    n = w4.w4a16_test_mx_tile_config(-1)
+    try:
+        for c in range(n):
+            w4.w4a16_test_mx_tile_config(c)
+            print(f"[case] mx grouped config {c}", flush=True)
+            _check_grouped(orc, to_host_u16(d.run()), p, f"mx_grouped_cfg{c}")
+    finally:
+        w4.w4a16_test_mx_tile_config(-1)
+
+
+def test_grouped_full_size_sampled(orc):
+    """The MoE grouped shape (64 experts, 4096 routed rows, K=2048, N=1408)
+    with the launch the benchmark times; checked on the most loaded expert
+    and four others."""
+    from gpu_helpers import to_host_u16
+    print("[case] mx grouped full", flush=True)
+    p = synth.mx_moe()
+    got = to_host_u16(DevMxGrouped(p).run())
+    sizes = np.diff(p.offsets)
+    experts = sorted(set([int(np.argmax(sizes)), 1, 17, 40, 63]))
+    _check_grouped(orc, got, p, "mx_grouped_full", experts=experts)

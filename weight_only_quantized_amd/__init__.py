@@ -57,6 +57,8 @@ _SIGS = {
     "w4a8_mxfp4_gemm_prequant": ([_p, _p, _p, _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
     "w4a8_mxfp4_workspace_bytes": ([_i64, _i64], C.c_size_t),
     "w4a8_mxfp4_gemm": ([_p, _p, _p, _i64, _i64, _i64, C.c_int, _p, C.c_size_t, _p], C.c_int),
+    "w4a8_mxfp4_grouped_workspace_bytes": ([_i64, _i64], C.c_size_t),
+    "w4a8_mxfp4_grouped_gemm": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p, C.c_size_t, _p], C.c_int),
     "w4a16_test_unpack": ([_p, _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
     "w4a16_test_msd_intermediates": ([_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, C.c_size_t, _p], C.c_int),
     "w4a16_test_msd_basic_workspace_bytes": ([_i64, _i64, _i64, _i64], C.c_size_t),
@@ -215,6 +217,17 @@ def w4a8_mxfp4_workspace_bytes(M: int, K: int) -> int:
 def w4a8_mxfp4_gemm(x, w_packed, y, M, K, N, dt=W4A16_BF16, workspace=None, workspace_bytes=0, stream=None):
     _check(lib().w4a8_mxfp4_gemm(_ptr(x), _ptr(w_packed), _ptr(y), M, K, N, int(dt), _ptr(workspace),
                                  int(workspace_bytes), _stream(stream)), "w4a8_mxfp4_gemm")
+
+
+def w4a8_mxfp4_grouped_workspace_bytes(R: int, K: int) -> int:
+    return lib().w4a8_mxfp4_grouped_workspace_bytes(R, K)
+
+
+def w4a8_mxfp4_grouped_gemm(x, expert_offsets, w_packed, y, E, R, K, N, dt=W4A16_BF16, workspace=None,
+                            workspace_bytes=0, stream=None):
+    _check(lib().w4a8_mxfp4_grouped_gemm(_ptr(x), _ptr(expert_offsets), _ptr(w_packed), _ptr(y), E, R, K, N,
+                                         int(dt), _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "w4a8_mxfp4_grouped_gemm")
 
 
 # ---- test hooks (include/w4a16_test.h) ----------------------------------------

@@ -405,6 +405,34 @@ w4a16_status w8a16_gemm(const void *x, const void *w_packed, const void *scale, 
     return map_err(w4::launch_w8_gemm(x, w_packed, scale, zero, y, M, K, N, dt, gm, small, (hipStream_t)stream));
 }
 
+size_t w4a8_mxfp4_grouped_workspace_bytes(int64_t R, int64_t K) {
+    if (R <= 0 || K <= 0) return 0;
+    return mx_ws_sx_offset(R, K) + (size_t)R * (size_t)(K / 32);
+}
+
+w4a16_status w4a8_mxfp4_grouped_gemm(const void *x, const int32_t *expert_offsets, const void *w_packed, void *y,
+                                     int64_t E, int64_t R, int64_t K, int64_t N, int dt, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
+    w4a16_status st = check_mx_kn(K, N);
+    if (st != W4A16_OK) return st;
+    if (E < 1 || E > (int64_t(1) << 20) || R < 0 || R > kMxMaxM) return W4A16_ERR_SHAPE;
+    if (R == 0) return W4A16_OK;
+    if (!x || !expert_offsets || !w_packed || !y) return W4A16_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 2) || !aligned(expert_offsets, 4))
+        return W4A16_ERR_ALIGN;
+    const size_t need = w4a8_mxfp4_grouped_workspace_bytes(R, K);
+    if (!workspace || workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    const hipStream_t s = (hipStream_t)stream;
+    uint8_t *qx = (uint8_t *)workspace;
+    uint8_t *sx = qx + mx_ws_sx_offset(R, K);
+    hipError_t e = w4::launch_mx_quantize(x, qx, sx, R, K, dt, s);
+    if (e != hipSuccess) return map_err(e);
+    return map_err(w4::launch_mx_gemm_tile(qx, sx, w_packed, y, R, K, N, dt, s, expert_offsets, E));
+}
+
 int w4a16_test_mx_tile_config(int idx) {
     w4::set_mx_tile_config(idx);
     return w4::mx_tile_config_count();

@@ -87,11 +87,13 @@ void set_mx_small_config(int idx);
 int64_t mx_small_max_k();
 hipError_t launch_mx_gemm_small(const void *x, const void *qx, const void *sx, const void *wp, void *y, int64_t M,
                                 int64_t K, int64_t N, int dt, hipStream_t stream);
-// Large-M tile kernel from prequantized activations (sx 4-byte aligned).
+// Large-M tile kernel from prequantized activations (sx 4-byte aligned);
+// grouped (MoE) when offsets != nullptr (then M = R routed rows, E experts).
 int mx_tile_config_count();
 void set_mx_tile_config(int idx);
 hipError_t launch_mx_gemm_tile(const void *qx, const void *sx, const void *wp, void *y, int64_t M, int64_t K,
-                               int64_t N, int dt, hipStream_t stream);
+                               int64_t N, int dt, hipStream_t stream, const int32_t *offsets = nullptr,
+                               int64_t E = 1);
 
 // W8A16: 8-bit weight prepack (2048-byte tiles) and the dense GEMM (small:
 // split-K kernel for M <= 16 and K <= w8_small_max_k(); else the tile kernel).

@@ -257,6 +257,31 @@ w4a16_status w8a16_gemm(const void *x, const void *w_packed, const void *scale, 
                         int64_t M, int64_t K, int64_t N, int64_t group_size, int dt, void *stream);
 
 /*
+ * Weight descriptor ("Humming: open-source library for quantized inference":
+ * its standard quantization descriptor keeps apart the weight format, the
+ * scale granularity, the scales' data type, the zero points and optional
+ * secondary scales).  One entry point for the dense integer-weight GEMMs:
+ *   dequant(W)[k][n] = (q[k][n] - z[k/gs][n]) * s[k/gs][n] * t[n]
+ * with t the optional secondary scale (one fp32 value per output column,
+ * applied to the fp32 sum before the one rounding; t = 1 when absent).
+ */
+typedef struct {
+    int32_t weight_bits;         /* 4 (prepacked by w4a16_prepack) or 8 (w8a16_prepack)             */
+    int32_t reserved;            /* must be 0                                                       */
+    int64_t group_size;          /* rows per scale group: a multiple of 128 dividing K              */
+    const void *scale;           /* [K/group_size][N], dtype of x                                   */
+    const void *zero;            /* NULL (signed weights) or zero points: uint4 [K/gs][N/2] packed
+                                    like the weights (4-bit), uint8 [K/gs][N] (8-bit)               */
+    const float *channel_scale;  /* NULL or [N] fp32 secondary scale t                              */
+} w4a16_weight_desc;
+
+/* y[M][N] = x[M][K] . dequant(W) as described by *desc (device pointers
+ * inside it; channel_scale 4-byte aligned); otherwise as w4a16_gemm /
+ * w8a16_gemm.  W4A16_ERR_UNSUPPORTED for another weight_bits or reserved != 0. */
+w4a16_status w4a16_gemm_desc(const void *x, const void *w_packed, const w4a16_weight_desc *desc, void *y,
+                             int64_t M, int64_t K, int64_t N, int dt, void *stream);
+
+/*
  * W4A8-MXFP4 ("Humming: open-source library for quantized inference", the
  * W4A8-MXFP4 path: MXFP4 weights with 8-bit activations, aimed at small-M
  * speed; the W4A8 configuration in its list of supported weight/activation

@@ -109,6 +109,16 @@ def round_array(v: np.ndarray, dtype: int) -> np.ndarray:
     return out
 
 
+def channel_scaled(y64, channel_scale, dtype):
+    """Secondary (per-output-column) scale of the weight descriptor (Humming
+    article: the descriptor's optional secondary scales, read as one fp32
+    factor per column on top of the group scales): y = RNE(t[n] * y64[m][n]),
+    the product in fp64.  Returns (scaled y64, 16-bit bits)."""
+    t = np.asarray(channel_scale, dtype=np.float32).astype(np.float64)
+    v = np.asarray(y64, dtype=np.float64) * t[None, :]
+    return v, round_array(v, dtype)
+
+
 def w4a16(x, w, scale, zero, M, K, N, dtype, group=128):
     """Return (y64 [M,N] float64, y [M,N] uint16 bits)."""
     y64 = np.empty((M, N), dtype=np.float64)

@@ -105,3 +105,25 @@ def test_small_weights_match_w4a16_oracle(orc):
     y8, _ = orc.w8a16(x, q.view(np.uint8), s, None, M, K, N, dt)
     y4, _ = orc.w4a16(x, synth.pack_nibbles(q.view(np.uint8) & 0xF), s, None, M, K, N, dt)
     assert np.array_equal(y8, y4)
+
+
+def test_channel_scale_composition(orc):
+    """The secondary per-column scale: t = 1 leaves the product unchanged,
+    t = 2^k shifts every 16-bit result by k in the exponent (no overflow,
+    no subnormals here), and the result is the fp64 product rounded once."""
+    rng = np.random.default_rng(9)
+    M, K, N, dt = 3, 256, 32, synth.BF16
+    q = rng.integers(-8, 8, (K, N)).astype(np.int8)
+    x = synth.to_bits(rng.standard_normal((M, K)).astype(np.float32), dt)
+    s = synth.to_bits((0.002 + 0.01 * rng.random((K // 128, N))).astype(np.float32), dt)
+    y64, y = orc.w8a16(x, q.view(np.uint8), s, None, M, K, N, dt)
+    v1, b1 = orc.channel_scaled(y64, np.ones(N, np.float32), dt)
+    assert np.array_equal(v1, y64) and np.array_equal(b1, y)
+    k = rng.integers(-3, 4, N)
+    v2, b2 = orc.channel_scaled(y64, np.exp2(k).astype(np.float32), dt)
+    ybits = y.astype(np.int64)
+    shifted = np.where(ybits & 0x7FFF, ybits + (k[None, :] << 7), ybits)   # bf16 exponent field starts at bit 7
+    assert np.array_equal(b2.astype(np.int64), shifted)
+    t = rng.uniform(0.5, 2.0, N).astype(np.float32)
+    v3, b3 = orc.channel_scaled(y64, t, dt)
+    assert np.array_equal(b3, rne(y64 * t.astype(np.float64), dt))

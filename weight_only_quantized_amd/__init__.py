@@ -30,6 +30,13 @@ class W4A16Error(RuntimeError):
         super().__init__(f"{where}: {w4a16_status_str(status)} (status {status})")
 
 
+class WeightDesc(C.Structure):
+    """w4a16_weight_desc (include/w4a16.h): weight bits, group size, scale,
+    zero points and the optional per-column secondary scale (device pointers)."""
+    _fields_ = [("weight_bits", C.c_int32), ("reserved", C.c_int32), ("group_size", C.c_int64),
+                ("scale", C.c_void_p), ("zero", C.c_void_p), ("channel_scale", C.c_void_p)]
+
+
 _lib = None
 _p = C.c_void_p
 _i64 = C.c_int64
@@ -48,6 +55,7 @@ _SIGS = {
     "w4a16_fused_moe_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64], C.c_size_t),
     "w4a16_fused_moe": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, C.c_int,
                          _p, C.c_size_t, _p], C.c_int),
+    "w4a16_gemm_desc": ([_p, _p, C.POINTER(WeightDesc), _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
     "w8a16_prepacked_bytes": ([_i64, _i64, _i64], C.c_size_t),
     "w8a16_prepack": ([_p, _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
     "w8a16_gemm": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p], C.c_int),
@@ -176,6 +184,13 @@ def w4a16_fused_moe(x, topk_ids, topk_w, w13_packed, s13, z13, w2_packed, s2, z2
                                  _ptr(w2_packed), _ptr(s2), _ptr(z2), _ptr(out), T, topk, E, H, I, group_size,
                                  int(dt), _ptr(workspace), int(workspace_bytes), _stream(stream)),
            "w4a16_fused_moe")
+
+
+def w4a16_gemm_desc(x, w_packed, y, M, K, N, scale, zero=None, channel_scale=None, weight_bits=4,
+                    group_size=GROUP_SIZE, dt=W4A16_BF16, stream=None):
+    d = WeightDesc(int(weight_bits), 0, int(group_size), _ptr(scale), _ptr(zero), _ptr(channel_scale))
+    _check(lib().w4a16_gemm_desc(_ptr(x), _ptr(w_packed), C.byref(d), _ptr(y), M, K, N, int(dt), _stream(stream)),
+           "w4a16_gemm_desc")
 
 
 def w8a16_prepacked_bytes(E: int, K: int, N: int) -> int:

@@ -19,8 +19,10 @@ int small_config_count();
 void set_small_config(int idx);
 int64_t small_max_k();
 // gm: 128-row groups per scale group (scale and zero have K/(128*gm) rows).
+// cs: optional per-column fp32 secondary scale applied before the rounding.
 hipError_t launch_gemm_small(const void *x, const void *wp, const void *scale, const void *zero, void *y,
-                             int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream, int gm = 1);
+                             int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream, int gm = 1,
+                             const float *cs = nullptr);
 
 // LDS-staged tile kernel; grouped when offsets != nullptr (then M = R rows).
 // With row_src, row r of the product reads x row row_src[r] (gathered load).
@@ -28,7 +30,8 @@ int tile_config_count();
 void set_tile_config(int idx);
 hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *wp, const void *scale,
                             const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
-                            int dt, hipStream_t stream, const int32_t *row_src = nullptr, int gm = 1);
+                            int dt, hipStream_t stream, const int32_t *row_src = nullptr, int gm = 1,
+                            const float *cs = nullptr);
 
 // MSD: decomposition, int8 products + merge, split-K reduction.
 struct MsdPlan {
@@ -106,6 +109,7 @@ void set_w8_small_config(int idx);
 int w8_tile_config_count();
 void set_w8_tile_config(int idx);
 hipError_t launch_w8_gemm(const void *x, const void *wp, const void *scale, const void *zero, void *y, int64_t M,
-                          int64_t K, int64_t N, int dt, int gm, bool small, hipStream_t stream);
+                          int64_t K, int64_t N, int dt, int gm, bool small, hipStream_t stream,
+                          const float *cs = nullptr);
 
 }  // namespace w4

@@ -394,10 +394,11 @@ static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const int
     if (idx < 0 || idx >= tile_config_count()) {
         idx = 0;
         if (GROUPED) {
-            // few rows per expert: 32 x 128 tiles of four waves (several
-            // resident workgroups per compute unit, little padding)
+            // few rows per expert: 32-row tiles (little padding); 32 x 256
+            // measured best on the MoE shapes (fused-experts chain 173-177 us
+            // against 190-194 us with 32 x 128; grouped call about even)
             const int64_t avg = M / E;          // mean rows per expert
-            idx = avg <= 96 ? 4 : 0;
+            idx = avg <= 96 ? 2 : 0;
         } else {
             // M ranges by workgroup count (measured over M = 17..4096 at
             // K = 4096, N = 4096 and 14336): while 32 x 128 tiles give at most

@@ -117,6 +117,14 @@ void oracle_fused_moe(const uint16_t *x, const int32_t *topk_ids, const float *t
                       int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I,
                       int64_t group, int dtype, const int64_t *tok, int64_t P, uint16_t *out);
 
+/* ---- W4A16 with floating-point zero points (Humming article: the
+ * descriptor's zero points, here as values of the activation dtype):
+ * dequant(W)[k][n] = (u[k][n] - zf[k/group][n]) * s[k/group][n], u the
+ * unsigned 4-bit code, zf [K/group][N] 16-bit patterns of dtype.  fp64 sums
+ * (every term exact), y = RNE(y64). ---- */
+void oracle_w4a16_fzero(const uint16_t *x, const uint8_t *w, const uint16_t *scale, const uint16_t *zf,
+                        int64_t M, int64_t K, int64_t N, int64_t group, int dtype, double *y64, uint16_t *y);
+
 /* ---- W8A16 (Humming article: the WNA16 setting with N = 8, i.e. 8-bit integer
  * weights with 16-bit activations, group scales and optional zero points).
  * w[K][N] one byte per weight: two's complement int8 when zero == NULL, else

@@ -127,3 +127,39 @@ def test_channel_scale_composition(orc):
     t = rng.uniform(0.5, 2.0, N).astype(np.float32)
     v3, b3 = orc.channel_scaled(y64, t, dt)
     assert np.array_equal(b3, rne(y64 * t.astype(np.float64), dt))
+
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F16])
+def test_float_zero_points(orc, dtype):
+    """W4A16 with floating-point zero points: integer-valued zero points give
+    the integer-zero-point oracle's result; zero points 0 with integer x and
+    unit scales give numpy's int64 matmul of the unsigned codes; raising one
+    group's zero points by d moves the result by exactly -d * s * (row sum of
+    x over that group)."""
+    rng = np.random.default_rng(12)
+    M, K, N, group = 4, 512, 32, 256
+    G = K // group
+    u = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    w = synth.pack_nibbles(u)
+    x = synth.to_bits(rng.standard_normal((M, K)).astype(np.float32), dtype)
+    s = synth.to_bits((0.002 + 0.01 * rng.random((G, N))).astype(np.float32), dtype)
+    zi = rng.integers(0, 16, (G, N)).astype(np.uint8)
+    y_int, _ = orc.w4a16(x, w, s, synth.pack_nibbles(zi), M, K, N, dtype, group=group)
+    y_f, _ = orc.w4a16_fzero(x, w, s, synth.to_bits(zi.astype(np.float32), dtype), M, K, N, dtype, group=group)
+    assert np.array_equal(y_int, y_f)
+    xi = rng.integers(-3, 4, (M, K)).astype(np.float32)
+    ones = synth.to_bits(np.ones((G, N), np.float32), dtype)
+    zeros = synth.to_bits(np.zeros((G, N), np.float32), dtype)
+    y0, _ = orc.w4a16_fzero(synth.to_bits(xi, dtype), w, ones, zeros, M, K, N, dtype, group=group)
+    assert np.array_equal(y0, (xi.astype(np.int64) @ u.astype(np.int64)).astype(np.float64))
+    zf = (rng.random((G, N)) * 15).astype(np.float32)
+    zb = synth.to_bits(zf, dtype)
+    base, _ = orc.w4a16_fzero(x, w, s, zb, M, K, N, dtype, group=group)
+    zb2 = zb.copy()
+    zb2[1] = synth.to_bits(synth.bits_to_f32(zb[1], dtype) + np.float32(0.5), dtype)
+    y2, _ = orc.w4a16_fzero(x, w, s, zb2, M, K, N, dtype, group=group)
+    d = synth.bits_to_f32(zb2[1], dtype).astype(np.float64) - synth.bits_to_f32(zb[1], dtype).astype(np.float64)
+    xv = synth.bits_to_f32(x, dtype).astype(np.float64)
+    S1 = xv[:, group:2 * group].sum(axis=1)
+    sv = synth.bits_to_f32(s[1], dtype).astype(np.float64)
+    assert np.allclose(y2 - base, -S1[:, None] * (d * sv)[None, :], rtol=1e-9, atol=1e-12)

@@ -263,23 +263,39 @@ w4a16_status w8a16_gemm(const void *x, const void *w_packed, const void *scale, 
  * secondary scales).  One entry point for the dense integer-weight GEMMs:
  *   dequant(W)[k][n] = (q[k][n] - z[k/gs][n]) * s[k/gs][n] * t[n]
  * with t the optional secondary scale (one fp32 value per output column,
- * applied to the fp32 sum before the one rounding; t = 1 when absent).
+ * applied to the fp32 sum before the one rounding; t = 1 when absent) and z
+ * integer codes or floating-point values (zero_format).
  */
 typedef struct {
     int32_t weight_bits;         /* 4 (prepacked by w4a16_prepack) or 8 (w8a16_prepack)             */
-    int32_t reserved;            /* must be 0                                                       */
+    int32_t zero_format;         /* 0: integer zero points (or none); 1: floating-point zero points */
     int64_t group_size;          /* rows per scale group: a multiple of 128 dividing K              */
     const void *scale;           /* [K/group_size][N], dtype of x                                   */
-    const void *zero;            /* NULL (signed weights) or zero points: uint4 [K/gs][N/2] packed
-                                    like the weights (4-bit), uint8 [K/gs][N] (8-bit)               */
+    const void *zero;            /* zero_format 0: NULL (signed weights) or uint4 [K/gs][N/2] packed
+                                    like the weights (4-bit) / uint8 [K/gs][N] (8-bit);
+                                    zero_format 1: [K/gs][N] values of the dtype of x, with the
+                                    weights unsigned codes (prepacked with is_signed = 0)           */
     const float *channel_scale;  /* NULL or [N] fp32 secondary scale t                              */
 } w4a16_weight_desc;
 
+/* Scratch for w4a16_gemm_desc: 0 unless zero_format == 1 (then fp32 row sums
+ * per scale group and an fp32 [M][N] correction). */
+size_t w4a16_gemm_desc_workspace_bytes(const w4a16_weight_desc *desc, int64_t M, int64_t K, int64_t N);
+
 /* y[M][N] = x[M][K] . dequant(W) as described by *desc (device pointers
  * inside it; channel_scale 4-byte aligned); otherwise as w4a16_gemm /
- * w8a16_gemm.  W4A16_ERR_UNSUPPORTED for another weight_bits or reserved != 0. */
+ * w8a16_gemm.  Floating-point zero points: the signed path multiplies the
+ * codes as u - 8 (4-bit) or u - 128 (8-bit), a correction kernel forms
+ * sum_g S[m][g] * (z[g][n] - 8 or 128) * s[g][n] into the workspace (S: row
+ * sums of x per scale group), and the GEMM epilogue subtracts it before the
+ * secondary scale and the rounding; requires K/group_size <= 8192 and
+ * M <= 1048560.  workspace: >= w4a16_gemm_desc_workspace_bytes() bytes,
+ * 16-byte aligned (may be NULL when that is 0); calls sharing it must be
+ * ordered on one stream.  W4A16_ERR_UNSUPPORTED for another weight_bits or
+ * zero_format. */
 w4a16_status w4a16_gemm_desc(const void *x, const void *w_packed, const w4a16_weight_desc *desc, void *y,
-                             int64_t M, int64_t K, int64_t N, int dt, void *stream);
+                             int64_t M, int64_t K, int64_t N, int dt, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /*
  * W4A8-MXFP4 ("Humming: open-source library for quantized inference", the

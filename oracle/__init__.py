@@ -68,6 +68,7 @@ def lib():
                                   C.c_int, _p, _i64, _p], None),
             "oracle_w8a16": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p, _p], None),
             "oracle_w4a16_fzero": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p, _p], None),
+            "oracle_w8a16_fzero": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p, _p], None),
             "oracle_e4m3_to_double": ([C.c_uint8], C.c_double),
             "oracle_e2m1_to_double": ([C.c_uint8], C.c_double),
             "oracle_e8m0_to_double": ([C.c_uint8], C.c_double),
@@ -239,6 +240,17 @@ def w4a16_fzero(x, w, scale, zf, M, K, N, dtype, group=128):
     xc, wc, sc, zc = (np.ascontiguousarray(x, np.uint16), np.ascontiguousarray(w, np.uint8),
                       np.ascontiguousarray(scale, np.uint16), np.ascontiguousarray(zf, np.uint16))
     lib().oracle_w4a16_fzero(_ptr(xc), _ptr(wc), _ptr(sc), _ptr(zc), M, K, N, group, dtype, _ptr(y64), _ptr(y))
+    return y64, y
+
+
+def w8a16_fzero(x, w, scale, zf, M, K, N, dtype, group=128):
+    """W8A16 with floating-point zero points: w [K][N] uint8 codes, zf
+    [K/group][N] 16-bit patterns of dtype; returns (y64, y bits)."""
+    y64 = np.empty((M, N), dtype=np.float64)
+    y = np.empty((M, N), dtype=np.uint16)
+    xc, wc, sc, zc = (np.ascontiguousarray(x, np.uint16), np.ascontiguousarray(w, np.uint8),
+                      np.ascontiguousarray(scale, np.uint16), np.ascontiguousarray(zf, np.uint16))
+    lib().oracle_w8a16_fzero(_ptr(xc), _ptr(wc), _ptr(sc), _ptr(zc), M, K, N, group, dtype, _ptr(y64), _ptr(y))
     return y64, y
 
 

@@ -634,3 +634,31 @@ void oracle_w4a16_fzero(const uint16_t *x, const uint8_t *w, const uint16_t *sca
     if (!y64) free(acc);
     free(wd);
 }
+
+void oracle_w8a16_fzero(const uint16_t *x, const uint8_t *w, const uint16_t *scale, const uint16_t *zf,
+                        int64_t M, int64_t K, int64_t N, int64_t group, int dtype, double *y64, uint16_t *y) {
+    if (M <= 0) return;
+    double *wd = (double *)malloc(sizeof(double) * (size_t)K * (size_t)N);
+    assert(wd);
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            const int64_t g = k / group;
+            wd[k * N + n] = ((double)w[k * N + n] - to_double(zf[g * N + n], dtype)) * to_double(scale[g * N + n], dtype);
+        }
+    double *acc = y64 ? y64 : (double *)malloc(sizeof(double) * (size_t)M * (size_t)N);
+    assert(acc);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        double *row = acc + m * N;
+        for (int64_t n = 0; n < N; ++n) row[n] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double xv = to_double(x[m * K + k], dtype);
+            const double *wr = wd + k * N;
+            for (int64_t n = 0; n < N; ++n) row[n] += xv * wr[n];
+        }
+    }
+    if (y) oracle_round_array(acc, y, M * N, dtype);
+    if (!y64) free(acc);
+    free(wd);
+}

@@ -132,6 +132,10 @@ void oracle_w4a16_fzero(const uint16_t *x, const uint8_t *w, const uint16_t *sca
  * y64 = x . ((q - z) * s) in fp64 (every product exact), y = RNE(y64). ---- */
 void oracle_w8a16(const uint16_t *x, const uint8_t *w, const uint16_t *scale, const uint8_t *zero,
                   int64_t M, int64_t K, int64_t N, int64_t group, int dtype, double *y64, uint16_t *y);
+/* W8A16 with floating-point zero points: (u - zf[k/group][n]) * s, u uint8,
+ * zf 16-bit patterns of dtype. */
+void oracle_w8a16_fzero(const uint16_t *x, const uint8_t *w, const uint16_t *scale, const uint16_t *zf,
+                        int64_t M, int64_t K, int64_t N, int64_t group, int dtype, double *y64, uint16_t *y);
 
 /* ---- W4A8-MXFP4 (Humming article: W4A8-MXFP4 path; formats per the OCP
  * Microscaling (MX) specification v1.0: blocks of 32 elements along K sharing

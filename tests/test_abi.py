@@ -214,3 +214,21 @@ def test_mxfp4_sizes_and_validation():
     for i, (call, st) in enumerate(cases):
         assert call() == st, i
     assert L.w4a8_mxfp4_gemm(F, F, F, 0, 128, 64, 1, None, 0, None) == 0              # M == 0: no-op
+
+
+def test_weight_desc_validation():
+    import ctypes as C
+    L = w4.lib()
+    F = 1 << 40
+    d = w4.WeightDesc(5, 0, 128, F, None, None)
+    assert L.w4a16_gemm_desc(F, F, C.byref(d), F, 1, 128, 64, 1, None, 0, None) == 3     # weight_bits
+    d = w4.WeightDesc(4, 2, 128, F, None, None)
+    assert L.w4a16_gemm_desc(F, F, C.byref(d), F, 1, 128, 64, 1, None, 0, None) == 3     # zero_format
+    d = w4.WeightDesc(8, 0, 128, F, None, F + 2)
+    assert L.w4a16_gemm_desc(F, F, C.byref(d), F, 1, 128, 64, 1, None, 0, None) == 4     # channel_scale alignment
+    assert L.w4a16_gemm_desc(F, F, None, F, 1, 128, 64, 1, None, 0, None) == 1
+    d = w4.WeightDesc(4, 1, 128, F, None, None)
+    assert L.w4a16_gemm_desc(F, F, C.byref(d), F, 1, 128, 64, 1, None, 0, None) == 1     # float zeros need zero
+    d = w4.WeightDesc(4, 1, 128, F, F, None)
+    assert L.w4a16_gemm_desc(F, F, C.byref(d), F, 1, 128, 64, 1, None, 0, None) == 5     # and a workspace
+    assert L.w4a16_gemm_desc_workspace_bytes(C.byref(d), 3, 256, 64) >= 3 * 64 * 4

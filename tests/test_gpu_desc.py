@@ -60,15 +60,39 @@ def test_gemm_desc(orc, bits, signed, M, dtype):
     assert torch.equal(y1, y2)
 
 
-def test_desc_validation():
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M", [1, 16, 100])
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F16])
+@pytest.mark.parametrize("with_t", [False, True])
+def test_float_zero_points(orc, bits, M, dtype, with_t):
+    """Floating-point zero points (values of the activation dtype, arbitrary
+    fractions) through the descriptor, with and without a secondary scale."""
     import weight_only_quantized_amd as w4
-    import ctypes as C
-    L = w4.lib()
-    F = 1 << 40
-    d = w4.WeightDesc(5, 0, 128, F, None, None)
-    assert L.w4a16_gemm_desc(F, F, C.byref(d), F, 1, 128, 64, 1, None) == 3     # weight_bits
-    d = w4.WeightDesc(4, 1, 128, F, None, None)
-    assert L.w4a16_gemm_desc(F, F, C.byref(d), F, 1, 128, 64, 1, None) == 3     # reserved
-    d = w4.WeightDesc(8, 0, 128, F, None, F + 2)
-    assert L.w4a16_gemm_desc(F, F, C.byref(d), F, 1, 128, 64, 1, None) == 4     # channel_scale alignment
-    assert L.w4a16_gemm_desc(F, F, None, F, 1, 128, 64, 1, None) == 1
+    from gpu_helpers import check_tol, to_dev, to_host_u16
+    K, N, group = 1024, 320, 256
+    G = K // group
+    rng = np.random.default_rng(M * 10 + bits + int(with_t))
+    print(f"[case] float zero bits={bits} M={M} dtype={dtype} t={with_t}", flush=True)
+    top = 15.0 if bits == 4 else 255.0
+    zf = synth.to_bits((rng.random((G, N)) * top).astype(np.float32), dtype)
+    if bits == 4:
+        p = synth.make_dense(M, K, N, dtype, signed=False, seed=M + 3, group=group)
+        wp = torch.empty(w4.w4a16_prepacked_bytes(1, K, N), dtype=torch.uint8, device=DEV)
+        w4.w4a16_prepack(to_dev(p.w.reshape(-1)), wp, 1, K, N, 0)
+        y64, _ = orc.w4a16_fzero(p.x, p.w, p.scale, zf, M, K, N, dtype, group=group)
+    else:
+        p = synth.make_w8(M, K, N, dtype, signed=False, seed=M + 3, group=group)
+        wp = torch.empty(w4.w8a16_prepacked_bytes(1, K, N), dtype=torch.uint8, device=DEV)
+        w4.w8a16_prepack(_u8(p.w), wp, 1, K, N, 0)
+        y64, _ = orc.w8a16_fzero(p.x, p.w, p.scale, zf, M, K, N, dtype, group=group)
+    t = rng.uniform(0.25, 4.0, N).astype(np.float32) if with_t else np.ones(N, np.float32)
+    ts = torch.from_numpy(t).to(DEV) if with_t else None
+    x, sc, zd = to_dev(p.x), to_dev(p.scale), to_dev(zf)
+    d = w4.weight_desc(sc, zd, ts, bits, group, zero_format=1)
+    nb = w4.w4a16_gemm_desc_workspace_bytes(d, M, K, N)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    w4.w4a16_gemm_desc(x, wp, y, M, K, N, sc, zd, ts, weight_bits=bits, group_size=group, dt=dtype, zero_format=1,
+                       workspace=ws, workspace_bytes=nb)
+    _, ref = orc.channel_scaled(y64, t, dtype)
+    check_tol(to_host_u16(y), ref, dtype, label=f"fzero_b{bits}_m{M}_t{int(with_t)}")

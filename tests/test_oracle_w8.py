@@ -163,3 +163,21 @@ def test_float_zero_points(orc, dtype):
     S1 = xv[:, group:2 * group].sum(axis=1)
     sv = synth.bits_to_f32(s[1], dtype).astype(np.float64)
     assert np.allclose(y2 - base, -S1[:, None] * (d * sv)[None, :], rtol=1e-9, atol=1e-12)
+
+
+def test_w8_float_zero_points(orc):
+    """8-bit codes with floating-point zero points: integer-valued zero points
+    reproduce the uint8-zero-point oracle; a half-unit shift of one group's
+    zero points moves the result by -0.5 * s * (that group's row sum of x)."""
+    rng = np.random.default_rng(13)
+    M, K, N, dt = 3, 256, 32, synth.F16
+    x, w, s, z = _problem(rng, M, K, N, dt, False)
+    y_int, _ = orc.w8a16(x, w, s, z, M, K, N, dt)
+    y_f, _ = orc.w8a16_fzero(x, w, s, synth.to_bits(z.astype(np.float32), dt), M, K, N, dt)
+    assert np.array_equal(y_int, y_f)
+    zf = z.astype(np.float32)
+    zf[0] += 0.5
+    y_h, _ = orc.w8a16_fzero(x, w, s, synth.to_bits(zf, dt), M, K, N, dt)
+    S0 = synth.bits_to_f32(x, dt).astype(np.float64)[:, :128].sum(axis=1)
+    sv = synth.bits_to_f32(s[0], dt).astype(np.float64)
+    assert np.allclose(y_h - y_f, -0.5 * S0[:, None] * sv[None, :], rtol=1e-9, atol=1e-12)

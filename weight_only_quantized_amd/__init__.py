@@ -33,7 +33,7 @@ class W4A16Error(RuntimeError):
 class WeightDesc(C.Structure):
     """w4a16_weight_desc (include/w4a16.h): weight bits, group size, scale,
     zero points and the optional per-column secondary scale (device pointers)."""
-    _fields_ = [("weight_bits", C.c_int32), ("reserved", C.c_int32), ("group_size", C.c_int64),
+    _fields_ = [("weight_bits", C.c_int32), ("zero_format", C.c_int32), ("group_size", C.c_int64),
                 ("scale", C.c_void_p), ("zero", C.c_void_p), ("channel_scale", C.c_void_p)]
 
 
@@ -55,7 +55,9 @@ _SIGS = {
     "w4a16_fused_moe_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64], C.c_size_t),
     "w4a16_fused_moe": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, C.c_int,
                          _p, C.c_size_t, _p], C.c_int),
-    "w4a16_gemm_desc": ([_p, _p, C.POINTER(WeightDesc), _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
+    "w4a16_gemm_desc_workspace_bytes": ([C.POINTER(WeightDesc), _i64, _i64, _i64], C.c_size_t),
+    "w4a16_gemm_desc": ([_p, _p, C.POINTER(WeightDesc), _p, _i64, _i64, _i64, C.c_int, _p, C.c_size_t, _p],
+                        C.c_int),
     "w8a16_prepacked_bytes": ([_i64, _i64, _i64], C.c_size_t),
     "w8a16_prepack": ([_p, _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
     "w8a16_gemm": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p], C.c_int),
@@ -186,11 +188,21 @@ def w4a16_fused_moe(x, topk_ids, topk_w, w13_packed, s13, z13, w2_packed, s2, z2
            "w4a16_fused_moe")
 
 
+def weight_desc(scale, zero=None, channel_scale=None, weight_bits=4, group_size=GROUP_SIZE, zero_format=0):
+    return WeightDesc(int(weight_bits), int(zero_format), int(group_size), _ptr(scale), _ptr(zero),
+                      _ptr(channel_scale))
+
+
+def w4a16_gemm_desc_workspace_bytes(desc, M, K, N) -> int:
+    return lib().w4a16_gemm_desc_workspace_bytes(C.byref(desc), M, K, N)
+
+
 def w4a16_gemm_desc(x, w_packed, y, M, K, N, scale, zero=None, channel_scale=None, weight_bits=4,
-                    group_size=GROUP_SIZE, dt=W4A16_BF16, stream=None):
-    d = WeightDesc(int(weight_bits), 0, int(group_size), _ptr(scale), _ptr(zero), _ptr(channel_scale))
-    _check(lib().w4a16_gemm_desc(_ptr(x), _ptr(w_packed), C.byref(d), _ptr(y), M, K, N, int(dt), _stream(stream)),
-           "w4a16_gemm_desc")
+                    group_size=GROUP_SIZE, dt=W4A16_BF16, zero_format=0, workspace=None, workspace_bytes=0,
+                    stream=None):
+    d = weight_desc(scale, zero, channel_scale, weight_bits, group_size, zero_format)
+    _check(lib().w4a16_gemm_desc(_ptr(x), _ptr(w_packed), C.byref(d), _ptr(y), M, K, N, int(dt), _ptr(workspace),
+                                 int(workspace_bytes), _stream(stream)), "w4a16_gemm_desc")
 
 
 def w8a16_prepacked_bytes(E: int, K: int, N: int) -> int:

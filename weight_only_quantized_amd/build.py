@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libw4a16.so")
 
-HIP_SOURCES = ["prepack.hip", "gemm_small.hip", "gemm_tile.hip", "msd.hip", "moe.hip", "mxfp4.hip", "w8.hip"]
+HIP_SOURCES = ["prepack.hip", "gemm_small.hip", "gemm_tile.hip", "msd.hip", "moe.hip", "mxfp4.hip", "w8.hip", "fzero.hip"]
 CPP_SOURCES = ["api.cpp"]
 ARCH = "gfx950"
 

@@ -433,32 +433,56 @@ w4a16_status w4a8_mxfp4_grouped_gemm(const void *x, const int32_t *expert_offset
     return map_err(w4::launch_mx_gemm_tile(qx, sx, w_packed, y, R, K, N, dt, s, expert_offsets, E));
 }
 
+size_t w4a16_gemm_desc_workspace_bytes(const w4a16_weight_desc *desc, int64_t M, int64_t K, int64_t N) {
+    if (!desc || desc->zero_format != 1 || M <= 0 || K <= 0 || N <= 0 || desc->group_size < 128 ||
+        K % desc->group_size != 0)
+        return 0;
+    return w4::fzero_workspace_bytes(M, K, N, desc->group_size);
+}
+
 w4a16_status w4a16_gemm_desc(const void *x, const void *w_packed, const w4a16_weight_desc *desc, void *y,
-                             int64_t M, int64_t K, int64_t N, int dt, void *stream) {
+                             int64_t M, int64_t K, int64_t N, int dt, void *workspace, size_t workspace_bytes,
+                             void *stream) {
     if (!desc) return W4A16_ERR_NULL;
-    if ((desc->weight_bits != 4 && desc->weight_bits != 8) || desc->reserved != 0) return W4A16_ERR_UNSUPPORTED;
+    if ((desc->weight_bits != 4 && desc->weight_bits != 8) || (desc->zero_format != 0 && desc->zero_format != 1))
+        return W4A16_ERR_UNSUPPORTED;
     if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
     int gm = 1;
     w4a16_status st = check_kn_groups(K, N, desc->group_size, &gm);
     if (st != W4A16_OK) return st;
     if (M < 0 || M > (int64_t(1) << 31) - 1) return W4A16_ERR_SHAPE;
     if (M == 0) return W4A16_OK;
-    if (!x || !w_packed || !desc->scale || !y) return W4A16_ERR_NULL;
+    const bool fz = desc->zero_format == 1;
+    if (!x || !w_packed || !desc->scale || !y || (fz && !desc->zero)) return W4A16_ERR_NULL;
     if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(desc->scale, 2) || !aligned(y, 2) ||
-        !aligned(desc->channel_scale, 4))
+        !aligned(desc->channel_scale, 4) || (fz && !aligned(desc->zero, 2)))
         return W4A16_ERR_ALIGN;
+    if (fz) {
+        if (K / desc->group_size > 8192 || M > 65535 * 16) return W4A16_ERR_SHAPE;
+        if (!workspace || workspace_bytes < w4a16_gemm_desc_workspace_bytes(desc, M, K, N))
+            return W4A16_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return W4A16_ERR_ALIGN;
+    }
     if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
     const hipStream_t s = (hipStream_t)stream;
     const float *cs = desc->channel_scale;
+    // floating-point zero points: the signed path (zero NULL) plus the correction
+    const void *zero = fz ? nullptr : desc->zero;
+    float *cz = nullptr;
+    if (fz) {
+        hipError_t e = w4::launch_fzero_corr(x, desc->scale, desc->zero, M, K, N, desc->group_size,
+                                             desc->weight_bits, dt, workspace, &cz, s);
+        if (e != hipSuccess) return map_err(e);
+    }
     if (desc->weight_bits == 8) {
         const int forced = g_force_variant.load(std::memory_order_relaxed);
         const bool small = forced != 2 && M <= 16 && K <= w4::w8_small_max_k();
-        return map_err(w4::launch_w8_gemm(x, w_packed, desc->scale, desc->zero, y, M, K, N, dt, gm, small, s, cs));
+        return map_err(w4::launch_w8_gemm(x, w_packed, desc->scale, zero, y, M, K, N, dt, gm, small, s, cs, cz));
     }
     if (pick_variant(M, K) == 1)
-        return map_err(w4::launch_gemm_small(x, w_packed, desc->scale, desc->zero, y, M, K, N, dt, s, gm, cs));
-    return map_err(w4::launch_gemm_tile(x, nullptr, w_packed, desc->scale, desc->zero, y, M, K, N, 1, dt, s, nullptr,
-                                        gm, cs));
+        return map_err(w4::launch_gemm_small(x, w_packed, desc->scale, zero, y, M, K, N, dt, s, gm, cs, cz));
+    return map_err(w4::launch_gemm_tile(x, nullptr, w_packed, desc->scale, zero, y, M, K, N, 1, dt, s, nullptr,
+                                        gm, cs, cz));
 }
 
 int w4a16_test_mx_tile_config(int idx) {

@@ -49,7 +49,8 @@ template <int DT, bool ZERO, int NB, int SG, int D>
 __global__ void __launch_bounds__(kSmallMaxWaves * 64)
 gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp,
                   const uint16_t *__restrict__ scale, const uint8_t *__restrict__ zero,
-                  uint16_t *__restrict__ y, int M, int64_t K, int64_t N, int gm, const float *__restrict__ cs) {
+                  uint16_t *__restrict__ y, int M, int64_t K, int64_t N, int gm, const float *__restrict__ cs,
+                  const float *__restrict__ cz) {
     static_assert(NB == 1 || NB == 2 || NB == 4, "one 64-lane load covers the scales of <= 4 blocks");
     constexpr int T = NB * SG;                    // tiles per wave, ordered block-major
     const int G = (int)(K / kGroup);
@@ -178,6 +179,7 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
         if (row < M) {
             float sum = 0.f;
             for (int w = 0; w < W; ++w) sum += red[w][b][row][col];
+            if (cz) sum -= cz[(int64_t)row * N + (nb0 + b) * 16 + col];   // floating-point zero points
             if (cs) sum *= cs[(nb0 + b) * 16 + col];     // secondary (per-column) scale
             y[(int64_t)row * N + (nb0 + b) * 16 + col] = f2h<DT>(sum);
         }
@@ -198,19 +200,21 @@ int64_t small_max_k() { return (int64_t)kSmallMaxWaves * 4 * kGroup; }
 
 template <int DT, bool ZERO, int NB, int SG, int D>
 static hipError_t small_launch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
-                               int64_t M, int64_t K, int64_t N, int gm, const float *cs, hipStream_t stream) {
+                               int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
+                               hipStream_t stream) {
     const int64_t G = K / kGroup;
     const int64_t waves = (G + SG - 1) / SG;
     const dim3 grid((unsigned)(N / (16 * NB)));
     hipLaunchKernelGGL((gemm_small_kernel<DT, ZERO, NB, SG, D>), grid, dim3((unsigned)(waves * 64)), 0, stream,
                        (const uint16_t *)x, (const uint8_t *)wp, (const uint16_t *)scale,
-                       (const uint8_t *)zero, (uint16_t *)y, (int)M, K, N, gm, cs);
+                       (const uint8_t *)zero, (uint16_t *)y, (int)M, K, N, gm, cs, cz);
     return hipGetLastError();
 }
 
 template <int DT, bool ZERO>
 static hipError_t small_dispatch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
-                                 int64_t M, int64_t K, int64_t N, int gm, const float *cs, hipStream_t stream) {
+                                 int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
+                                 hipStream_t stream) {
     const int64_t G = K / kGroup;
     int idx = g_small_cfg;
     if (idx < 0 || idx >= small_config_count()) idx = M > 4 ? 1 : 0;
@@ -226,7 +230,7 @@ static hipError_t small_dispatch(const void *x, const void *wp, const void *scal
     while ((N / 16) % c.nb != 0) c.nb /= 2;
 #define W4_SMALL(NBV, SGV, DV)                                                                  \
     if (c.nb == NBV && c.sg == SGV && c.d == DV)                                                \
-        return small_launch<DT, ZERO, NBV, SGV, DV>(x, wp, scale, zero, y, M, K, N, gm, cs, stream);
+        return small_launch<DT, ZERO, NBV, SGV, DV>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
     W4_SMALL(4, 2, 4) W4_SMALL(4, 2, 8) W4_SMALL(4, 2, 2) W4_SMALL(2, 4, 4) W4_SMALL(2, 2, 4)
     W4_SMALL(2, 4, 8) W4_SMALL(1, 2, 2) W4_SMALL(1, 4, 4) W4_SMALL(2, 2, 2) W4_SMALL(2, 4, 2)
     W4_SMALL(1, 4, 2) W4_SMALL(1, 2, 4) W4_SMALL(4, 1, 4) W4_SMALL(2, 1, 4) W4_SMALL(1, 1, 4)
@@ -237,12 +241,13 @@ static hipError_t small_dispatch(const void *x, const void *wp, const void *scal
 }
 
 hipError_t launch_gemm_small(const void *x, const void *wp, const void *scale, const void *zero, void *y,
-                             int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream, int gm, const float *cs) {
+                             int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream, int gm, const float *cs,
+                             const float *cz) {
     if (dt == DT_BF16)
-        return zero ? small_dispatch<DT_BF16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, stream)
-                    : small_dispatch<DT_BF16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, stream);
-    return zero ? small_dispatch<DT_F16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, stream)
-                : small_dispatch<DT_F16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, stream);
+        return zero ? small_dispatch<DT_BF16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream)
+                    : small_dispatch<DT_BF16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
+    return zero ? small_dispatch<DT_F16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream)
+                : small_dispatch<DT_F16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
 }
 
 }  // namespace w4

@@ -46,7 +46,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 2)
 gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
                  const int32_t *__restrict__ row_src, const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
                  const uint8_t *__restrict__ zero, uint16_t *__restrict__ y,
-                 int64_t M, int64_t K, int64_t N, int E, int gm, const float *__restrict__ cs) {
+                 int64_t M, int64_t K, int64_t N, int E, int gm, const float *__restrict__ cs,
+                 const float *__restrict__ cz) {
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int RT = TM / 32, CT = TN / 32;
@@ -345,7 +346,11 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = row0 + wm * TM + rt * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
-                if (row < row_end) y[row * N + col] = f2h<DT>(cs ? yacc[rt][ct][r] * t : yacc[rt][ct][r]);
+                if (row < row_end) {
+                    float v = yacc[rt][ct][r];
+                    if (cz) v -= cz[row * N + col];       // floating-point zero points
+                    y[row * N + col] = f2h<DT>(cs ? v * t : v);
+                }
             }
         }
 }
@@ -372,7 +377,7 @@ void set_tile_config(int idx) { g_tile_cfg = idx; }
 template <int DT, bool ZERO, bool GROUPED, int BM, int BN, int WM, int WN>
 static hipError_t tile_launch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
                               const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
-                              int64_t E, int gm, const float *cs, hipStream_t stream) {
+                              int64_t E, int gm, const float *cs, const float *cz, hipStream_t stream) {
     // grouped: every expert may end in a partial row tile, hence + E; the
     // items go on a 1-D grid rounded up to whole rounds over the XCDs
     const int64_t ncb = (N + BN - 1) / BN;
@@ -382,14 +387,14 @@ static hipError_t tile_launch(const void *x, const int32_t *offsets, const int32
     const dim3 grid = GROUPED ? dim3((unsigned)slots) : dim3((unsigned)mtiles, (unsigned)ncb);
     hipLaunchKernelGGL((gemm_tile_kernel<DT, ZERO, BM, BN, WM, WN, GROUPED>), grid, dim3(WM * WN * 64), 0,
                        stream, (const uint16_t *)x, offsets, row_src, (const uint8_t *)wp, (const uint16_t *)scale,
-                       (const uint8_t *)zero, (uint16_t *)y, M, K, N, (int)E, gm, cs);
+                       (const uint8_t *)zero, (uint16_t *)y, M, K, N, (int)E, gm, cs, cz);
     return hipGetLastError();
 }
 
 template <int DT, bool ZERO, bool GROUPED>
 static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
                                 const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
-                                int64_t E, int gm, const float *cs, hipStream_t stream) {
+                                int64_t E, int gm, const float *cs, const float *cz, hipStream_t stream) {
     int idx = g_tile_cfg;
     if (idx < 0 || idx >= tile_config_count()) {
         idx = 0;
@@ -414,7 +419,7 @@ static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const int
 #define W4_TILE(BMV, BNV, WMV, WNV)                                                                    \
     if (c.bm == BMV && c.bn == BNV && c.wm == WMV && c.wn == WNV)                                      \
         return tile_launch<DT, ZERO, GROUPED, BMV, BNV, WMV, WNV>(x, offsets, row_src, wp, scale, zero, y, M, K,   \
-                                                                  N, E, gm, cs, stream);
+                                                                  N, E, gm, cs, cz, stream);
     W4_TILE(128, 256, 2, 4) W4_TILE(64, 256, 2, 4) W4_TILE(32, 256, 1, 4) W4_TILE(64, 128, 2, 2)
     W4_TILE(32, 128, 1, 4) W4_TILE(128, 128, 2, 2) W4_TILE(64, 256, 1, 4) W4_TILE(64, 128, 1, 2)
 #undef W4_TILE
@@ -424,19 +429,21 @@ static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const int
 template <bool GROUPED>
 static hipError_t tile_dispatch_dt(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
                                    const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
-                                   int64_t E, int gm, int dt, const float *cs, hipStream_t stream) {
+                                   int64_t E, int gm, int dt, const float *cs, const float *cz,
+                                   hipStream_t stream) {
     if (dt == DT_BF16)
-        return zero ? tile_dispatch<DT_BF16, true, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, cs, stream)
-                    : tile_dispatch<DT_BF16, false, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, cs, stream);
-    return zero ? tile_dispatch<DT_F16, true, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, cs, stream)
-                : tile_dispatch<DT_F16, false, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, cs, stream);
+        return zero ? tile_dispatch<DT_BF16, true, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, cs, cz, stream)
+                    : tile_dispatch<DT_BF16, false, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, cs, cz, stream);
+    return zero ? tile_dispatch<DT_F16, true, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, cs, cz, stream)
+                : tile_dispatch<DT_F16, false, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, cs, cz, stream);
 }
 
 hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *wp, const void *scale,
                             const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
-                            int dt, hipStream_t stream, const int32_t *row_src, int gm, const float *cs) {
-    if (offsets) return tile_dispatch_dt<true>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, dt, cs, stream);
-    return tile_dispatch_dt<false>(x, nullptr, row_src, wp, scale, zero, y, M, K, N, 1, gm, dt, cs, stream);
+                            int dt, hipStream_t stream, const int32_t *row_src, int gm, const float *cs,
+                            const float *cz) {
+    if (offsets) return tile_dispatch_dt<true>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, dt, cs, cz, stream);
+    return tile_dispatch_dt<false>(x, nullptr, row_src, wp, scale, zero, y, M, K, N, 1, gm, dt, cs, cz, stream);
 }
 
 }  // namespace w4

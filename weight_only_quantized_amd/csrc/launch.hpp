@@ -19,10 +19,11 @@ int small_config_count();
 void set_small_config(int idx);
 int64_t small_max_k();
 // gm: 128-row groups per scale group (scale and zero have K/(128*gm) rows).
-// cs: optional per-column fp32 secondary scale applied before the rounding.
+// cs: optional per-column fp32 secondary scale applied before the rounding;
+// cz: optional fp32 [M][N] subtracted before it (floating-point zero points).
 hipError_t launch_gemm_small(const void *x, const void *wp, const void *scale, const void *zero, void *y,
                              int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream, int gm = 1,
-                             const float *cs = nullptr);
+                             const float *cs = nullptr, const float *cz = nullptr);
 
 // LDS-staged tile kernel; grouped when offsets != nullptr (then M = R rows).
 // With row_src, row r of the product reads x row row_src[r] (gathered load).
@@ -31,7 +32,7 @@ void set_tile_config(int idx);
 hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *wp, const void *scale,
                             const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
                             int dt, hipStream_t stream, const int32_t *row_src = nullptr, int gm = 1,
-                            const float *cs = nullptr);
+                            const float *cs = nullptr, const float *cz = nullptr);
 
 // MSD: decomposition, int8 products + merge, split-K reduction.
 struct MsdPlan {
@@ -110,6 +111,12 @@ int w8_tile_config_count();
 void set_w8_tile_config(int idx);
 hipError_t launch_w8_gemm(const void *x, const void *wp, const void *scale, const void *zero, void *y, int64_t M,
                           int64_t K, int64_t N, int dt, int gm, bool small, hipStream_t stream,
-                          const float *cs = nullptr);
+                          const float *cs = nullptr, const float *cz = nullptr);
+
+// Floating-point zero points: S (row sums per scale group) and the fp32
+// correction C[M][N] in the workspace; *corr receives C for the epilogue.
+size_t fzero_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t gs);
+hipError_t launch_fzero_corr(const void *x, const void *scale, const void *zf, int64_t M, int64_t K, int64_t N,
+                             int64_t gs, int bits, int dt, void *workspace, float **corr, hipStream_t stream);
 
 }  // namespace w4

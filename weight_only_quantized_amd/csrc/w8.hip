@@ -106,7 +106,7 @@ template <int DT, bool ZERO, int NB, int SG, int D>
 __global__ void __launch_bounds__(kW8SmallMaxWaves * 64)
 w8_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
                 const uint8_t *__restrict__ zero, uint16_t *__restrict__ y, int M, int64_t K, int64_t N, int gm,
-                const float *__restrict__ cs) {
+                const float *__restrict__ cs, const float *__restrict__ cz) {
     static_assert(NB == 1 || NB == 2 || NB == 4, "one 64-lane load covers the scales of <= 4 blocks");
     constexpr int T = NB * SG;
     const int G = (int)(K / kGroup);
@@ -225,6 +225,7 @@ w8_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp, 
         if (row < M) {
             float sum = 0.f;
             for (int w = 0; w < W; ++w) sum += red[w][b][row][col];
+            if (cz) sum -= cz[(int64_t)row * N + (nb0 + b) * 16 + col];   // floating-point zero points
             if (cs) sum *= cs[(nb0 + b) * 16 + col];     // secondary (per-column) scale
             y[(int64_t)row * N + (nb0 + b) * 16 + col] = f2h<DT>(sum);
         }
@@ -242,7 +243,7 @@ template <int DT, bool ZERO, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(WM * WN * 64, 2)
 w8_tile_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
                const uint8_t *__restrict__ zero, uint16_t *__restrict__ y, int64_t M, int64_t K, int64_t N, int gm,
-               const float *__restrict__ cs) {
+               const float *__restrict__ cs, const float *__restrict__ cz) {
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int RT = TM / 32, CT = TN / 32;
@@ -445,7 +446,11 @@ w8_tile_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp, c
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = row0 + wm * TM + rt * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
-                if (row < M) y[row * N + col] = f2h<DT>(cs ? yacc[rt][ct][r] * t : yacc[rt][ct][r]);
+                if (row < M) {
+                    float v = yacc[rt][ct][r];
+                    if (cz) v -= cz[row * N + col];       // floating-point zero points
+                    y[row * N + col] = f2h<DT>(cs ? v * t : v);
+                }
             }
         }
 }
@@ -474,18 +479,20 @@ void set_w8_small_config(int idx) { g_w8_small_cfg = idx; }
 
 template <int DT, bool ZERO, int NB, int SG, int D>
 static hipError_t w8_small_launch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
-                                  int64_t M, int64_t K, int64_t N, int gm, const float *cs, hipStream_t stream) {
+                                  int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
+                                  hipStream_t stream) {
     const int64_t G = K / kGroup;
     const int64_t waves = (G + SG - 1) / SG;
     hipLaunchKernelGGL((w8_small_kernel<DT, ZERO, NB, SG, D>), dim3((unsigned)(N / (16 * NB))),
                        dim3((unsigned)(waves * 64)), 0, stream, (const uint16_t *)x, (const uint8_t *)wp,
-                       (const uint16_t *)scale, (const uint8_t *)zero, (uint16_t *)y, (int)M, K, N, gm, cs);
+                       (const uint16_t *)scale, (const uint8_t *)zero, (uint16_t *)y, (int)M, K, N, gm, cs, cz);
     return hipGetLastError();
 }
 
 template <int DT, bool ZERO>
 static hipError_t w8_small_dispatch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
-                                    int64_t M, int64_t K, int64_t N, int gm, const float *cs, hipStream_t stream) {
+                                    int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
+                                    hipStream_t stream) {
     const int64_t G = K / kGroup;
     int idx = g_w8_small_cfg;
     if (idx < 0 || idx >= w8_small_config_count()) idx = 0;
@@ -499,7 +506,7 @@ static hipError_t w8_small_dispatch(const void *x, const void *wp, const void *s
     while ((N / 16) % c.nb != 0) c.nb /= 2;
 #define W4_W8S(NBV, SGV, DV)                                                                    \
     if (c.nb == NBV && c.sg == SGV && c.d == DV)                                                \
-        return w8_small_launch<DT, ZERO, NBV, SGV, DV>(x, wp, scale, zero, y, M, K, N, gm, cs, stream);
+        return w8_small_launch<DT, ZERO, NBV, SGV, DV>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
     W4_W8S(4, 2, 4) W4_W8S(4, 2, 8) W4_W8S(2, 2, 4) W4_W8S(1, 4, 4) W4_W8S(1, 2, 2) W4_W8S(2, 2, 2)
     W4_W8S(1, 4, 2) W4_W8S(4, 1, 4) W4_W8S(2, 1, 2) W4_W8S(1, 2, 4) W4_W8S(1, 1, 2) W4_W8S(2, 1, 4)
     W4_W8S(4, 1, 2) W4_W8S(2, 2, 8)
@@ -520,48 +527,51 @@ void set_w8_tile_config(int idx) { g_w8_tile_cfg = idx; }
 
 template <int DT, bool ZERO, int BM, int BN, int WM, int WN>
 static hipError_t w8_tile_launch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
-                                 int64_t M, int64_t K, int64_t N, int gm, const float *cs, hipStream_t stream) {
+                                 int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
+                                 hipStream_t stream) {
     if constexpr (DT == DT_BF16 && BM == 64 && BN == 256) {
         return hipErrorInvalidValue;             // not built: spills (see the table)
     } else {
         const dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((N + BN - 1) / BN));
         hipLaunchKernelGGL((w8_tile_kernel<DT, ZERO, BM, BN, WM, WN>), grid, dim3(WM * WN * 64), 0, stream,
                            (const uint16_t *)x, (const uint8_t *)wp, (const uint16_t *)scale, (const uint8_t *)zero,
-                           (uint16_t *)y, M, K, N, gm, cs);
+                           (uint16_t *)y, M, K, N, gm, cs, cz);
         return hipGetLastError();
     }
 }
 
 template <int DT, bool ZERO>
 static hipError_t w8_tile_dispatch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
-                                   int64_t M, int64_t K, int64_t N, int gm, const float *cs, hipStream_t stream) {
+                                   int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
+                                   hipStream_t stream) {
     int idx = g_w8_tile_cfg;
     if (idx < 0 || idx >= w8_tile_config_count()) idx = (DT == DT_BF16 || M <= 64) ? 1 : 0;
     if (DT == DT_BF16 && idx == 0) idx = 2;
     const W8TileCfg c = kW8TileCfgs[idx];
 #define W4_W8T(BMV, BNV, WMV, WNV)                                                              \
     if (c.bm == BMV && c.bn == BNV && c.wm == WMV && c.wn == WNV)                               \
-        return w8_tile_launch<DT, ZERO, BMV, BNV, WMV, WNV>(x, wp, scale, zero, y, M, K, N, gm, cs, stream);
+        return w8_tile_launch<DT, ZERO, BMV, BNV, WMV, WNV>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
     W4_W8T(64, 256, 1, 4) W4_W8T(32, 256, 1, 4) W4_W8T(64, 128, 2, 2)
 #undef W4_W8T
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_w8_gemm(const void *x, const void *wp, const void *scale, const void *zero, void *y, int64_t M,
-                          int64_t K, int64_t N, int dt, int gm, bool small, hipStream_t stream, const float *cs) {
+                          int64_t K, int64_t N, int dt, int gm, bool small, hipStream_t stream, const float *cs,
+                          const float *cz) {
     if (M == 0) return hipSuccess;
     if (small) {
         if (dt == DT_BF16)
-            return zero ? w8_small_dispatch<DT_BF16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, stream)
-                        : w8_small_dispatch<DT_BF16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, stream);
-        return zero ? w8_small_dispatch<DT_F16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, stream)
-                    : w8_small_dispatch<DT_F16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, stream);
+            return zero ? w8_small_dispatch<DT_BF16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream)
+                        : w8_small_dispatch<DT_BF16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
+        return zero ? w8_small_dispatch<DT_F16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream)
+                    : w8_small_dispatch<DT_F16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
     }
     if (dt == DT_BF16)
-        return zero ? w8_tile_dispatch<DT_BF16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, stream)
-                    : w8_tile_dispatch<DT_BF16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, stream);
-    return zero ? w8_tile_dispatch<DT_F16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, stream)
-                : w8_tile_dispatch<DT_F16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, stream);
+        return zero ? w8_tile_dispatch<DT_BF16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream)
+                    : w8_tile_dispatch<DT_BF16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
+    return zero ? w8_tile_dispatch<DT_F16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream)
+                : w8_tile_dispatch<DT_F16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
 }
 
 }  // namespace w4

@@ -514,13 +514,16 @@ static hipError_t w8_small_dispatch(const void *x, const void *wp, const void *s
     return hipErrorInvalidValue;
 }
 
-// Tile variants (BM, BN, WM, WN).  Defaults: 32 x 256 with four 32 x 64 waves
-// for bf16 (the byte-to-bf16 conversion makes the kernel vector-ALU bound;
-// measured on 4096^3: 238 us against 258 us for 64 x 128; 64 x 256 spills
-// there and is not built) and for fp16 at M <= 64, 64 x 256 with four 64 x 64
-// waves for fp16 otherwise.
+// Tile variants (BM, BN, WM, WN).  Defaults: for bf16 above M = 64, 64 x 128
+// with four 64 x 32 waves (the byte-to-bf16 conversion makes the kernel
+// vector-ALU bound, and a 64-row wave tile converts each weight once for two
+// row blocks: 4096^3 in 220-225 us against 252-254 us for 32 x 256 and
+// 272-275 us for 64 x 128 with 32-row waves; 64 x 256 and 128 x 128 spill in
+// bf16 and are not built there); 32 x 256 at M <= 64; for fp16 64 x 256 with
+// four 64 x 64 waves.
 struct W8TileCfg { int bm, bn, wm, wn; };
-static constexpr W8TileCfg kW8TileCfgs[] = {{64, 256, 1, 4}, {32, 256, 1, 4}, {64, 128, 2, 2}};
+static constexpr W8TileCfg kW8TileCfgs[] = {{64, 256, 1, 4}, {32, 256, 1, 4}, {64, 128, 2, 2}, {64, 128, 1, 4},
+                                            {128, 128, 1, 4}};
 static int g_w8_tile_cfg = -1;
 int w8_tile_config_count() { return (int)(sizeof(kW8TileCfgs) / sizeof(kW8TileCfgs[0])); }
 void set_w8_tile_config(int idx) { g_w8_tile_cfg = idx; }
@@ -529,7 +532,7 @@ template <int DT, bool ZERO, int BM, int BN, int WM, int WN>
 static hipError_t w8_tile_launch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
                                  int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
                                  hipStream_t stream) {
-    if constexpr (DT == DT_BF16 && BM == 64 && BN == 256) {
+    if constexpr (DT == DT_BF16 && ((BM == 64 && BN == 256) || (BM == 128 && BN == 128))) {
         return hipErrorInvalidValue;             // not built: spills (see the table)
     } else {
         const dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((N + BN - 1) / BN));
@@ -545,13 +548,13 @@ static hipError_t w8_tile_dispatch(const void *x, const void *wp, const void *sc
                                    int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
                                    hipStream_t stream) {
     int idx = g_w8_tile_cfg;
-    if (idx < 0 || idx >= w8_tile_config_count()) idx = (DT == DT_BF16 || M <= 64) ? 1 : 0;
-    if (DT == DT_BF16 && idx == 0) idx = 2;
+    if (idx < 0 || idx >= w8_tile_config_count()) idx = M <= 64 ? 1 : (DT == DT_BF16 ? 3 : 0);
+    if (DT == DT_BF16 && (idx == 0 || idx == 4)) idx = 3;
     const W8TileCfg c = kW8TileCfgs[idx];
 #define W4_W8T(BMV, BNV, WMV, WNV)                                                              \
     if (c.bm == BMV && c.bn == BNV && c.wm == WMV && c.wn == WNV)                               \
         return w8_tile_launch<DT, ZERO, BMV, BNV, WMV, WNV>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
-    W4_W8T(64, 256, 1, 4) W4_W8T(32, 256, 1, 4) W4_W8T(64, 128, 2, 2)
+    W4_W8T(64, 256, 1, 4) W4_W8T(32, 256, 1, 4) W4_W8T(64, 128, 2, 2) W4_W8T(64, 128, 1, 4) W4_W8T(128, 128, 1, 4)
 #undef W4_W8T
     return hipErrorInvalidValue;
 }

@@ -204,3 +204,27 @@ def test_fused_moe_full_sampled(orc):
     ref = orc.fused_moe(c, np.array(toks))
     check_tol(out[toks], ref, c.dtype, label=f"fused_moe_full tokens={toks}")
     assert np.all(np.isfinite(synth.bits_to_f32(out, c.dtype)))
+
+
+@pytest.mark.parametrize("cfg", [0, 2])
+def test_silu_epilogue_equals_separate_kernel(cfg):
+    """The gate/up projection with SiLU-and-multiply in its epilogue (tile
+    configurations 0 and 2: a gate and an up tile per wave) against the same
+    chain through the stored projection and the separate kernel
+    (configuration 4, one column tile per wave): bit for bit, since both round
+    the projection to the dtype before the same fp32 SiLU and product, and every
+    tile configuration accumulates each output in the same order."""
+    import weight_only_quantized_amd as w4
+    from gpu_helpers import to_host_u16
+    k = dict(CHAINS[4])
+    c = synth.make_moe_chain(seed=9, **k)
+    print(f"[case] silu epilogue cfg={cfg} vs separate kernel {CHAINS[4]}", flush=True)
+    d = DevChain(c)
+    try:
+        w4.w4a16_test_tile_config(cfg)
+        fused = to_host_u16(d.run())
+        w4.w4a16_test_tile_config(4)
+        separate = to_host_u16(d.run())
+    finally:
+        w4.w4a16_test_tile_config(-1)
+    assert np.array_equal(fused, separate)

@@ -41,7 +41,14 @@ constexpr int kXcds = 8;
 
 // At least two waves per SIMD: two resident workgroups of four waves (or one
 // of eight) per compute unit, each wave within 256 registers.
-template <int DT, bool ZERO, int BM, int BN, int WM, int WN, bool GROUPED>
+//
+// SILU (grouped, two 32-column tiles per wave): the weights hold 2 * NOUT
+// columns, gate then up (the fused-experts gate/up projection); a wave's two
+// tiles are gate columns c and up columns NOUT + c of the same 32 output
+// columns, and the epilogue stores a = silu(gate) * up with each input first
+// rounded to the activation dtype (as if the projection were stored and read
+// back), so the result equals that of the separate SiLU-and-multiply kernel.
+template <int DT, bool ZERO, int BM, int BN, int WM, int WN, bool GROUPED, bool SILU = false>
 __global__ void __launch_bounds__(WM * WN * 64, 2)
 gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
                  const int32_t *__restrict__ row_src, const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
@@ -57,6 +64,9 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert((BM * 16) % NT == 0, "x staging must divide evenly");
     static_assert(XP <= 16, "one row-sum split per lane");
+    static_assert(!SILU || (GROUPED && CT == 2), "SiLU epilogue: grouped, gate and up tile per wave");
+    constexpr int BNO = SILU ? BN / 2 : BN;   // output columns per workgroup
+    constexpr int TNO = SILU ? 32 : TN;       // output columns per wave
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BM * ROWB];
 
@@ -67,6 +77,7 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     const int wm = wave / WN, wn = wave % WN;
     const int G = (int)(K / kGroup);
     const int64_t NBLK = N / 16;
+    const int64_t NOUT = SILU ? N / 2 : N;    // output columns (row stride of y)
 
     int64_t row0, row_end, n0;
     int64_t e = 0;
@@ -77,6 +88,41 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
             const int cnt = ee < E ? offsets[ee + 1] - offsets[ee] : 0;
             return cnt > 0 ? (cnt + BM - 1) / BM : 0;
         };
+        // this workgroup's item: slot bid / 8 of XCD bid % 8's contiguous range
+        // of (row tile, column block) items
+        const int64_t ncb = (NOUT + BNO - 1) / BNO;
+        const int64_t bid = blockIdx.x, xcd = bid % kXcds;
+        int64_t item, last;
+        if (E <= 64) {
+            // one wave: inclusive scan of the experts' row tiles over its
+            // lanes, then the expert holding this item's row tile
+            if (wave == 0) {
+                const int tl = tiles_of(lane);
+                int incl = tl;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int v = __shfl_up(incl, off);
+                    if (lane >= off) incl += v;
+                }
+                const int64_t total = __shfl(incl, 63);
+                const int64_t items = total * ncb;
+                const int64_t it = items * xcd / kXcds + bid / kXcds;
+                const int tile = (int)(it / ncb);
+                if (lane == 0) {
+                    s_info[0] = -1;
+                    s_info[2] = (int)total;
+                }
+                if (it < items * (xcd + 1) / kXcds && lane < E && tile >= incl - tl && tile < incl) {
+                    s_info[0] = lane;
+                    s_info[1] = tile - (incl - tl);
+                }
+            }
+            __syncthreads();
+            const int64_t items = (int64_t)s_info[2] * ncb;
+            item = items * xcd / kXcds + bid / kXcds;
+            last = items * (xcd + 1) / kXcds;
+            if (item >= last) return;   // uniform: surplus workgroup
+        } else {
         // total row tiles over all experts
         if (tid == 0) {
             s_info[0] = -1;
@@ -89,15 +135,11 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
         for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
         if (lane == 0) atomicAdd(&s_info[2], part);
         __syncthreads();
-        // this workgroup's item: slot bid / 8 of XCD bid % 8's contiguous range
-        const int64_t ncb = (N + BN - 1) / BN;
         const int64_t items = (int64_t)s_info[2] * ncb;
-        const int64_t bid = blockIdx.x;
-        const int64_t xcd = bid % kXcds, first = items * xcd / kXcds, last = items * (xcd + 1) / kXcds;
-        const int64_t item = first + bid / kXcds;
+        item = items * xcd / kXcds + bid / kXcds;
+        last = items * (xcd + 1) / kXcds;
         if (item >= last) return;   // uniform: surplus workgroup
         const int tile = (int)(item / ncb);
-        n0 = (item % ncb) * BN;
         // expert and row tile within it (block-wide inclusive scan per chunk)
         int carry = 0;
         for (int base = 0; base < E; base += NT) {
@@ -119,6 +161,8 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
             carry += scan[NT - 1];
             __syncthreads();
         }
+        }
+        n0 = (item % ncb) * BNO;
         e = s_info[0];   // always found: tile < total row tiles
         row0 = offsets[e] + (int64_t)s_info[1] * BM;
         row_end = offsets[e + 1] < M ? offsets[e + 1] : M;   // offsets[E] == R by contract
@@ -130,8 +174,8 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     // A wave whose columns lie past N (N % 64 == 0, so a wave's columns are all
     // in or all out) still runs the loop on the last columns, with every load
     // in bounds, and stores nothing: no branch around any load in the loop.
-    const bool wave_cols = n0 + (int64_t)wn * TN < N;
-    const int64_t wcol0 = wave_cols ? n0 + (int64_t)wn * TN : N - TN;
+    const bool wave_cols = n0 + (int64_t)wn * TNO < NOUT;
+    const int64_t wcol0 = wave_cols ? n0 + (int64_t)wn * TNO : NOUT - TNO;
 
     // one scale (and zero) row per gm consecutive 128-row groups
     const int64_t GS = G / gm;
@@ -208,10 +252,12 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
 
     // ---- weight fragments, scales and zero points -----------------------------
     const int lj = lane & 31, kg = lane >> 5;
+    // weight column of this lane in column tile ct
+    auto wcol = [&](int ct) -> int64_t { return wcol0 + (SILU ? ct * NOUT : ct * 32) + lj; };
     int64_t boff[CT];          // byte offset of this lane's slot (chunk 2*kg) in group 0
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-        const int64_t n = wcol0 + ct * 32 + lj;
+        const int64_t n = wcol(ct);
         const int64_t nb = n >> 4, jj = n & 15;
         boff[ct] = nb * (int64_t)G * kTileBytes + ((2 * kg) * 16 + jj) * 16;
     }
@@ -230,7 +276,7 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
         }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            const int64_t n = wcol0 + ct * 32 + lj;
+            const int64_t n = wcol(ct);
             const int64_t gs = g / gm;
             sdst[ct] = sc[gs * N + n];
             zdst[ct] = ZERO ? zp[(gs * N + n) >> 1] : (uint8_t)0;
@@ -270,7 +316,7 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
         u32x4_t bcorr[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            const int64_t n = wcol0 + ct * 32 + lj;
+            const int64_t n = wcol(ct);
             s[ct] = h2f<DT>(sw[ct]);
             uint32_t z = 8;
             if constexpr (ZERO) z = __builtin_amdgcn_ubfe((uint32_t)zw[ct], (uint32_t)(n & 1) * 4u, 4);
@@ -337,6 +383,23 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     }
 
     if (!wave_cols) return;
+    if constexpr (SILU) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int64_t col = wcol0 + lj;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = row0 + wm * TM + rt * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
+                if (row < row_end) {
+                    const float gf = h2f<DT>(f2h<DT>(yacc[rt][0][r]));
+                    const float uf = h2f<DT>(f2h<DT>(yacc[rt][1][r]));
+                    const float sg = gf / (1.0f + expf(-gf));
+                    y[row * NOUT + col] = f2h<DT>(sg * uf);
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -374,18 +437,18 @@ static int g_tile_cfg = -1;      // -1: automatic
 int tile_config_count() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0])); }
 void set_tile_config(int idx) { g_tile_cfg = idx; }
 
-template <int DT, bool ZERO, bool GROUPED, int BM, int BN, int WM, int WN>
+template <int DT, bool ZERO, bool GROUPED, int BM, int BN, int WM, int WN, bool SILU = false>
 static hipError_t tile_launch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
                               const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
                               int64_t E, int gm, const float *cs, const float *cz, hipStream_t stream) {
     // grouped: every expert may end in a partial row tile, hence + E; the
     // items go on a 1-D grid rounded up to whole rounds over the XCDs
-    const int64_t ncb = (N + BN - 1) / BN;
+    const int64_t ncb = SILU ? (N / 2 + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
     const int64_t mtiles = GROUPED ? (M + BM - 1) / BM + E : (M + BM - 1) / BM;
     const int64_t slots = (mtiles * ncb + kXcds - 1) / kXcds * kXcds;
     if (GROUPED && slots > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid = GROUPED ? dim3((unsigned)slots) : dim3((unsigned)mtiles, (unsigned)ncb);
-    hipLaunchKernelGGL((gemm_tile_kernel<DT, ZERO, BM, BN, WM, WN, GROUPED>), grid, dim3(WM * WN * 64), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<DT, ZERO, BM, BN, WM, WN, GROUPED, SILU>), grid, dim3(WM * WN * 64), 0,
                        stream, (const uint16_t *)x, offsets, row_src, (const uint8_t *)wp, (const uint16_t *)scale,
                        (const uint8_t *)zero, (uint16_t *)y, M, K, N, (int)E, gm, cs, cz);
     return hipGetLastError();
@@ -436,6 +499,36 @@ static hipError_t tile_dispatch_dt(const void *x, const int32_t *offsets, const 
                     : tile_dispatch<DT_BF16, false, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, cs, cz, stream);
     return zero ? tile_dispatch<DT_F16, true, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, cs, cz, stream)
                 : tile_dispatch<DT_F16, false, GROUPED>(x, offsets, row_src, wp, scale, zero, y, M, K, N, E, gm, cs, cz, stream);
+}
+
+// Grouped gate/up projection with the SiLU-and-multiply epilogue (N = 2 * I
+// weight columns in, a [M][I] out) for the grouped tile shapes whose waves
+// hold a gate and an up tile; hipErrorNotSupported for any other shape (the
+// caller then runs the projection and the separate kernel).
+template <int DT, bool ZERO>
+static hipError_t tile_silu_dispatch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
+                                     const void *scale, const void *zero, void *a, int64_t M, int64_t K, int64_t N,
+                                     int64_t E, hipStream_t stream) {
+    int idx = g_tile_cfg;
+    if (idx < 0 || idx >= tile_config_count()) idx = M / E <= 96 ? 2 : 0;     // the grouped defaults
+    const TileCfg c = kTileCfgs[idx];
+    if (c.bm == 32 && c.bn == 256 && c.wm == 1 && c.wn == 4)
+        return tile_launch<DT, ZERO, true, 32, 256, 1, 4, true>(x, offsets, row_src, wp, scale, zero, a, M, K, N, E,
+                                                                1, nullptr, nullptr, stream);
+    if (c.bm == 64 && c.bn == 256 && c.wm == 1 && c.wn == 4)
+        return tile_launch<DT, ZERO, true, 64, 256, 1, 4, true>(x, offsets, row_src, wp, scale, zero, a, M, K, N, E,
+                                                                1, nullptr, nullptr, stream);
+    return hipErrorNotSupported;
+}
+
+hipError_t launch_gemm_tile_silu(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
+                                 const void *scale, const void *zero, void *a, int64_t M, int64_t K, int64_t N,
+                                 int64_t E, int dt, hipStream_t stream) {
+    if (dt == DT_BF16)
+        return zero ? tile_silu_dispatch<DT_BF16, true>(x, offsets, row_src, wp, scale, zero, a, M, K, N, E, stream)
+                    : tile_silu_dispatch<DT_BF16, false>(x, offsets, row_src, wp, scale, zero, a, M, K, N, E, stream);
+    return zero ? tile_silu_dispatch<DT_F16, true>(x, offsets, row_src, wp, scale, zero, a, M, K, N, E, stream)
+                : tile_silu_dispatch<DT_F16, false>(x, offsets, row_src, wp, scale, zero, a, M, K, N, E, stream);
 }
 
 hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *wp, const void *scale,

@@ -33,6 +33,12 @@ hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *w
                             const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
                             int dt, hipStream_t stream, const int32_t *row_src = nullptr, int gm = 1,
                             const float *cs = nullptr, const float *cz = nullptr);
+// Grouped gate/up projection (N = 2 * I weight columns) with the
+// SiLU-and-multiply epilogue, a [M][I]; hipErrorNotSupported for tile shapes
+// without a gate/up pair per wave.
+hipError_t launch_gemm_tile_silu(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
+                                 const void *scale, const void *zero, void *a, int64_t M, int64_t K, int64_t N,
+                                 int64_t E, int dt, hipStream_t stream);
 
 // MSD: decomposition, int8 products + merge, split-K reduction.
 struct MsdPlan {

@@ -11,7 +11,11 @@
 //                         token of every row
 //   gemm_tile_kernel      gate/up projection  h = x[token of row] . W13_e
 //                         (grouped; the gather is folded into its x loads)
-//   silu_and_mul_kernel   a = silu(h[:, :I]) * h[:, I:]
+//                         with a = silu(h[:, :I]) * h[:, I:] in its epilogue
+//                         (h rounded to the dtype first, never stored)
+//   silu_and_mul_kernel   the same a from a stored h (standalone entry point,
+//                         and the chain's fallback for tile shapes without a
+//                         gate/up pair per wave)
 //   gemm_tile_kernel      down projection     o = a . W2_e          (grouped)
 //   moe_sum_kernel        out[t] = sum_k topk_w[t,k] * o[row of (t,k)]
 //
@@ -270,8 +274,16 @@ hipError_t launch_fused_moe(const void *x, const int32_t *ids, const float *topk
     hipError_t err = launch_moe_align(ids, T, topk, E, offsets, sorted, row_of, stream, tok);
     // the grouped kernel takes its row tiles from the offsets (offsets[E] <= n)
     // and reads row r of its x operand from token tok[r]
-    if (err == hipSuccess) err = launch_gemm_tile(x, offsets, w13, s13, z13, h, n, H, 2 * I, E, dt, stream, tok);
-    if (err == hipSuccess) err = launch_silu_and_mul(h, offsets + E, n, I, a, dt, stream);
+    if (err == hipSuccess) {
+        // gate/up projection with SiLU-and-multiply in its epilogue; tile
+        // shapes without a gate/up pair per wave (test hook) run the
+        // projection into h and the separate kernel
+        err = launch_gemm_tile_silu(x, offsets, tok, w13, s13, z13, a, n, H, 2 * I, E, dt, stream);
+        if (err == hipErrorNotSupported) {
+            err = launch_gemm_tile(x, offsets, w13, s13, z13, h, n, H, 2 * I, E, dt, stream, tok);
+            if (err == hipSuccess) err = launch_silu_and_mul(h, offsets + E, n, I, a, dt, stream);
+        }
+    }
     if (err == hipSuccess) err = launch_gemm_tile(a, offsets, w2, s2, z2, o, n, I, H, E, dt, stream);
     if (err == hipSuccess) err = launch_moe_sum(o, row_of, topk_w, T, topk, H, out, dt, stream);
     return err;

@@ -35,8 +35,9 @@ constexpr int kAlignCache = 8192;                     // routing ids kept in LDS
 
 // One workgroup: per-expert counts (LDS atomics), an exclusive scan over the
 // experts, then a stable placement of 1024 entries at a time.  The first
-// kAlignCache ids are read from memory once and kept in LDS for the placement
-// pass.  Inside a wave the lanes holding the same expert are found with one
+// kAlignCache ids are read from memory once (every load issued before the
+// first is used) and kept in LDS for the placement pass; with E <= 64 one
+// wave scans the counts.  Inside a wave the lanes holding the same expert are found with one
 // ballot per bit of the expert id; a lane's rank among them is the count of
 // such lanes below it, and the waves' per-expert counts (in LDS) order the
 // waves.
@@ -48,6 +49,7 @@ moe_align_kernel(const int32_t *__restrict__ ids, int64_t n, int E, int topk, in
     __shared__ int base[kMoeMaxExperts];              // counts, then the running position per expert
     __shared__ int wcnt[NW][kMoeMaxExperts];          // per-wave counts of the current chunk
     __shared__ int scan[kAlignThreads];
+    constexpr int PT = kAlignCache / kAlignThreads;     // cached ids per thread (entry tid + 1024 j)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     for (int e = tid; e < E; e += kAlignThreads) {
@@ -56,27 +58,60 @@ moe_align_kernel(const int32_t *__restrict__ ids, int64_t n, int E, int topk, in
         for (int w = 0; w < NW; ++w) wcnt[w][e] = 0;
     }
     __syncthreads();
-    for (int64_t i = tid; i < n; i += kAlignThreads) {
+    int ev[PT];
+    {
+#pragma unroll
+        for (int j = 0; j < PT; ++j) {
+            const int64_t i = tid + (int64_t)j * kAlignThreads;
+            ev[j] = i < n ? ids[i] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < PT; ++j) {
+            const int64_t i = tid + (int64_t)j * kAlignThreads;
+            if (i < n) {
+                idc[i] = ev[j];
+                if (ev[j] >= 0 && ev[j] < E) atomicAdd(&base[ev[j]], 1);
+            }
+        }
+    }
+    for (int64_t i = kAlignCache + tid; i < n; i += kAlignThreads) {
         const int e = ids[i];
-        if (i < kAlignCache) idc[i] = e;
         if (e >= 0 && e < E) atomicAdd(&base[e], 1);
     }
     __syncthreads();
-    // exclusive scan over the experts (E <= kAlignThreads: one per thread)
-    const int cnt = tid < E ? base[tid] : 0;
-    scan[tid] = cnt;
-    __syncthreads();
-    for (int off = 1; off < kAlignThreads; off <<= 1) {
-        const int v = tid >= off ? scan[tid - off] : 0;
+    // exclusive scan over the experts
+    if (E <= 64) {
+        if (wave == 0) {
+            const int cnt = lane < E ? base[lane] : 0;
+            int incl = cnt;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int v = __shfl_up(incl, off);
+                if (lane >= off) incl += v;
+            }
+            if (lane < E) {
+                offsets[lane] = incl - cnt;
+                base[lane] = incl - cnt;
+            }
+            if (lane == 63) offsets[E] = incl;
+        }
+    } else {
+        // E <= kAlignThreads: one expert per thread
+        const int cnt = tid < E ? base[tid] : 0;
+        scan[tid] = cnt;
         __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
+        for (int off = 1; off < kAlignThreads; off <<= 1) {
+            const int v = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += v;
+            __syncthreads();
+        }
+        if (tid < E) {
+            offsets[tid] = scan[tid] - cnt;
+            base[tid] = scan[tid] - cnt;
+        }
+        if (tid == kAlignThreads - 1) offsets[E] = scan[tid];
     }
-    if (tid < E) {
-        offsets[tid] = scan[tid] - cnt;
-        base[tid] = scan[tid] - cnt;
-    }
-    if (tid == kAlignThreads - 1) offsets[E] = scan[tid];
     __syncthreads();
 
     int nbits = 0;
@@ -165,7 +200,9 @@ silu_and_mul_kernel(const uint16_t *__restrict__ h, const int32_t *__restrict__ 
 }
 
 // out[t][n] = RNE(sum over routed k, ascending, of topk_w[t,k] * o[row][n])
-// in fp32; 8 columns per lane.
+// in fp32; 8 columns per lane.  The routing entries and rows of up to eight k
+// are loaded before any is used (one memory round trip per eight k instead
+// of two per k); the sum keeps the ascending order.
 template <int DT>
 __global__ void __launch_bounds__(256)
 moe_sum_kernel(const uint16_t *__restrict__ o, const int32_t *__restrict__ row_of,
@@ -176,16 +213,27 @@ moe_sum_kernel(const uint16_t *__restrict__ o, const int32_t *__restrict__ row_o
         float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-        for (int k = 0; k < topk; ++k) {
-            const int32_t r = row_of[t * topk + k];
-            if (r < 0) continue;
-            const float wk = topk_w[t * topk + k];
-            const u32x4_t ov = ld128(o + (int64_t)r * N + v * 8);
+        for (int k0 = 0; k0 < topk; k0 += 8) {
+            int32_t r[8];
+            float wk[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t word = ov[q];
-                acc[2 * q] = __builtin_fmaf(wk, h2f<DT>((uint16_t)(word & 0xFFFFu)), acc[2 * q]);
-                acc[2 * q + 1] = __builtin_fmaf(wk, h2f<DT>((uint16_t)(word >> 16)), acc[2 * q + 1]);
+            for (int j = 0; j < 8; ++j) {
+                const bool in = k0 + j < topk;
+                r[j] = in ? row_of[t * topk + k0 + j] : -1;
+                wk[j] = in ? topk_w[t * topk + k0 + j] : 0.f;
+            }
+            u32x4_t ov[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ov[j] = r[j] >= 0 ? ld128(o + (int64_t)r[j] * N + v * 8) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (r[j] < 0) continue;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t word = ov[j][q];
+                    acc[2 * q] = __builtin_fmaf(wk[j], h2f<DT>((uint16_t)(word & 0xFFFFu)), acc[2 * q]);
+                    acc[2 * q + 1] = __builtin_fmaf(wk[j], h2f<DT>((uint16_t)(word >> 16)), acc[2 * q + 1]);
+                }
             }
         }
         u32x4_t res;

@@ -324,6 +324,42 @@ mx_tile_kernel(const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx, c
             const int cnt = ee < E ? offsets[ee + 1] - offsets[ee] : 0;
             return cnt > 0 ? (cnt + BM - 1) / BM : 0;
         };
+        // this workgroup's item: slot bid / 8 of XCD bid % 8's contiguous range
+        const int64_t ncb = (N + BN - 1) / BN;
+        const int64_t bid = blockIdx.x, xcd = bid % kMxXcds;
+        int64_t item;
+        if (E <= 64) {
+            // one wave: inclusive scan of the experts' row tiles over its
+            // lanes, then the expert holding this item's row tile
+            if (wave == 0) {
+                const int tl = tiles_of(lane);
+                int incl = tl;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int v = __shfl_up(incl, off);
+                    if (lane >= off) incl += v;
+                }
+                const int64_t total = __shfl(incl, 63);
+                const int64_t items = total * ncb;
+                const int64_t it = items * xcd / kMxXcds + bid / kMxXcds;
+                const int tile = (int)(it / ncb);
+                if (lane == 0) {
+                    s_info[0] = -1;
+                    s_info[2] = (int)total;
+                }
+                if (it < items * (xcd + 1) / kMxXcds && lane < E && tile >= incl - tl && tile < incl) {
+                    s_info[0] = lane;
+                    s_info[1] = tile - (incl - tl);
+                }
+            }
+            __syncthreads();
+            // values read back from LDS are the same in every lane:
+            // readfirstlane keeps them (and the tile offsets derived from
+            // them) scalar
+            const int64_t items = (int64_t)__builtin_amdgcn_readfirstlane(s_info[2]) * ncb;
+            item = items * xcd / kMxXcds + bid / kMxXcds;
+            if (item >= items * (xcd + 1) / kMxXcds) return;   // uniform: surplus workgroup
+        } else {
         if (tid == 0) {
             s_info[0] = -1;
             s_info[2] = 0;
@@ -335,16 +371,10 @@ mx_tile_kernel(const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx, c
         for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
         if (lane == 0) atomicAdd(&s_info[2], part);
         __syncthreads();
-        // values read back from LDS are the same in every lane: readfirstlane
-        // keeps them (and the tile offsets derived from them) scalar
-        const int64_t ncb = (N + BN - 1) / BN;
         const int64_t items = (int64_t)__builtin_amdgcn_readfirstlane(s_info[2]) * ncb;
-        const int64_t bid = blockIdx.x;
-        const int64_t xcd = bid % kMxXcds, first = items * xcd / kMxXcds, last = items * (xcd + 1) / kMxXcds;
-        const int64_t item = first + bid / kMxXcds;
-        if (item >= last) return;   // uniform: surplus workgroup
+        item = items * xcd / kMxXcds + bid / kMxXcds;
+        if (item >= items * (xcd + 1) / kMxXcds) return;   // uniform: surplus workgroup
         const int tile = (int)(item / ncb);
-        n0 = (item % ncb) * BN;
         int carry = 0;
         for (int base = 0; base < E; base += NT) {
             const int ee = base + tid;
@@ -365,6 +395,8 @@ mx_tile_kernel(const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx, c
             carry += scan[NT - 1];
             __syncthreads();
         }
+        }
+        n0 = (item % ncb) * BN;
         e = __builtin_amdgcn_readfirstlane(s_info[0]);   // always found: tile < total row tiles
         row0 = offsets[e] + (int64_t)__builtin_amdgcn_readfirstlane(s_info[1]) * BM;
         row_end = offsets[e + 1] < M ? offsets[e + 1] : M;   // offsets[E] == R by contract

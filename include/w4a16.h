@@ -214,6 +214,9 @@ size_t w4a16_fused_moe_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64
  *   a = silu_and_mul(h)              rounded to dt
  *   o = a . dequant(W2_e)            (grouped W4A16; W2_e [I][H]), rounded to dt
  *   out[t] = moe_sum(o)              [T][H], dt
+ * The first two lines run as one kernel: h is rounded to dt in registers and
+ * a is formed in the projection's epilogue, bit-identical to the separate
+ * steps (the h part of the workspace is then unused).
  * w13_packed / w2_packed are the prepacked weights of all E experts (K = H,
  * N = 2I and K = I, N = H); s13 [E][H/128][2I], s2 [E][I/128][H] in dt;
  * z13 [E][H/128][I], z2 [E][I/128][H/2] uint4 zero points or both NULL

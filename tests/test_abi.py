@@ -118,7 +118,10 @@ def test_binding_raises_on_error():
 def test_variant_table():
     assert "small" in w4.w4a16_test_variant_name(1, 4096, 14336, 1, 1)
     assert "small" in w4.w4a16_test_variant_name(16, 4096, 14336, 1, 1)
-    assert "tile" in w4.w4a16_test_variant_name(17, 4096, 4096, 1, 0)
+    assert "small" in w4.w4a16_test_variant_name(17, 4096, 4096, 1, 0)      # two 16-row tiles
+    assert "small" in w4.w4a16_test_variant_name(32, 4096, 14336, 1, 1)
+    assert "tile" in w4.w4a16_test_variant_name(17, 4224, 4096, 1, 0)       # past 32 groups
+    assert "tile" in w4.w4a16_test_variant_name(33, 4096, 4096, 1, 0)
     assert "tile" in w4.w4a16_test_variant_name(4096, 4096, 4096, 1, 0)
 
 

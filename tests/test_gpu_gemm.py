@@ -29,7 +29,7 @@ def test_tiny(orc):
     _run_and_check(orc, synth.tiny(), "tiny")
 
 
-@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("M", [1, 4, 16, 32])
 def test_decode_full(orc, M):
     _run_and_check(orc, synth.decode(M), f"decode_m{M}")
 
@@ -53,6 +53,14 @@ def test_prefill_full(orc):
     (16, 4096, 512, synth.BF16, False, 1),
     (1, 9216, 128, synth.BF16, False, 0),   # K past the small-M kernel's 64 groups: tile kernel
     (3, 8192, 192, synth.F16, True, 0),     # exactly 64 groups: small-M kernel, 4 groups per wave
+    # 16 < M <= 32: the small-M kernel with two 16-row tiles (8 waves; 4, 2
+    # or 1 groups per wave), and past 32 groups the tile kernel
+    (32, 4096, 1024, synth.BF16, False, 0),
+    (24, 2048, 192, synth.F16, True, 0),
+    (31, 1024, 320, synth.BF16, True, 0),
+    (18, 256, 128, synth.F16, False, 0),
+    (20, 4224, 128, synth.BF16, False, 0),
+    (29, 1536, 256, synth.BF16, True, 1),
 ])
 def test_edge_shapes(orc, M, K, N, dt, signed, variant):
     p = synth.make_dense(M, K, N, dt, signed=signed, seed=M + K + N,
@@ -69,15 +77,17 @@ def test_large_activations_bf16(orc):
     _run_and_check(orc, p, "large_x_small", 1)
 
 
-@pytest.mark.parametrize("dt,signed,variant", [
-    (synth.BF16, False, 1), (synth.BF16, True, 2), (synth.F16, False, 2), (synth.F16, True, 1)])
-def test_unit_rows_bit_exact(orc, dt, signed, variant):
+@pytest.mark.parametrize("dt,signed,variant,rows", [
+    (synth.BF16, False, 1, 10), (synth.BF16, True, 2, 10), (synth.F16, False, 2, 10), (synth.F16, True, 1, 10),
+    (synth.BF16, False, 1, 20), (synth.F16, True, 1, 20)])
+def test_unit_rows_bit_exact(orc, dt, signed, variant, rows):
     """x = e_k rows: y row = RNE((q[k,:] - z) * s) exactly (pins weight,
-    scale and zero indexing in the kernels)."""
+    scale and zero indexing in the kernels; 20 rows: the second 16-row tile
+    of the small-M kernel)."""
     import weight_only_quantized_amd as w4
     from gpu_helpers import Dev, to_host_u16
     K, N = 512, 192
-    ks = [0, 1, 2, 9, 31, 32, 127, 128, 200, 511]
+    ks = [0, 1, 2, 9, 31, 32, 127, 128, 200, 511, 3, 64, 65, 255, 256, 300, 383, 384, 447, 510][:rows]
     p = synth.make_dense(len(ks), K, N, dt, signed=signed, seed=21)
     xf = np.zeros((len(ks), K), np.float32)
     for i, k in enumerate(ks):

@@ -88,10 +88,11 @@ bool mx_use_small(int64_t M, int64_t K) {
 // Offset of sx behind qx in the W4A8-MXFP4 workspace (256-byte aligned).
 size_t mx_ws_sx_offset(int64_t M, int64_t K) { return ((size_t)M * (size_t)K + 255) & ~(size_t)255; }
 
-// Dense dispatch table: decode-sized M goes to the split-K kernel, the rest to
-// the LDS-staged tile kernel.
+// Dense dispatch table: decode-sized M goes to the split-K kernel (one 16-row
+// tile up to M = 16, two up to M = 32 with K <= 4096), the rest to the
+// LDS-staged tile kernel.
 int pick_variant(int64_t M, int64_t K) {
-    const bool small_ok = M <= 16 && K <= w4::small_max_k();
+    const bool small_ok = (M <= 16 && K <= w4::small_max_k()) || (M <= 32 && K <= w4::small2_max_k());
     const int forced = g_force_variant.load(std::memory_order_relaxed);
     if (forced == 1 && small_ok) return 1;
     if (forced == 2) return 2;

@@ -1,5 +1,5 @@
-// gemm_small.hip — decode-sized W4A16 GEMM (M <= 16): split-K over the waves
-// of a workgroup, reduced through LDS.
+// gemm_small.hip — decode-sized W4A16 GEMM (M <= 16, or M <= 32 with two
+// 16-row tiles): split-K over the waves of a workgroup, reduced through LDS.
 //
 // Work split: a workgroup owns NB 16-column blocks and the whole K range.
 // Wave w owns the K slice of SG consecutive 128-row groups w*SG .. w*SG+SG-1
@@ -44,14 +44,19 @@
 namespace w4 {
 
 constexpr int kSmallMaxWaves = 16;
+// MT = 2 (two 16-row tiles: twice the x slice in registers) runs at most 8
+// waves per workgroup (two per SIMD, 256 registers each)
+constexpr int kSmallMaxWaves2 = 8;
 
-template <int DT, bool ZERO, int NB, int SG, int D>
-__global__ void __launch_bounds__(kSmallMaxWaves * 64)
+// MT 16-row tiles of x share every dequantized weight operand.
+template <int DT, bool ZERO, int NB, int SG, int D, int MT = 1>
+__global__ void __launch_bounds__((MT == 1 ? kSmallMaxWaves : kSmallMaxWaves2) * 64)
 gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp,
                   const uint16_t *__restrict__ scale, const uint8_t *__restrict__ zero,
                   uint16_t *__restrict__ y, int M, int64_t K, int64_t N, int gm, const float *__restrict__ cs,
                   const float *__restrict__ cz) {
     static_assert(NB == 1 || NB == 2 || NB == 4, "one 64-lane load covers the scales of <= 4 blocks");
+    static_assert(MT == 1 || MT == 2, "one or two 16-row tiles");
     constexpr int T = NB * SG;                    // tiles per wave, ordered block-major
     const int G = (int)(K / kGroup);
     const int W = blockDim.x >> 6;
@@ -65,9 +70,13 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     // Rows >= M read row M - 1 (in bounds, finite): the matrix core keeps rows
     // apart, and those result rows are never stored.  No branch around the
     // loads, so no wait for every outstanding load.
-    const int jrow = j < M ? j : M - 1;
     const uint8_t *xbase = reinterpret_cast<const uint8_t *>(x);
-    const uint32_t xoff = (uint32_t)((int64_t)jrow * K + 32 * kc) * 2u;
+    uint32_t xoff[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int jrow = 16 * mt + j < M ? 16 * mt + j : M - 1;
+        xoff[mt] = (uint32_t)((int64_t)jrow * K + 32 * kc) * 2u;
+    }
     // buffer resource over this workgroup's NB * G weight tiles (raw, 32-bit
     // data format; every offset below is in range)
     const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -75,12 +84,14 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     const int woff = lane * 16;
 
     // ---- x slice of this wave: A operands of every group, loaded once ---------
-    u32x4_t xa[SG][4];
+    u32x4_t xa[SG][MT][4];
 #pragma unroll
     for (int i = 0; i < SG; ++i) {
         const int g = g0 + i < G ? g0 + i : G - 1;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) xa[i][t] = ld128(xbase + (int64_t)g * (kGroup * 2) + xoff + 16 * t);
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xa[i][mt][t] = ld128(xbase + (int64_t)g * (kGroup * 2) + xoff[mt] + 16 * t);
     }
 
     // ---- scales and zero points: one load per group for all NB blocks -------
@@ -120,23 +131,27 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     // the same for every block, used as accumulator input) or, with zero
     // points, the row sums of x (B = 1.0 in every slot) that each tile scales
     // by its column's -(128 + z).
-    f32x4_t corr[SG];
+    f32x4_t corr[SG][MT];
     if constexpr (DT == DT_BF16) {
         const uint32_t c2 = ZERO ? 0x3F803F80u : bf16_negbias(8) * 0x10001u;
         const u32x4_t bc = {c2, c2, c2, c2};
 #pragma unroll
-        for (int i = 0; i < SG; ++i) {
-            corr[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < SG; ++i)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) corr[i] = mfma16x16x32<DT>(xa[i][t], bc, corr[i]);
-        }
+            for (int mt = 0; mt < MT; ++mt) {
+                corr[i][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) corr[i][mt] = mfma16x16x32<DT>(xa[i][mt][t], bc, corr[i][mt]);
+            }
     }
 
-    float yacc[NB][4];
+    float yacc[NB][MT][4];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yacc[b][r] = 0.f;
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yacc[b][mt][r] = 0.f;
 
 #pragma unroll
     for (int q = 0; q < T; ++q) {
@@ -145,37 +160,47 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
         __builtin_amdgcn_sched_barrier(0);
         const int b = q / SG, i = q % SG;
         const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * b + j) << 2, (int)sz[i]);
-        f32x4_t acc;
+        f32x4_t acc[MT];
         uint32_t nb2 = 0;
-        if constexpr (DT == DT_BF16 && !ZERO) {
-            acc = corr[i];
-        } else {
-            acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if constexpr (DT == DT_F16) nb2 = ZERO ? f16_negbias2(v >> 16) : f16_negbias2(8u);
-        }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc = mfma16x16x32<DT>(xa[i][t], dequant_word<DT>(raw[q][t], nb2), acc);
+        for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (DT == DT_BF16 && !ZERO) acc[mt] = corr[i][mt];
+            else acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        if constexpr (DT == DT_F16) nb2 = ZERO ? f16_negbias2(v >> 16) : f16_negbias2(8u);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const u32x4_t wq = dequant_word<DT>(raw[q][t], nb2);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x32<DT>(xa[i][mt][t], wq, acc[mt]);
+        }
         if constexpr (DT == DT_BF16 && ZERO) {
             // 128 + z sits in byte 2: one byte-to-float conversion
             const float nbias = -(float)((v >> 16) & 0xFFu);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(nbias, corr[i][r], acc[r]);
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(nbias, corr[i][mt][r], acc[mt][r]);
         }
         const float sv = h2f<DT>((uint16_t)(v & 0xFFFFu));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yacc[b][r] += sv * acc[r];
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yacc[b][mt][r] += sv * acc[mt][r];
     }
 
     // ---- reduce the waves' partial sums ---------------------------------------
-    __shared__ float red[kSmallMaxWaves][NB][16][17];
+    __shared__ float red[MT == 1 ? kSmallMaxWaves : kSmallMaxWaves2][NB][16 * MT][17];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][b][4 * kc + r][j] = yacc[b][r];
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][b][16 * mt + 4 * kc + r][j] = yacc[b][mt][r];
     __syncthreads();
 
-    for (int idx = threadIdx.x; idx < NB * 256; idx += W * 64) {
-        const int b = idx >> 8, row = (idx >> 4) & 15, col = idx & 15;
+    for (int idx = threadIdx.x; idx < NB * 256 * MT; idx += W * 64) {
+        const int b = idx / (256 * MT), row = (idx >> 4) % (16 * MT), col = idx & 15;
         if (row < M) {
             float sum = 0.f;
             for (int w = 0; w < W; ++w) sum += red[w][b][row][col];
@@ -198,14 +223,14 @@ int small_config_count() { return (int)(sizeof(kSmallCfgs) / sizeof(kSmallCfgs[0
 void set_small_config(int idx) { g_small_cfg = idx; }
 int64_t small_max_k() { return (int64_t)kSmallMaxWaves * 4 * kGroup; }
 
-template <int DT, bool ZERO, int NB, int SG, int D>
+template <int DT, bool ZERO, int NB, int SG, int D, int MT = 1>
 static hipError_t small_launch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
                                int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
                                hipStream_t stream) {
     const int64_t G = K / kGroup;
     const int64_t waves = (G + SG - 1) / SG;
     const dim3 grid((unsigned)(N / (16 * NB)));
-    hipLaunchKernelGGL((gemm_small_kernel<DT, ZERO, NB, SG, D>), grid, dim3((unsigned)(waves * 64)), 0, stream,
+    hipLaunchKernelGGL((gemm_small_kernel<DT, ZERO, NB, SG, D, MT>), grid, dim3((unsigned)(waves * 64)), 0, stream,
                        (const uint16_t *)x, (const uint8_t *)wp, (const uint16_t *)scale,
                        (const uint8_t *)zero, (uint16_t *)y, (int)M, K, N, gm, cs, cz);
     return hipGetLastError();
@@ -240,9 +265,38 @@ static hipError_t small_dispatch(const void *x, const void *wp, const void *scal
     return hipErrorInvalidValue;
 }
 
+// Two 16-row tiles (16 < M <= 32): at most 8 waves, so SG = ceil(G / 8) in
+// {1, 2, 4} (K <= 4096), NB * SG <= 8 and every tile of a wave in flight.
+int64_t small2_max_k() { return (int64_t)kSmallMaxWaves2 * 4 * kGroup; }
+
+template <int DT, bool ZERO>
+static hipError_t small2_dispatch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
+                                  int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
+                                  hipStream_t stream) {
+    const int64_t G = K / kGroup;
+    if (G > kSmallMaxWaves2 * 4) return hipErrorInvalidValue;       // K > small2_max_k()
+    const int sg = G <= kSmallMaxWaves2 ? 1 : G <= 2 * kSmallMaxWaves2 ? 2 : 4;
+    int nb = 4;
+    while ((N / 16) % nb != 0) nb /= 2;
+#define W4_SMALL2(NBV, SGV, DV)                                                                 \
+    if (nb == NBV && sg == SGV)                                                                 \
+        return small_launch<DT, ZERO, NBV, SGV, DV, 2>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
+    W4_SMALL2(4, 4, 8) W4_SMALL2(2, 4, 8) W4_SMALL2(4, 2, 8) W4_SMALL2(4, 1, 4) W4_SMALL2(1, 4, 4) W4_SMALL2(2, 2, 4)
+    W4_SMALL2(1, 2, 2) W4_SMALL2(2, 1, 2) W4_SMALL2(1, 1, 1)
+#undef W4_SMALL2
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm_small(const void *x, const void *wp, const void *scale, const void *zero, void *y,
                              int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream, int gm, const float *cs,
                              const float *cz) {
+    if (M > 16) {
+        if (dt == DT_BF16)
+            return zero ? small2_dispatch<DT_BF16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream)
+                        : small2_dispatch<DT_BF16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
+        return zero ? small2_dispatch<DT_F16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream)
+                    : small2_dispatch<DT_F16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);
+    }
     if (dt == DT_BF16)
         return zero ? small_dispatch<DT_BF16, true>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream)
                     : small_dispatch<DT_BF16, false>(x, wp, scale, zero, y, M, K, N, gm, cs, cz, stream);

@@ -18,6 +18,8 @@ hipError_t launch_unpack(const void *in, void *w, int64_t E, int64_t K, int64_t 
 int small_config_count();
 void set_small_config(int idx);
 int64_t small_max_k();
+// Its two-tile form for 16 < M <= 32 (K <= small2_max_k()).
+int64_t small2_max_k();
 // gm: 128-row groups per scale group (scale and zero have K/(128*gm) rows).
 // cs: optional per-column fp32 secondary scale applied before the rounding;
 // cz: optional fp32 [M][N] subtracted before it (floating-point zero points).

@@ -21,7 +21,7 @@ def _u8(a):
 
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("signed", [True, False])
-@pytest.mark.parametrize("M", [1, 16, 100])
+@pytest.mark.parametrize("M", [1, 16, 24, 100])
 @pytest.mark.parametrize("dtype", [synth.BF16, synth.F16])
 def test_gemm_desc(orc, bits, signed, M, dtype):
     import weight_only_quantized_amd as w4
@@ -61,7 +61,7 @@ def test_gemm_desc(orc, bits, signed, M, dtype):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("M", [1, 16, 100])
+@pytest.mark.parametrize("M", [1, 16, 24, 100])
 @pytest.mark.parametrize("dtype", [synth.BF16, synth.F16])
 @pytest.mark.parametrize("with_t", [False, True])
 def test_float_zero_points(orc, bits, M, dtype, with_t):

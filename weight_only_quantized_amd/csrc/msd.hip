@@ -362,13 +362,25 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
 // Sum of the K slices' partial sums (matrix-core result layout: per row chunk z,
 // 16-column block nb and 16-row tile mt, 64 lanes x 4 result registers) and
 // rounding to fp16.  One thread per lane and tile; slice stride `slice` floats.
+// The slices of up to eight k are loaded before any is added (one memory
+// round trip per eight slices); the sum keeps the order 0 .. ksplit-1.
 __global__ void __launch_bounds__(256)
 msd_reduce_kernel(const float *__restrict__ part, uint16_t *__restrict__ y, int64_t M, int64_t N, int mt_count,
                   int64_t nlanes, int64_t slice, int ksplit) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;      // (z, nb, mt, lane)
     if (t >= nlanes) return;
     f32x4_t acc = *reinterpret_cast<const f32x4_t *>(part + t * 4);
-    for (int k = 1; k < ksplit; ++k) acc += *reinterpret_cast<const f32x4_t *>(part + k * slice + t * 4);
+    for (int k0 = 1; k0 < ksplit; k0 += 8) {
+        f32x4_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int k = k0 + i < ksplit ? k0 + i : ksplit - 1;   // in bounds; not added past ksplit
+            v[i] = *reinterpret_cast<const f32x4_t *>(part + k * slice + t * 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (k0 + i < ksplit) acc += v[i];
+    }
     const int lane = (int)(t & 63);
     const int64_t tile = t >> 6;
     const int mt = (int)(tile % mt_count);

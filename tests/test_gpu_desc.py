@@ -96,3 +96,28 @@ def test_float_zero_points(orc, bits, M, dtype, with_t):
                        workspace=ws, workspace_bytes=nb)
     _, ref = orc.channel_scaled(y64, t, dtype)
     check_tol(to_host_u16(y), ref, dtype, label=f"fzero_b{bits}_m{M}_t{int(with_t)}")
+
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F16])
+def test_float_zero_points_many_groups(orc, dtype):
+    """Floating-point zero points over 18 scale groups: the correction kernel
+    takes groups eight at a time (two full chunks and a ragged one)."""
+    import weight_only_quantized_amd as w4
+    from gpu_helpers import check_tol, to_dev, to_host_u16
+    M, K, N, group = 3, 2304, 192, 128
+    G = K // group
+    rng = np.random.default_rng(77)
+    print(f"[case] float zero many groups M={M} K={K} N={N} dtype={dtype}", flush=True)
+    zf = synth.to_bits((rng.random((G, N)) * 15.0).astype(np.float32), dtype)
+    p = synth.make_dense(M, K, N, dtype, signed=False, seed=5, group=group)
+    wp = torch.empty(w4.w4a16_prepacked_bytes(1, K, N), dtype=torch.uint8, device=DEV)
+    w4.w4a16_prepack(to_dev(p.w.reshape(-1)), wp, 1, K, N, 0)
+    y64, ref = orc.w4a16_fzero(p.x, p.w, p.scale, zf, M, K, N, dtype, group=group)
+    x, sc, zd = to_dev(p.x), to_dev(p.scale), to_dev(zf)
+    d = w4.weight_desc(sc, zd, None, 4, group, zero_format=1)
+    nb = w4.w4a16_gemm_desc_workspace_bytes(d, M, K, N)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    w4.w4a16_gemm_desc(x, wp, y, M, K, N, sc, zd, None, weight_bits=4, group_size=group, dt=dtype, zero_format=1,
+                       workspace=ws, workspace_bytes=nb)
+    check_tol(to_host_u16(y), ref, dtype, label="fzero_many_groups")

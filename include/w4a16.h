@@ -321,8 +321,9 @@ w4a16_status w4a16_gemm_desc(const void *x, const void *w_packed, const w4a16_we
  * Shape rules: K % 128 == 0, N % 64 == 0, M >= 0, E >= 1, and one expert's
  * packed weights below 2 GiB ((K/128) * (N/16) * 1088 < 2^31).
  * Alignment: x, qx, w, w_packed, workspace 16 bytes; sx 4 bytes; y 2 bytes.
- * Kernels: M <= 16 with K <= 8192 runs a split-K kernel; everything else a
- * tile kernel that stages the quantized activations in LDS.
+ * Kernels: M <= 48 with K <= 8192 runs a split-K kernel (one 16-row tile per
+ * grid row); everything else a tile kernel that stages the quantized
+ * activations in LDS.
  */
 
 /* Bytes of the prepacked MXFP4 buffer: E * (K/128) * (N/16) * 1088. */
@@ -350,14 +351,14 @@ w4a16_status w4a8_mxfp8_quantize(const void *x, void *qx, void *sx, int64_t M, i
 w4a16_status w4a8_mxfp4_gemm_prequant(const void *qx, const void *sx, const void *w_packed, void *y, int64_t M,
                                       int64_t K, int64_t N, int dt, void *stream);
 
-/* Scratch for w4a8_mxfp4_gemm: 0 when the split-K kernel runs (M <= 16,
+/* Scratch for w4a8_mxfp4_gemm: 0 when the split-K kernel runs (M <= 48,
  * K <= 8192: activations are quantized in its registers), else room for qx
  * and sx. */
 size_t w4a8_mxfp4_workspace_bytes(int64_t M, int64_t K);
 
 /*
  * y[M][N] = MXFP8(x) . MXFP4(W): quantizes x (dtype dt) and multiplies.  For
- * M <= 16 (K <= 8192) one kernel does both (each wave quantizes its K slice
+ * M <= 48 (K <= 8192) one kernel does both (each wave quantizes its K slice
  * in registers); otherwise x is quantized into the workspace first.
  * workspace: device, >= w4a8_mxfp4_workspace_bytes(M, K) bytes (may be NULL
  * when that is 0); contents on return unspecified; calls sharing one

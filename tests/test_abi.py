@@ -189,9 +189,10 @@ def test_mxfp4_sizes_and_validation():
     assert w4.w4a8_mxfp4_prepacked_bytes(1, 4096, 14336) == 32 * 896 * 1088
     assert w4.w4a8_mxfp4_prepacked_bytes(0, 128, 64) == 0
     assert w4.w4a8_mxfp4_workspace_bytes(16, 4096) == 0               # quantized in registers
+    assert w4.w4a8_mxfp4_workspace_bytes(48, 4096) == 0
     assert w4.w4a8_mxfp4_workspace_bytes(16, 16384) >= 16 * 16384     # K beyond the split-K kernel
-    ws = w4.w4a8_mxfp4_workspace_bytes(17, 4096)
-    assert ws >= 17 * 4096 + 17 * 128 and (17 * 4096 + 255) // 256 * 256 <= ws
+    ws = w4.w4a8_mxfp4_workspace_bytes(49, 4096)
+    assert ws >= 49 * 4096 + 49 * 128 and (49 * 4096 + 255) // 256 * 256 <= ws
     L = w4.lib()
     F = FAKE
     # (call, expected status): shapes, dtype, nulls, alignment, workspace; all
@@ -205,8 +206,8 @@ def test_mxfp4_sizes_and_validation():
         (lambda: L.w4a8_mxfp4_gemm(F, F, F, 1, 128, 64, 5, None, 0, None), 3),        # dtype
         (lambda: L.w4a8_mxfp4_gemm(None, F, F, 1, 128, 64, 1, None, 0, None), 1),
         (lambda: L.w4a8_mxfp4_gemm(F + 8, F, F, 1, 128, 64, 1, None, 0, None), 4),    # x alignment
-        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 17, 128, 64, 1, None, 0, None), 5),       # workspace
-        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 17, 128, 64, 1, F, 16, None), 5),
+        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 49, 128, 64, 1, None, 0, None), 5),       # workspace
+        (lambda: L.w4a8_mxfp4_gemm(F, F, F, 49, 128, 64, 1, F, 16, None), 5),
         (lambda: L.w4a8_mxfp4_gemm_prequant(F, F, F, F, 1, 128, 48, 1, None), 2),
         (lambda: L.w4a8_mxfp4_gemm_prequant(F, None, F, F, 1, 128, 64, 1, None), 1),
         (lambda: L.w4a8_mxfp8_quantize(F, F, F, 1, 96, 1, None), 2),

@@ -159,7 +159,8 @@ def _check_bound(orc, got_bits, qx, sx, p, label):
 
 @pytest.mark.parametrize("dtype", [synth.BF16, synth.F16])
 @pytest.mark.parametrize("M,K,N", [(1, 128, 64), (3, 384, 192), (16, 1024, 320), (9, 4096, 256),
-                                   (16, 8192, 128), (17, 256, 64), (100, 2048, 512)])
+                                   (16, 8192, 128), (17, 256, 64), (33, 1024, 192), (48, 4096, 128),
+                                   (49, 512, 64), (100, 2048, 512)])
 def test_gemm(orc, dtype, M, K, N):
     print(f"[case] mx gemm dtype={dtype} M={M} K={K} N={N}", flush=True)
     from gpu_helpers import to_host_u16
@@ -169,7 +170,7 @@ def test_gemm(orc, dtype, M, K, N):
     _check_bound(orc, got, qx, sx, p, f"mx_gemm_{M}x{K}x{N}")
 
 
-@pytest.mark.parametrize("M", [1, 16, 33])
+@pytest.mark.parametrize("M", [1, 16, 33, 60])
 def test_gemm_prequant(orc, M):
     from gpu_helpers import to_host_u16
     p = synth.make_mx(M, 1024, 256, synth.BF16, seed=M)
@@ -245,10 +246,10 @@ def test_empty_and_errors():
     d = DevMx(p)
     y = torch.empty((0, 64), dtype=torch.int16, device=DEV)
     w4.w4a8_mxfp4_gemm(d.x, d.wp, y, 0, 256, 64, synth.BF16, None, 0)      # M == 0: no-op
-    x = torch.zeros((32, 256), dtype=torch.int16, device=DEV)
-    y = torch.empty((32, 64), dtype=torch.int16, device=DEV)
+    x = torch.zeros((49, 256), dtype=torch.int16, device=DEV)
+    y = torch.empty((49, 64), dtype=torch.int16, device=DEV)
     with pytest.raises(w4.W4A16Error) as e:
-        w4.w4a8_mxfp4_gemm(x, d.wp, y, 32, 256, 64, synth.BF16, None, 0)     # M > 16 needs a workspace
+        w4.w4a8_mxfp4_gemm(x, d.wp, y, 49, 256, 64, synth.BF16, None, 0)     # M > 48 needs a workspace
     assert e.value.status == 5
 
 

@@ -76,13 +76,15 @@ w4a16_status check_mx_kn(int64_t K, int64_t N) {
 // Row limit of the MXFP4 GEMM (32-bit row tiles on the first grid axis).
 constexpr int64_t kMxMaxM = (int64_t(1) << 31) - 1;
 
-// MXFP4 dispatch: M <= 16 (and K within the split-K kernel's reach) runs the
-// split-K kernel, everything else the tile kernel; the test hook can force
-// the tile kernel.
+// MXFP4 dispatch: M <= 48 (and K within the split-K kernel's reach) runs the
+// split-K kernel, one 16-row tile per grid row (measured at K = 4096,
+// N = 14336: M = 24/32/48 in 15.5/16.8/23.1 us against 26.4/27.0/26.4 us on
+// the tile kernel, M = 64 in 29.3 against 26.8 us), everything else the tile
+// kernel; the test hook can force the tile kernel.
 bool mx_use_small(int64_t M, int64_t K) {
     const int forced = g_force_variant.load(std::memory_order_relaxed);
     if (forced == 2) return false;
-    return M <= 16 && K <= w4::mx_small_max_k();
+    return M <= 48 && K <= w4::mx_small_max_k();
 }
 
 // Offset of sx behind qx in the W4A8-MXFP4 workspace (256-byte aligned).

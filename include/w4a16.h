@@ -97,9 +97,10 @@ w4a16_status w4a16_prepack(const void *w, void *w_packed, int64_t E, int64_t K, 
  *   scale    [K/group_size][N], dtype dt
  *   zero     [K/group_size][N/2] uint4 or NULL (see Signedness)
  *   y        [M][N], dtype dt
- * M <= 16 (K <= 8192), and 16 < M <= 32 with K <= 4096 (two 16-row tiles),
- * run a split-K matrix-core kernel whose waves reduce through LDS; larger M
- * runs an LDS-staged tile kernel whose tile shape follows M.
+ * M <= 16 (K <= 8192), and 16 < M <= 64 with K <= 4096 (two 16-row tiles
+ * per workgroup, 32-row groups on the grid), run a split-K matrix-core kernel
+ * whose waves reduce through LDS; larger M runs an LDS-staged tile kernel
+ * whose tile shape follows M.
  */
 w4a16_status w4a16_gemm(const void *x, const void *w_packed, const void *scale,
                         const void *zero, void *y, int64_t M, int64_t K, int64_t N,

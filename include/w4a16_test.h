@@ -52,7 +52,7 @@ int w4a16_test_force_variant(int variant);
 /*
  * Select the (column blocks, groups per wave) configuration of the small-M
  * kernel for subsequent calls with M <= 16: idx in [0, count), or -1 for the
- * default (its two-tile form for 16 < M <= 32 always takes the shape that
+ * default (its two-tile form for 16 < M <= 64 always takes the shape that
  * fits 8 waves).  Tuning only; not thread-safe.  Returns the number of
  * configurations.
  */

@@ -121,7 +121,8 @@ def test_variant_table():
     assert "small" in w4.w4a16_test_variant_name(17, 4096, 4096, 1, 0)      # two 16-row tiles
     assert "small" in w4.w4a16_test_variant_name(32, 4096, 14336, 1, 1)
     assert "tile" in w4.w4a16_test_variant_name(17, 4224, 4096, 1, 0)       # past 32 groups
-    assert "tile" in w4.w4a16_test_variant_name(33, 4096, 4096, 1, 0)
+    assert "small" in w4.w4a16_test_variant_name(64, 4096, 4096, 1, 0)      # two 32-row groups
+    assert "tile" in w4.w4a16_test_variant_name(65, 4096, 4096, 1, 0)
     assert "tile" in w4.w4a16_test_variant_name(4096, 4096, 4096, 1, 0)
 
 

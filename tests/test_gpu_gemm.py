@@ -61,6 +61,9 @@ def test_prefill_full(orc):
     (18, 256, 128, synth.F16, False, 0),
     (20, 4224, 128, synth.BF16, False, 0),
     (29, 1536, 256, synth.BF16, True, 1),
+    (48, 1024, 256, synth.F16, False, 0),   # second 32-row group on the grid, half filled
+    (64, 4096, 512, synth.BF16, False, 0),
+    (33, 384, 192, synth.BF16, True, 0),
 ])
 def test_edge_shapes(orc, M, K, N, dt, signed, variant):
     p = synth.make_dense(M, K, N, dt, signed=signed, seed=M + K + N,

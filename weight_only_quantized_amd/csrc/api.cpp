@@ -91,10 +91,10 @@ bool mx_use_small(int64_t M, int64_t K) {
 size_t mx_ws_sx_offset(int64_t M, int64_t K) { return ((size_t)M * (size_t)K + 255) & ~(size_t)255; }
 
 // Dense dispatch table: decode-sized M goes to the split-K kernel (one 16-row
-// tile up to M = 16, two up to M = 32 with K <= 4096), the rest to the
-// LDS-staged tile kernel.
+// tile up to M = 16; with K <= 4096 two, and a second pair of tiles on the
+// grid up to M = 64), the rest to the LDS-staged tile kernel.
 int pick_variant(int64_t M, int64_t K) {
-    const bool small_ok = (M <= 16 && K <= w4::small_max_k()) || (M <= 32 && K <= w4::small2_max_k());
+    const bool small_ok = (M <= 16 && K <= w4::small_max_k()) || (M <= 64 && K <= w4::small2_max_k());
     const int forced = g_force_variant.load(std::memory_order_relaxed);
     if (forced == 1 && small_ok) return 1;
     if (forced == 2) return 2;

@@ -1,5 +1,6 @@
-// gemm_small.hip — decode-sized W4A16 GEMM (M <= 16, or M <= 32 with two
-// 16-row tiles): split-K over the waves of a workgroup, reduced through LDS.
+// gemm_small.hip — decode-sized W4A16 GEMM (M <= 16, or M <= 64 with two
+// 16-row tiles per workgroup and 32-row groups on the grid): split-K over the
+// waves of a workgroup, reduced through LDS.
 //
 // Work split: a workgroup owns NB 16-column blocks and the whole K range.
 // Wave w owns the K slice of SG consecutive 128-row groups w*SG .. w*SG+SG-1
@@ -66,6 +67,9 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     const int kc = lane >> 4;      // 32-row chunk within a group
     const int64_t nb0 = (int64_t)blockIdx.x * NB;
     const int g0 = wave * SG;
+    // two-tile form: 32-row groups of x on the second grid axis (each streams
+    // the weights; the row groups of a column block share one XCD's L2)
+    const int m0 = MT == 1 ? 0 : (int)blockIdx.y * 16 * MT;
 
     // Rows >= M read row M - 1 (in bounds, finite): the matrix core keeps rows
     // apart, and those result rows are never stored.  No branch around the
@@ -74,7 +78,7 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     uint32_t xoff[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int jrow = 16 * mt + j < M ? 16 * mt + j : M - 1;
+        const int jrow = m0 + 16 * mt + j < M ? m0 + 16 * mt + j : M - 1;
         xoff[mt] = (uint32_t)((int64_t)jrow * K + 32 * kc) * 2u;
     }
     // buffer resource over this workgroup's NB * G weight tiles (raw, 32-bit
@@ -201,12 +205,12 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
 
     for (int idx = threadIdx.x; idx < NB * 256 * MT; idx += W * 64) {
         const int b = idx / (256 * MT), row = (idx >> 4) % (16 * MT), col = idx & 15;
-        if (row < M) {
+        if (m0 + row < M) {
             float sum = 0.f;
             for (int w = 0; w < W; ++w) sum += red[w][b][row][col];
-            if (cz) sum -= cz[(int64_t)row * N + (nb0 + b) * 16 + col];   // floating-point zero points
+            if (cz) sum -= cz[(int64_t)(m0 + row) * N + (nb0 + b) * 16 + col];   // floating-point zero points
             if (cs) sum *= cs[(nb0 + b) * 16 + col];     // secondary (per-column) scale
-            y[(int64_t)row * N + (nb0 + b) * 16 + col] = f2h<DT>(sum);
+            y[(int64_t)(m0 + row) * N + (nb0 + b) * 16 + col] = f2h<DT>(sum);
         }
     }
 }
@@ -229,7 +233,7 @@ static hipError_t small_launch(const void *x, const void *wp, const void *scale,
                                hipStream_t stream) {
     const int64_t G = K / kGroup;
     const int64_t waves = (G + SG - 1) / SG;
-    const dim3 grid((unsigned)(N / (16 * NB)));
+    const dim3 grid((unsigned)(N / (16 * NB)), MT == 1 ? 1u : (unsigned)((M + 16 * MT - 1) / (16 * MT)));
     hipLaunchKernelGGL((gemm_small_kernel<DT, ZERO, NB, SG, D, MT>), grid, dim3((unsigned)(waves * 64)), 0, stream,
                        (const uint16_t *)x, (const uint8_t *)wp, (const uint16_t *)scale,
                        (const uint8_t *)zero, (uint16_t *)y, (int)M, K, N, gm, cs, cz);

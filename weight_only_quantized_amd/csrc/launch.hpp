@@ -18,7 +18,7 @@ hipError_t launch_unpack(const void *in, void *w, int64_t E, int64_t K, int64_t 
 int small_config_count();
 void set_small_config(int idx);
 int64_t small_max_k();
-// Its two-tile form for 16 < M <= 32 (K <= small2_max_k()).
+// Its two-tile form for M > 16 (K <= small2_max_k(); 32-row groups on the grid).
 int64_t small2_max_k();
 // gm: 128-row groups per scale group (scale and zero have K/(128*gm) rows).
 // cs: optional per-column fp32 secondary scale applied before the rounding;

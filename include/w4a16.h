@@ -241,8 +241,8 @@ w4a16_status w4a16_fused_moe(const void *x, const int32_t *topk_ids, const float
  *   prepacked with is_signed = 1) or uint8 q with uint8 zero points
  *   zero[K/gs][N] (one byte each; is_signed = 0); scale[K/gs][N] in dt.
  * Shape, group and alignment rules as for w4a16_gemm (group_size a multiple
- * of 128 dividing K).  M <= 16 with K <= 8192 runs a split-K kernel, larger M
- * an LDS-staged tile kernel.
+ * of 128 dividing K).  M <= 48 with K <= 8192 runs a split-K kernel (one
+ * 16-row tile per grid row), larger M an LDS-staged tile kernel.
  */
 
 /* Bytes of the prepacked 8-bit buffer: E*K*N. */

@@ -82,7 +82,7 @@ def test_prepack_layout(signed):
 
 
 CASES = [(1, 4096, 256), (5, 384, 192), (16, 8192, 128), (3, 128, 64),
-         (17, 256, 64), (100, 2048, 576), (300, 1024, 1088)]
+         (17, 256, 64), (40, 1024, 320), (48, 4096, 128), (49, 512, 128), (100, 2048, 576), (300, 1024, 1088)]
 
 
 @pytest.mark.parametrize("signed", [True, False])

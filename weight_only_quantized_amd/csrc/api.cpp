@@ -90,6 +90,11 @@ bool mx_use_small(int64_t M, int64_t K) {
 // Offset of sx behind qx in the W4A8-MXFP4 workspace (256-byte aligned).
 size_t mx_ws_sx_offset(int64_t M, int64_t K) { return ((size_t)M * (size_t)K + 255) & ~(size_t)255; }
 
+// W8A16: the split-K kernel (one 16-row tile per grid row) up to M = 48
+// (measured at K = 4096, N = 14336: M = 24/32/48 in 22.2/24.1/33.0 us against
+// 37.4/38.6/40.4 us on the tile kernel; M = 64 42.2 against 40.4 us).
+constexpr int64_t kW8SmallMaxM = 48;
+
 // Dense dispatch table: decode-sized M goes to the split-K kernel (one 16-row
 // tile up to M = 16; with K <= 4096 two, and a second pair of tiles on the
 // grid up to M = 64), the rest to the LDS-staged tile kernel.
@@ -404,7 +409,7 @@ w4a16_status w8a16_gemm(const void *x, const void *w_packed, const void *scale, 
         return W4A16_ERR_ALIGN;
     if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
     const int forced = g_force_variant.load(std::memory_order_relaxed);
-    const bool small = forced != 2 && M <= 16 && K <= w4::w8_small_max_k();
+    const bool small = forced != 2 && M <= kW8SmallMaxM && K <= w4::w8_small_max_k();
     return map_err(w4::launch_w8_gemm(x, w_packed, scale, zero, y, M, K, N, dt, gm, small, (hipStream_t)stream));
 }
 
@@ -479,7 +484,7 @@ w4a16_status w4a16_gemm_desc(const void *x, const void *w_packed, const w4a16_we
     }
     if (desc->weight_bits == 8) {
         const int forced = g_force_variant.load(std::memory_order_relaxed);
-        const bool small = forced != 2 && M <= 16 && K <= w4::w8_small_max_k();
+        const bool small = forced != 2 && M <= kW8SmallMaxM && K <= w4::w8_small_max_k();
         return map_err(w4::launch_w8_gemm(x, w_packed, desc->scale, zero, y, M, K, N, dt, gm, small, s, cs, cz));
     }
     if (pick_variant(M, K) == 1)

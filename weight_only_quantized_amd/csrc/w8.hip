@@ -117,8 +117,9 @@ w8_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp, 
     const int kc = lane >> 4;
     const int64_t nb0 = (int64_t)blockIdx.x * NB;
     const int g0 = wave * SG;
+    const int m0 = (int)blockIdx.y * 16;             // 16-row tile of x (grid rows)
 
-    const int jrow = j < M ? j : M - 1;
+    const int jrow = m0 + j < M ? m0 + j : M - 1;
     const uint8_t *xbase = reinterpret_cast<const uint8_t *>(x);
     const uint32_t xoff = (uint32_t)((int64_t)jrow * K + 32 * kc) * 2u;
     const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -222,12 +223,12 @@ w8_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp, 
 
     for (int idx = threadIdx.x; idx < NB * 256; idx += W * 64) {
         const int b = idx >> 8, row = (idx >> 4) & 15, col = idx & 15;
-        if (row < M) {
+        if (m0 + row < M) {
             float sum = 0.f;
             for (int w = 0; w < W; ++w) sum += red[w][b][row][col];
-            if (cz) sum -= cz[(int64_t)row * N + (nb0 + b) * 16 + col];   // floating-point zero points
+            if (cz) sum -= cz[(int64_t)(m0 + row) * N + (nb0 + b) * 16 + col];   // floating-point zero points
             if (cs) sum *= cs[(nb0 + b) * 16 + col];     // secondary (per-column) scale
-            y[(int64_t)row * N + (nb0 + b) * 16 + col] = f2h<DT>(sum);
+            y[(int64_t)(m0 + row) * N + (nb0 + b) * 16 + col] = f2h<DT>(sum);
         }
     }
 }
@@ -483,7 +484,7 @@ static hipError_t w8_small_launch(const void *x, const void *wp, const void *sca
                                   hipStream_t stream) {
     const int64_t G = K / kGroup;
     const int64_t waves = (G + SG - 1) / SG;
-    hipLaunchKernelGGL((w8_small_kernel<DT, ZERO, NB, SG, D>), dim3((unsigned)(N / (16 * NB))),
+    hipLaunchKernelGGL((w8_small_kernel<DT, ZERO, NB, SG, D>), dim3((unsigned)(N / (16 * NB)), (unsigned)((M + 15) / 16)),
                        dim3((unsigned)(waves * 64)), 0, stream, (const uint16_t *)x, (const uint8_t *)wp,
                        (const uint16_t *)scale, (const uint8_t *)zero, (uint16_t *)y, (int)M, K, N, gm, cs, cz);
     return hipGetLastError();

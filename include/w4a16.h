@@ -352,17 +352,20 @@ w4a16_status w4a8_mxfp8_quantize(const void *x, void *qx, void *sx, int64_t M, i
 w4a16_status w4a8_mxfp4_gemm_prequant(const void *qx, const void *sx, const void *w_packed, void *y, int64_t M,
                                       int64_t K, int64_t N, int dt, void *stream);
 
-/* Scratch for w4a8_mxfp4_gemm: 0 when the split-K kernel runs (M <= 48,
- * K <= 8192: activations are quantized in its registers), else room for qx
- * and sx. */
+/* Scratch for w4a8_mxfp4_gemm: room for qx and sx (M*K bytes rounded up to
+ * 256, then M*K/32), whichever kernel the call picks, so one query always
+ * suffices.  The split-K kernel (M <= 48, K <= 8192: activations quantized in
+ * its registers) uses none of it, and for those calls the workspace may be
+ * NULL.  Returns 0 for M <= 0 or K <= 0. */
 size_t w4a8_mxfp4_workspace_bytes(int64_t M, int64_t K);
 
 /*
  * y[M][N] = MXFP8(x) . MXFP4(W): quantizes x (dtype dt) and multiplies.  For
  * M <= 48 (K <= 8192) one kernel does both (each wave quantizes its K slice
  * in registers); otherwise x is quantized into the workspace first.
- * workspace: device, >= w4a8_mxfp4_workspace_bytes(M, K) bytes (may be NULL
- * when that is 0); contents on return unspecified; calls sharing one
+ * workspace: device, >= w4a8_mxfp4_workspace_bytes(M, K) bytes, or NULL for
+ * a call that runs the split-K kernel (W4A16_ERR_WORKSPACE if the tile kernel
+ * runs without one); contents on return unspecified; calls sharing one
  * workspace must be ordered on one stream.
  */
 w4a16_status w4a8_mxfp4_gemm(const void *x, const void *w_packed, void *y, int64_t M, int64_t K, int64_t N,

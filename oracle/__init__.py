@@ -48,6 +48,7 @@ def lib():
         L = C.CDLL(LIB_PATH)
         sig = {
             "oracle_num_threads": ([], C.c_int),
+            "oracle_set_num_threads": ([C.c_int], None),
             "oracle_f16_to_double": ([C.c_uint16], C.c_double),
             "oracle_bf16_to_double": ([C.c_uint16], C.c_double),
             "oracle_double_to_f16": ([C.c_double], C.c_uint16),
@@ -94,6 +95,11 @@ def _ptr(a):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's parallel loops from now on."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def f16_to_double(bits: int) -> float:
@@ -230,6 +236,26 @@ def fused_moe(c, tokens=None):
                            _ptr(c.z13), _ptr(c.w2), _ptr(c.s2), _ptr(c.z2), c.T, c.topk, c.E, c.H, c.I,
                            128, c.dtype, _ptr(tok), tok.shape[0], _ptr(out))
     return out
+
+
+def fused_moe_steps(c):
+    """The whole fused-experts chain of a synth.MoeChain for every token, composed
+    from the oracle's own steps in the chain's order (routing prep, gate/up
+    grouped W4A16 on the routed rows, silu_and_mul, down grouped W4A16,
+    weighted moe_sum); returns [T][H] bits.  Each routed row is computed once,
+    so this is far cheaper than fused_moe at full size; every row and sum is
+    taken in the same order as fused_moe, so the two agree bit for bit."""
+    offsets, sorted_, row_of = moe_align(c.topk_ids, c.E)
+    R = int(offsets[-1])
+    if R == 0:
+        return moe_sum(np.zeros((1, c.H), np.uint16), row_of, c.topk_w, c.dtype)
+    xs = np.ascontiguousarray(np.asarray(c.x)[sorted_ // c.topk], dtype=np.uint16)   # token of each routed row
+    _, h = grouped(xs, offsets, np.ascontiguousarray(c.w13), np.ascontiguousarray(c.s13),
+                   None if c.z13 is None else np.ascontiguousarray(c.z13), c.E, R, c.H, 2 * c.I, c.dtype)
+    a = silu_and_mul(h, c.dtype)
+    _, o = grouped(a, offsets, np.ascontiguousarray(c.w2), np.ascontiguousarray(c.s2),
+                   None if c.z2 is None else np.ascontiguousarray(c.z2), c.E, R, c.I, c.H, c.dtype)
+    return moe_sum(o, row_of, c.topk_w, c.dtype)
 
 
 def w4a16_fzero(x, w, scale, zf, M, K, N, dtype, group=128):

@@ -40,6 +40,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Thread count of the following parallel loops (timing runs only). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------- */
 /* 16-bit float decoding (exact) and RNE encoding from fp64.                  */
 /* ------------------------------------------------------------------------- */
@@ -544,24 +553,50 @@ void oracle_mxfp8_quantize(const uint16_t *x, int64_t M, int64_t K, int dtype, u
 
 void oracle_w4a8_mxfp4(const uint8_t *qx, const uint8_t *sx, const uint8_t *w, const uint8_t *sw,
                        int64_t M, int64_t K, int64_t N, int dtype, double *y64, uint16_t *y) {
+    if (M <= 0) return;
     int64_t B = K / 32;
-    double *acc = y64 ? y64 : (double *)malloc(sizeof(double) * (size_t)(M * N));
-    assert(acc);
+    /* Step 1: both operands decoded once into fp64 (exact: an E4M3 or E2M1
+     * value times a power of two).  a[m][k] = E4M3(qx) * 2^(sx - 127) for the
+     * 32-block k / 32 of row m; b[k][n] = E2M1(code of (k, n)) * 2^(sw - 127)
+     * for the 32-block k / 32 of column n; the low nibble is the even column. */
+    double *a = (double *)malloc(sizeof(double) * (size_t)M * (size_t)K);
+    double *b = (double *)malloc(sizeof(double) * (size_t)K * (size_t)N);
+    assert(a && b);
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k)
+            a[m * K + k] = oracle_e4m3_to_double(qx[m * K + k]) * oracle_e8m0_to_double(sx[m * B + k / 32]);
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
         for (int64_t n = 0; n < N; ++n) {
-            double s = 0.0;
-            for (int64_t k = 0; k < K; ++k) {
-                double a = oracle_e4m3_to_double(qx[m * K + k]) * oracle_e8m0_to_double(sx[m * B + k / 32]);
-                uint8_t byte = w[k * (N / 2) + n / 2];
-                uint8_t code = (n & 1) ? (byte >> 4) : (byte & 0xF);
-                double b = oracle_e2m1_to_double(code) * oracle_e8m0_to_double(sw[(k / 32) * N + n]);
-                s += a * b;
-            }
-            acc[m * N + n] = s;
+            uint8_t byte = w[k * (N / 2) + n / 2];
+            uint8_t code = (n & 1) ? (byte >> 4) : (byte & 0xF);
+            b[k * N + n] = oracle_e2m1_to_double(code) * oracle_e8m0_to_double(sw[(k / 32) * N + n]);
         }
+    double *acc = y64 ? y64 : (double *)malloc(sizeof(double) * (size_t)(M * N));
+    assert(acc);
+    /* Step 2: acc[m][n] = sum_k a[m][k] * b[k][n], each sum in ascending k
+     * (every product is exact in fp64; the loop over n only runs independent
+     * sums side by side). */
+    const int64_t NC = 512;
+    int64_t nchunks = (N + NC - 1) / NC;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t c = 0; c < nchunks; ++c) {
+            int64_t n0 = c * NC, n1 = n0 + NC < N ? n0 + NC : N;
+            double *row = acc + m * N;
+            for (int64_t n = n0; n < n1; ++n) row[n] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double av = a[m * K + k];
+                const double *br = b + k * N;
+                for (int64_t n = n0; n < n1; ++n) row[n] += av * br[n];
+            }
+        }
+    /* Step 3: one rounding to the output dtype. */
     if (y) oracle_round_array(acc, y, M * N, dtype);
     if (!y64) free(acc);
+    free(a);
+    free(b);
 }
 
 /* ------------------------------------------------------------------------- */

@@ -38,6 +38,7 @@ extern "C" {
 enum { ORACLE_F16 = 0, ORACLE_BF16 = 1 };
 
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 
 /* Exact decoding of 16-bit float patterns and round-to-nearest-even encoding. */
 double   oracle_f16_to_double(uint16_t h);

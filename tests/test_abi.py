@@ -189,8 +189,11 @@ def test_group_sizes_accepted_by_gemm_only():
 def test_mxfp4_sizes_and_validation():
     assert w4.w4a8_mxfp4_prepacked_bytes(1, 4096, 14336) == 32 * 896 * 1088
     assert w4.w4a8_mxfp4_prepacked_bytes(0, 128, 64) == 0
-    assert w4.w4a8_mxfp4_workspace_bytes(16, 4096) == 0               # quantized in registers
-    assert w4.w4a8_mxfp4_workspace_bytes(48, 4096) == 0
+    # the size does not depend on the kernel a call picks (the split-K kernel,
+    # M <= 48, uses none of it but may be given it)
+    assert w4.w4a8_mxfp4_workspace_bytes(16, 4096) == 16 * 4096 + 16 * 128
+    assert w4.w4a8_mxfp4_workspace_bytes(48, 4096) == 48 * 4096 + 48 * 128
+    assert w4.w4a8_mxfp4_workspace_bytes(0, 4096) == 0
     assert w4.w4a8_mxfp4_workspace_bytes(16, 16384) >= 16 * 16384     # K beyond the split-K kernel
     ws = w4.w4a8_mxfp4_workspace_bytes(49, 4096)
     assert ws >= 49 * 4096 + 49 * 128 and (49 * 4096 + 255) // 256 * 256 <= ws
@@ -237,3 +240,4 @@ def test_weight_desc_validation():
     d = w4.WeightDesc(4, 1, 128, F, F, None)
     assert L.w4a16_gemm_desc(F, F, C.byref(d), F, 1, 128, 64, 1, None, 0, None) == 5     # and a workspace
     assert L.w4a16_gemm_desc_workspace_bytes(C.byref(d), 3, 256, 64) >= 3 * 64 * 4
+

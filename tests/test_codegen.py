@@ -6,6 +6,10 @@ corrupts the result (seen on rows 4k+2, 4k+3 of a 16x16 step).  The kernels
 guard every matrix-core call against it; this test compiles each kernel source
 to device assembly and verifies that no MFMA destination overlaps its A or B
 operand (the accumulator input may equal the destination).
+
+Every build disables packed fp32 instructions for the device code; a second
+check verifies that none of the three packed fp32 arithmetic instructions
+appears in the kernels' assembly.
 """
 import concurrent.futures as cf
 import os
@@ -39,11 +43,33 @@ def _device_asm(src, out_dir):
     return open(out).read()
 
 
+_ASMS = None
+
+
+def _all_asm():
+    global _ASMS
+    if _ASMS is None:
+        srcs = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".hip")]
+        with tempfile.TemporaryDirectory() as td, cf.ThreadPoolExecutor(4) as ex:
+            _ASMS = (srcs, list(ex.map(lambda s: _device_asm(s, td), srcs)))
+    return _ASMS
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_no_packed_fp32_arithmetic():
+    srcs, asms = _all_asm()
+    bad = []
+    for src, asm in zip(srcs, asms):
+        for line in asm.splitlines():
+            op = line.strip().split(None, 1)[0] if line.strip() else ""
+            if op in ("v_pk_fma_f32", "v_pk_mul_f32", "v_pk_add_f32"):
+                bad.append(f"{os.path.basename(src)}: {line.strip()}")
+    assert not bad, bad[:10]
+
+
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
 def test_no_mfma_destination_overlaps_sources():
-    srcs = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".hip")]
-    with tempfile.TemporaryDirectory() as td, cf.ThreadPoolExecutor(4) as ex:
-        asms = list(ex.map(lambda s: _device_asm(s, td), srcs))
+    srcs, asms = _all_asm()
     bad, n = [], 0
     for src, asm in zip(srcs, asms):
         for line in asm.splitlines():

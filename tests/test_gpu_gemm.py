@@ -38,6 +38,28 @@ def test_prefill_full(orc):
     _run_and_check(orc, synth.prefill(), "prefill")
 
 
+def test_mrange_full(orc):
+    """The M-range workload the benchmark times: the decode weights (K = 4096,
+    N = 14336, uint4 + zero points, bf16) at M = 32 .. 2048, each M with the
+    kernel the dispatcher picks, on the first M rows of one seeded x; every
+    output compared (the oracle's rows are independent, so one 2048-row
+    reference serves every M)."""
+    import weight_only_quantized_amd as w4
+    from gpu_helpers import Dev, check_tol, to_host_u16
+    Ms = (32, 64, 128, 256, 512, 1024, 2048)
+    p = synth.make_dense(max(Ms), 4096, 14336, synth.BF16, signed=False, scale_range=(0.002, 0.01),
+                         zero_range=(6, 9), seed=0, name="mrange")
+    d = Dev(p)
+    _, y_ref = orc.w4a16(p.x, p.w, p.scale, p.zero, p.M, p.K, p.N, p.dtype)
+    for M in Ms:
+        print(f"[case] mrange M={M} ({w4.w4a16_test_variant_name(M, p.K, p.N, p.dtype, 1)})", flush=True)
+        x = d.x[:M].contiguous()
+        y = torch.empty((M, p.N), dtype=torch.int16, device="cuda:0")
+        w4.w4a16_gemm(x, d.wp, d.scale, d.zero, y, M, p.K, p.N, 128, p.dtype)
+        torch.cuda.synchronize()
+        check_tol(to_host_u16(y), np.ascontiguousarray(y_ref[:M]), p.dtype, label=f"mrange_m{M}")
+
+
 @pytest.mark.parametrize("M,K,N,dt,signed,variant", [
     (1, 128, 64, synth.BF16, True, 0),
     (3, 384, 192, synth.BF16, False, 0),

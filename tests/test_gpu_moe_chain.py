@@ -190,21 +190,16 @@ def test_fused_moe_small(orc, cfg):
     check_tol(to_host_u16(out), orc.fused_moe(c), c.dtype, label=f"fused_moe_cfg{cfg}")
 
 
-def test_fused_moe_full_sampled(orc):
-    """The chain at the MoE workload's sizes (512 tokens, top-8 of 64 experts,
-    H=2048, I=1408), checked on sampled tokens (including ones routed to the
-    most loaded expert)."""
+def test_fused_moe_full(orc):
+    """The chain at the sizes the benchmark times (512 tokens, top-8 of 64
+    experts, H=2048, I=1408, the same seeded inputs), every token compared
+    against the oracle's steps composed over all routed rows."""
     from gpu_helpers import check_tol, to_host_u16
     c = synth.moe_chain()
     print("[case] fused_moe full T=512 topk=8 E=64 H=2048 I=1408", flush=True)
     out = to_host_u16(DevChain(c).run())
     torch.cuda.synchronize()
-    hot = np.bincount(c.topk_ids.reshape(-1), minlength=c.E).argmax()
-    toks = sorted(set([0, 1, 255, 511] + list(np.nonzero((c.topk_ids == hot).any(axis=1))[0][:4]) +
-                      list(np.random.default_rng(0).choice(c.T, 6, replace=False))))
-    ref = orc.fused_moe(c, np.array(toks))
-    check_tol(out[toks], ref, c.dtype, label=f"fused_moe_full tokens={toks}")
-    assert np.all(np.isfinite(synth.bits_to_f32(out, c.dtype)))
+    check_tol(out, orc.fused_moe_steps(c), c.dtype, label="fused_moe_full all tokens")
 
 
 @pytest.mark.parametrize("cfg", [0, 2])

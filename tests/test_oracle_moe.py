@@ -159,3 +159,15 @@ def test_chain_duplicate_experts_and_unrouted(orc):
     none = synth.MoeChain(**{**c.__dict__})
     none.topk_ids = np.full((c.T, 2), -1, np.int32)
     assert not orc.fused_moe(none).any()
+
+
+@pytest.mark.parametrize("cfg", [dict(T=9, topk=2, E=3, H=256, I=128, dtype=synth.BF16, signed=True),
+                                 dict(T=21, topk=4, E=7, H=128, I=256, dtype=synth.F16, signed=False)])
+def test_chain_from_steps_equals_per_token_chain(orc, cfg):
+    """The chain composed from the oracle's steps over all routed rows (used at
+    full size) equals the per-token chain bit for bit, including tokens with
+    unrouted entries."""
+    c = synth.make_moe_chain(seed=cfg["T"], **cfg)
+    c.topk_ids[0, 0] = -1
+    c.topk_ids[-1, -1] = cfg["E"]
+    assert np.array_equal(orc.fused_moe_steps(c), orc.fused_moe(c))

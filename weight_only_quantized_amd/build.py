@@ -32,21 +32,42 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# hipcc passes the target feature to the host (x86) compile too, which
+# rejects it with exactly this message; the device compile must accept it
+# (checked by _check_device_feature before every build).
+_HOST_FEATURE_MSG = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in l and "unknown target feature" not in l.lower()
-                    and l.strip() and "warning generated" not in l)
+                    if l.strip() != _HOST_FEATURE_MSG and l.strip() and "warning generated" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"build failed: {' '.join(cmd)}\n{out}")
     return out
 
 
+def _check_device_feature(cc):
+    """The device compile alone must accept '-packed-fp32-ops' without any
+    message, so that the only rejection the full build can print (and
+    _run drops) is the host compile's."""
+    os.makedirs(BUILD, exist_ok=True)
+    src = os.path.join(BUILD, "feature_probe.hip")
+    with open(src, "w") as f:
+        f.write("#include <hip/hip_runtime.h>\n__global__ void k(float *p) { p[threadIdx.x] *= 2.f; }\n")
+    r = subprocess.run([cc, *COMMON, *DEVICE, "--offload-device-only", "-c", src, "-o", src + ".o"],
+                       capture_output=True, text=True)
+    msg = (r.stdout + r.stderr).strip()
+    if r.returncode != 0 or "packed-fp32-ops" in msg:
+        raise RuntimeError(f"device compile does not accept -packed-fp32-ops:\n{msg}")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
+    _check_device_feature(cc)
     jobs = []
     for s in HIP_SOURCES:
         jobs.append([cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, s), "-o", os.path.join(BUILD, s + ".o")])

@@ -39,6 +39,8 @@
 // wave then issues a single memory instruction, the 128-bit weight load, as
 // a buffer load whose tile offset is a scalar register (no per-load address
 // arithmetic in the vector ALU).
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -221,10 +223,10 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
 struct SmallCfg { int nb, sg, d; };
 static constexpr SmallCfg kSmallCfgs[] = {{4, 2, 4}, {4, 2, 8}, {4, 2, 2}, {2, 4, 4}, {2, 2, 4},
                                           {1, 2, 2}, {1, 4, 4}, {4, 1, 4}};
-static int g_small_cfg = -1;     // -1: automatic
+static std::atomic<int> g_small_cfg{-1};     // -1: automatic
 
 int small_config_count() { return (int)(sizeof(kSmallCfgs) / sizeof(kSmallCfgs[0])); }
-void set_small_config(int idx) { g_small_cfg = idx; }
+void set_small_config(int idx) { g_small_cfg.store(idx, std::memory_order_relaxed); }
 int64_t small_max_k() { return (int64_t)kSmallMaxWaves * 4 * kGroup; }
 
 template <int DT, bool ZERO, int NB, int SG, int D, int MT = 1>
@@ -245,7 +247,7 @@ static hipError_t small_dispatch(const void *x, const void *wp, const void *scal
                                  int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
                                  hipStream_t stream) {
     const int64_t G = K / kGroup;
-    int idx = g_small_cfg;
+    int idx = g_small_cfg.load(std::memory_order_relaxed);
     if (idx < 0 || idx >= small_config_count()) idx = M > 4 ? 1 : 0;
     SmallCfg c = kSmallCfgs[idx];
     // at most 16 waves per workgroup: widen the per-wave slice for long K, and
@@ -269,8 +271,9 @@ static hipError_t small_dispatch(const void *x, const void *wp, const void *scal
     return hipErrorInvalidValue;
 }
 
-// Two 16-row tiles (16 < M <= 32): at most 8 waves, so SG = ceil(G / 8) in
-// {1, 2, 4} (K <= 4096), NB * SG <= 8 and every tile of a wave in flight.
+// Two 16-row tiles (16 < M <= 64 with K <= 4096; above 32 rows further
+// 32-row groups on the grid): at most 8 waves, so SG = ceil(G / 8) in
+// {1, 2, 4}, NB * SG <= 8 and every tile of a wave in flight.
 int64_t small2_max_k() { return (int64_t)kSmallMaxWaves2 * 4 * kGroup; }
 
 template <int DT, bool ZERO>

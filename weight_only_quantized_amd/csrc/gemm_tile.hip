@@ -31,6 +31,8 @@
 // and k-block l / 32 (64 rows of the group: chunks 2*(l/32) and 2*(l/32)+1 of
 // the prepacked slot layout); result register r of lane l is row
 // 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -432,10 +434,10 @@ struct TileCfg { int bm, bn, wm, wn; };
 static constexpr TileCfg kTileCfgs[] = {{64, 256, 1, 4}, {64, 256, 2, 4}, {32, 256, 1, 4},
                                         {64, 128, 2, 2}, {32, 128, 1, 4}, {128, 128, 2, 2},
                                         {128, 256, 2, 4}, {64, 128, 1, 2}};
-static int g_tile_cfg = -1;      // -1: automatic
+static std::atomic<int> g_tile_cfg{-1};      // -1: automatic
 
 int tile_config_count() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0])); }
-void set_tile_config(int idx) { g_tile_cfg = idx; }
+void set_tile_config(int idx) { g_tile_cfg.store(idx, std::memory_order_relaxed); }
 
 template <int DT, bool ZERO, bool GROUPED, int BM, int BN, int WM, int WN, bool SILU = false>
 static hipError_t tile_launch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
@@ -458,7 +460,7 @@ template <int DT, bool ZERO, bool GROUPED>
 static hipError_t tile_dispatch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
                                 const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
                                 int64_t E, int gm, const float *cs, const float *cz, hipStream_t stream) {
-    int idx = g_tile_cfg;
+    int idx = g_tile_cfg.load(std::memory_order_relaxed);
     if (idx < 0 || idx >= tile_config_count()) {
         idx = 0;
         if (GROUPED) {
@@ -509,7 +511,7 @@ template <int DT, bool ZERO>
 static hipError_t tile_silu_dispatch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
                                      const void *scale, const void *zero, void *a, int64_t M, int64_t K, int64_t N,
                                      int64_t E, hipStream_t stream) {
-    int idx = g_tile_cfg;
+    int idx = g_tile_cfg.load(std::memory_order_relaxed);
     if (idx < 0 || idx >= tile_config_count()) idx = M / E <= 96 ? 2 : 0;     // the grouped defaults
     const TileCfg c = kTileCfgs[idx];
     if (c.bm == 32 && c.bn == 256 && c.wm == 1 && c.wn == 4)

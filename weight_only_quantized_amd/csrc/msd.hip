@@ -28,6 +28,8 @@
 // (word & 0x0F0F0F0F gives rows 0,4,1,5; (word >> 4) & 0x0F0F0F0F gives
 // 2,6,3,7), so both operands of v_mfma_i32_16x16x64_i8 see the same k in the
 // same byte.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -449,9 +451,9 @@ static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // tuning through the test hook.
 struct MsdCfg { int mt, nb, waves; };
 static constexpr MsdCfg kMsdCfgs[] = {{2, 4, 8}, {2, 4, 4}, {1, 4, 8}, {4, 2, 8}, {2, 2, 8}, {4, 4, 4}};
-static int g_msd_cfg = -1;       // -1: automatic
+static std::atomic<int> g_msd_cfg{-1};       // -1: automatic
 int msd_config_count() { return (int)(sizeof(kMsdCfgs) / sizeof(kMsdCfgs[0])); }
-void set_msd_config(int idx) { g_msd_cfg = idx; }
+void set_msd_config(int idx) { g_msd_cfg.store(idx, std::memory_order_relaxed); }
 
 static MsdPlan msd_plan_cfg(int64_t M, int64_t K, int64_t N, const MsdCfg &c) {
     MsdPlan p{};
@@ -484,7 +486,7 @@ static MsdPlan msd_plan_cfg(int64_t M, int64_t K, int64_t N, const MsdCfg &c) {
 }
 
 MsdPlan msd_plan(int64_t M, int64_t K, int64_t N) {
-    int idx = g_msd_cfg;
+    int idx = g_msd_cfg.load(std::memory_order_relaxed);
     if (idx < 0 || idx >= msd_config_count()) idx = 0;
     return msd_plan_cfg(M, K, N, kMsdCfgs[idx]);
 }
@@ -558,6 +560,7 @@ hipError_t launch_msd(const void *x, const void *wp, const void *scale, void *y,
                        (const float *)(ws + p.off_part), (uint16_t *)y, M, N, p.mt, nlanes, slice, p.ksplit);
     return hipGetLastError();
 }
+
 
 size_t msd_basic_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     return align_up(msd_workspace_bytes(M, K, N), 256) + sizeof(int32_t) * (size_t)(K / kGroup) * 3 * (size_t)M * (size_t)N;

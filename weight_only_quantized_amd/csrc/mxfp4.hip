@@ -21,6 +21,8 @@
 // bytes 0..1023 are the 64 lanes' B operands (16 bytes each, lane-major), bytes
 // 1024..1087 the 64 lanes' B scales.  One 128-bit and one 8-bit load per lane
 // deliver a whole instruction's weight operand.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -563,10 +565,10 @@ hipError_t launch_mx_quantize(const void *x, void *qx, void *sx, int64_t M, int6
 // Small-kernel variants (NB, SG, D); index 0 is the default.
 struct MxSmallCfg { int nb, sg, d; };
 static constexpr MxSmallCfg kMxSmallCfgs[] = {{4, 2, 4}, {4, 2, 8}, {2, 2, 4}, {4, 1, 4}, {2, 4, 8}, {1, 2, 2}};
-static int g_mx_small_cfg = -1;
+static std::atomic<int> g_mx_small_cfg{-1};
 
 int mx_small_config_count() { return (int)(sizeof(kMxSmallCfgs) / sizeof(kMxSmallCfgs[0])); }
-void set_mx_small_config(int idx) { g_mx_small_cfg = idx; }
+void set_mx_small_config(int idx) { g_mx_small_cfg.store(idx, std::memory_order_relaxed); }
 int64_t mx_small_max_k() { return (int64_t)kMxSmallMaxWaves * 4 * kGroup; }
 
 template <int DT, bool FUSED, int NB, int SG, int D>
@@ -585,7 +587,7 @@ template <int DT, bool FUSED>
 static hipError_t mx_small_dispatch(const void *x, const void *qx, const void *sx, const void *wp, void *y,
                                     int64_t M, int64_t K, int64_t N, hipStream_t stream) {
     const int64_t G = K / kGroup;
-    int idx = g_mx_small_cfg;
+    int idx = g_mx_small_cfg.load(std::memory_order_relaxed);
     if (idx < 0 || idx >= mx_small_config_count()) idx = 0;
     MxSmallCfg c = kMxSmallCfgs[idx];
     while ((G + c.sg - 1) / c.sg > kMxSmallMaxWaves && c.sg < 4) c.sg *= 2;
@@ -627,10 +629,10 @@ hipError_t launch_mx_gemm_small(const void *x, const void *qx, const void *sx, c
 struct MxTileCfg { int bm, bn, wm, wn; };
 static constexpr MxTileCfg kMxTileCfgs[] = {{128, 256, 1, 4}, {128, 256, 2, 4}, {128, 128, 2, 2}, {64, 128, 1, 2},
                                             {64, 256, 1, 4}, {32, 256, 1, 4}, {256, 256, 2, 4}, {128, 512, 1, 8}};
-static int g_mx_tile_cfg = -1;
+static std::atomic<int> g_mx_tile_cfg{-1};
 
 int mx_tile_config_count() { return (int)(sizeof(kMxTileCfgs) / sizeof(kMxTileCfgs[0])); }
-void set_mx_tile_config(int idx) { g_mx_tile_cfg = idx; }
+void set_mx_tile_config(int idx) { g_mx_tile_cfg.store(idx, std::memory_order_relaxed); }
 
 template <int DT, int BM, int BN, int WM, int WN>
 static hipError_t mx_tile_launch(const void *qx, const void *sx, const int32_t *offsets, const void *wp, void *y,
@@ -656,7 +658,7 @@ static hipError_t mx_tile_launch(const void *qx, const void *sx, const int32_t *
 template <int DT>
 static hipError_t mx_tile_dispatch(const void *qx, const void *sx, const int32_t *offsets, const void *wp, void *y,
                                    int64_t M, int64_t K, int64_t N, int64_t E, hipStream_t stream) {
-    int idx = g_mx_tile_cfg;
+    int idx = g_mx_tile_cfg.load(std::memory_order_relaxed);
     if (idx < 0 || idx >= mx_tile_config_count()) {
         if (offsets) {
             // grouped: 64 x 256 tiles (MoE shape, 64 rows per expert on average:

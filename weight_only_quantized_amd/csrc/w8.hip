@@ -20,6 +20,8 @@
 //    and the zero point comes out through the row sums of x: acc - z * S,
 //    S = sum_k x over the group (from extra matrix-core steps with B = 1, or
 //    with B = -128 straight into the accumulator for signed weights).
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -95,7 +97,8 @@ __global__ void __launch_bounds__(64) w8_prepack_kernel(const uint8_t *__restric
 }
 
 // ---------------------------------------------------------------------------
-// Small-M kernel (M <= 16): the split-K structure of the W4A16 decode kernel.
+// Small-M kernel (M <= 48, K <= 8192; one 16-row tile per grid row): the
+// split-K structure of the W4A16 decode kernel.
 // A workgroup owns NB 16-column blocks and all of K; wave w owns the SG groups
 // w*SG .. w*SG+SG-1 for every block, loads its x slice once and streams its
 // NB*SG tiles (two 128-bit buffer loads each) through a D-deep pipeline.
@@ -234,7 +237,7 @@ w8_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp, 
 }
 
 // ---------------------------------------------------------------------------
-// Tile kernel (M > 16): the structure of the W4A16 tile kernel (x slice of a
+// Tile kernel (M > 48, or K beyond the small kernel): the structure of the W4A16 tile kernel (x slice of a
 // group staged in LDS, double-buffered, with the bf16 limbs of its row sums;
 // weights straight from memory into registers; 32x32x16 steps; per-group
 // scale on the fp32 group sum), with 8-bit weight fragments: four 128-bit
@@ -474,9 +477,9 @@ int64_t w8_small_max_k() { return (int64_t)kW8SmallMaxWaves * 4 * kGroup; }
 
 struct W8SmallCfg { int nb, sg, d; };
 static constexpr W8SmallCfg kW8SmallCfgs[] = {{4, 2, 4}, {4, 2, 8}, {2, 2, 4}, {1, 4, 4}};
-static int g_w8_small_cfg = -1;
+static std::atomic<int> g_w8_small_cfg{-1};
 int w8_small_config_count() { return (int)(sizeof(kW8SmallCfgs) / sizeof(kW8SmallCfgs[0])); }
-void set_w8_small_config(int idx) { g_w8_small_cfg = idx; }
+void set_w8_small_config(int idx) { g_w8_small_cfg.store(idx, std::memory_order_relaxed); }
 
 template <int DT, bool ZERO, int NB, int SG, int D>
 static hipError_t w8_small_launch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
@@ -495,7 +498,7 @@ static hipError_t w8_small_dispatch(const void *x, const void *wp, const void *s
                                     int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
                                     hipStream_t stream) {
     const int64_t G = K / kGroup;
-    int idx = g_w8_small_cfg;
+    int idx = g_w8_small_cfg.load(std::memory_order_relaxed);
     if (idx < 0 || idx >= w8_small_config_count()) idx = 0;
     W8SmallCfg c = kW8SmallCfgs[idx];
     while ((G + c.sg - 1) / c.sg > kW8SmallMaxWaves && c.sg < 4) c.sg *= 2;
@@ -525,9 +528,9 @@ static hipError_t w8_small_dispatch(const void *x, const void *wp, const void *s
 struct W8TileCfg { int bm, bn, wm, wn; };
 static constexpr W8TileCfg kW8TileCfgs[] = {{64, 256, 1, 4}, {32, 256, 1, 4}, {64, 128, 2, 2}, {64, 128, 1, 4},
                                             {128, 128, 1, 4}};
-static int g_w8_tile_cfg = -1;
+static std::atomic<int> g_w8_tile_cfg{-1};
 int w8_tile_config_count() { return (int)(sizeof(kW8TileCfgs) / sizeof(kW8TileCfgs[0])); }
-void set_w8_tile_config(int idx) { g_w8_tile_cfg = idx; }
+void set_w8_tile_config(int idx) { g_w8_tile_cfg.store(idx, std::memory_order_relaxed); }
 
 template <int DT, bool ZERO, int BM, int BN, int WM, int WN>
 static hipError_t w8_tile_launch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
@@ -548,7 +551,7 @@ template <int DT, bool ZERO>
 static hipError_t w8_tile_dispatch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
                                    int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
                                    hipStream_t stream) {
-    int idx = g_w8_tile_cfg;
+    int idx = g_w8_tile_cfg.load(std::memory_order_relaxed);
     if (idx < 0 || idx >= w8_tile_config_count()) idx = M <= 64 ? 1 : (DT == DT_BF16 ? 3 : 0);
     if (DT == DT_BF16 && (idx == 0 || idx == 4)) idx = 3;
     const W8TileCfg c = kW8TileCfgs[idx];

@@ -61,7 +61,8 @@ typedef enum {
     W4A16_ERR_UNSUPPORTED = 3,  /* group_size or dtype not supported        */
     W4A16_ERR_ALIGN = 4,        /* a pointer is not aligned as required     */
     W4A16_ERR_WORKSPACE = 5,    /* MSD workspace missing or too small       */
-    W4A16_ERR_DEVICE = 6        /* not a gfx950 device, or a launch failed  */
+    W4A16_ERR_DEVICE = 6,       /* not a gfx950 device, or a launch failed  */
+    W4A16_ERR_SCRATCH = 7       /* needs more than the static scratch holds */
 } w4a16_status;
 
 typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1 } w4a16_dtype;
@@ -129,6 +130,26 @@ size_t w4a16_msd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_
 w4a16_status w4a16_msd_gemm(const void *x, const void *w_packed, const void *antiquant_scale,
                             void *y, int64_t M, int64_t K, int64_t N, int64_t group_size,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * w4a16_msd_gemm without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, result and kernels as
+ * w4a16_msd_gemm; the workspace is a static device array inside the library,
+ * W4A16_MSD_SCRATCH_BYTES per GPU, held by every GPU the library runs on until
+ * the process ends.  A problem whose workspace (that of the kernel
+ * configuration the call runs, at most w4a16_msd_workspace_bytes()) exceeds
+ * it returns W4A16_ERR_SCRATCH before anything is enqueued; the shapes of the
+ * MSD page fit (M = 64, K = N = 8192 needs about 19 MB; M = 1, K = 8192,
+ * N = 12288 about 1 MB).  Calls no allocating routine.  Every call on one GPU shares that GPU's array: calls
+ * that may overlap in time on one GPU (different streams without ordering,
+ * other threads) race and must be serialized by the caller.
+ */
+#define W4A16_MSD_SCRATCH_BYTES ((size_t)32 << 20)
+
+w4a16_status w4a16_msd_gemm_noalloc(const void *x, const void *w_packed, const void *antiquant_scale,
+                                    void *y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+                                    void *stream);
 
 /*
  * Grouped (MoE) W4A16 GEMM: for each expert e, rows

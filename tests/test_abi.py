@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert w4.w4a16_status_str(s).startswith(w4.STATUS_NAMES[s])
     assert "UNKNOWN" in w4.w4a16_status_str(99)
 
@@ -241,3 +241,14 @@ def test_weight_desc_validation():
     assert L.w4a16_gemm_desc(F, F, C.byref(d), F, 1, 128, 64, 1, None, 0, None) == 5     # and a workspace
     assert L.w4a16_gemm_desc_workspace_bytes(C.byref(d), 3, 256, 64) >= 3 * 64 * 4
 
+
+def test_msd_noalloc_validation():
+    L = w4.lib()
+    # the scratch bound is checked on the host, before any device call
+    assert w4.w4a16_msd_workspace_bytes(4096, 8192, 8192) > w4.MSD_SCRATCH_BYTES
+    assert L.w4a16_msd_gemm_noalloc(FAKE, FAKE, FAKE, FAKE, 4096, 8192, 8192, 128, None) == 7
+    assert L.w4a16_msd_gemm_noalloc(None, FAKE, FAKE, FAKE, 64, 8192, 8192, 128, None) == 1
+    assert L.w4a16_msd_gemm_noalloc(FAKE, FAKE, FAKE, FAKE, 64, 8192, 8192, 64, None) == 3
+    assert L.w4a16_msd_gemm_noalloc(FAKE, FAKE, FAKE, FAKE, 64, 8000, 8192, 128, None) == 2
+    assert L.w4a16_msd_gemm_noalloc(FAKE + 8, FAKE, FAKE, FAKE, 64, 8192, 8192, 128, None) == 4
+    assert L.w4a16_msd_gemm_noalloc(FAKE, FAKE, FAKE, FAKE, 0, 8192, 8192, 128, None) == 0

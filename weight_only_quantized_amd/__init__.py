@@ -21,7 +21,7 @@ GROUP_SIZE = 128
 
 W4A16_OK = 0
 STATUS_NAMES = {0: "W4A16_OK", 1: "W4A16_ERR_NULL", 2: "W4A16_ERR_SHAPE", 3: "W4A16_ERR_UNSUPPORTED",
-                4: "W4A16_ERR_ALIGN", 5: "W4A16_ERR_WORKSPACE", 6: "W4A16_ERR_DEVICE"}
+                4: "W4A16_ERR_ALIGN", 5: "W4A16_ERR_WORKSPACE", 6: "W4A16_ERR_DEVICE", 7: "W4A16_ERR_SCRATCH"}
 
 
 class W4A16Error(RuntimeError):
@@ -47,6 +47,7 @@ _SIGS = {
     "w4a16_gemm": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p], C.c_int),
     "w4a16_msd_workspace_bytes": ([_i64, _i64, _i64, _i64], C.c_size_t),
     "w4a16_msd_gemm": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, C.c_size_t, _p], C.c_int),
+    "w4a16_msd_gemm_noalloc": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p], C.c_int),
     "w4a16_grouped_gemm": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, C.c_int, _p], C.c_int),
     "w4a16_moe_align": ([_p, _i64, _i64, _i64, _p, _p, _p, _p], C.c_int),
     "w4a16_moe_gather": ([_p, _p, _p, _i64, _i64, _i64, _i64, _p, C.c_int, _p], C.c_int),
@@ -83,6 +84,9 @@ _SIGS = {
     "w4a16_test_w8_config": ([C.c_int, C.c_int], C.c_int),
 }
 EXPORTED = tuple(_SIGS)
+
+# size of the static per-device scratch of w4a16_msd_gemm_noalloc (W4A16_MSD_SCRATCH_BYTES)
+MSD_SCRATCH_BYTES = 32 << 20
 
 
 def lib():
@@ -147,6 +151,11 @@ def w4a16_msd_gemm(x, w_packed, antiquant_scale, y, M, K, N, group_size=GROUP_SI
                    workspace_bytes=0, stream=None):
     _check(lib().w4a16_msd_gemm(_ptr(x), _ptr(w_packed), _ptr(antiquant_scale), _ptr(y), M, K, N, group_size,
                                 _ptr(workspace), int(workspace_bytes), _stream(stream)), "w4a16_msd_gemm")
+
+
+def w4a16_msd_gemm_noalloc(x, w_packed, antiquant_scale, y, M, K, N, group_size=GROUP_SIZE, stream=None):
+    _check(lib().w4a16_msd_gemm_noalloc(_ptr(x), _ptr(w_packed), _ptr(antiquant_scale), _ptr(y), M, K, N,
+                                        group_size, _stream(stream)), "w4a16_msd_gemm_noalloc")
 
 
 def w4a16_grouped_gemm(x, expert_offsets, w_packed, scale, zero, y, E, R, K, N, group_size=GROUP_SIZE,

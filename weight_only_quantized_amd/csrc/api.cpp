@@ -119,6 +119,9 @@ const char *w4a16_status_str(int status) {
         case W4A16_ERR_ALIGN: return "W4A16_ERR_ALIGN: x, w_packed, workspace need 16-byte, scale and y 2-byte alignment";
         case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE: MSD workspace is NULL or smaller than w4a16_msd_workspace_bytes()";
         case W4A16_ERR_DEVICE: return "W4A16_ERR_DEVICE: current device is not gfx950 or a launch failed";
+        case W4A16_ERR_SCRATCH:
+            return "W4A16_ERR_SCRATCH: the problem needs more workspace than the library's static scratch "
+                   "(W4A16_MSD_SCRATCH_BYTES); use w4a16_msd_gemm with a caller workspace";
         default: return "W4A16_ERR_UNKNOWN";
     }
 }
@@ -177,6 +180,20 @@ w4a16_status w4a16_msd_gemm(const void *x, const void *w_packed, const void *ant
         return W4A16_ERR_ALIGN;
     if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
     return map_err(w4::launch_msd(x, w_packed, antiquant_scale, y, M, K, N, workspace, (hipStream_t)stream));
+}
+
+w4a16_status w4a16_msd_gemm_noalloc(const void *x, const void *w_packed, const void *antiquant_scale, void *y,
+                                    int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream) {
+    w4a16_status st = check_kn(K, N, group_size);
+    if (st != W4A16_OK) return st;
+    if (M < 0 || M > (int64_t(1) << 24)) return W4A16_ERR_SHAPE;
+    if (M == 0) return W4A16_OK;
+    if (!x || !w_packed || !antiquant_scale || !y) return W4A16_ERR_NULL;
+    if (w4::msd_noalloc_bytes(M, K, N) > w4::kMsdScratchBytes) return W4A16_ERR_SCRATCH;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(antiquant_scale, 2) || !aligned(y, 16))
+        return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_msd_noalloc(x, w_packed, antiquant_scale, y, M, K, N, (hipStream_t)stream));
 }
 
 w4a16_status w4a16_grouped_gemm(const void *x, const int32_t *expert_offsets, const void *w_packed,

@@ -59,6 +59,14 @@ int msd_config_count();
 void set_msd_config(int idx);
 hipError_t launch_msd(const void *x, const void *wp, const void *scale, void *y, int64_t M, int64_t K,
                       int64_t N, void *workspace, hipStream_t stream);
+// The same call with the workspace in the library's per-device static scratch
+// (kMsdScratchBytes); hipErrorInvalidValue when the plan that runs needs more
+// (msd_noalloc_bytes: the workspace of that plan alone, not the maximum over
+// configurations that msd_workspace_bytes gives).
+constexpr size_t kMsdScratchBytes = size_t(32) << 20;
+size_t msd_noalloc_bytes(int64_t M, int64_t K, int64_t N);
+hipError_t launch_msd_noalloc(const void *x, const void *wp, const void *scale, void *y, int64_t M, int64_t K,
+                              int64_t N, hipStream_t stream);
 // Basic MSD pipeline (integer products through memory, separate merge).
 size_t msd_basic_workspace_bytes(int64_t M, int64_t K, int64_t N);
 hipError_t launch_msd_basic(const void *x, const void *wp, const void *scale, void *y, int64_t M, int64_t K,

@@ -29,6 +29,7 @@
 // 2,6,3,7), so both operands of v_mfma_i32_16x16x64_i8 see the same k in the
 // same byte.
 #include <atomic>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -544,9 +545,8 @@ static hipError_t msd_pre(const MsdPlan &p, const void *x, uint8_t *ws, int64_t 
     return hipGetLastError();
 }
 
-hipError_t launch_msd(const void *x, const void *wp, const void *scale, void *y, int64_t M, int64_t K,
-                      int64_t N, void *workspace, hipStream_t stream) {
-    const MsdPlan p = msd_plan(M, K, N);
+static hipError_t launch_msd_plan(const MsdPlan &p, const void *x, const void *wp, const void *scale, void *y,
+                                  int64_t M, int64_t K, int64_t N, void *workspace, hipStream_t stream) {
     uint8_t *ws = (uint8_t *)workspace;
     hipError_t err = msd_pre(p, x, ws, M, K, stream);
     if (err != hipSuccess) return err;
@@ -561,6 +561,58 @@ hipError_t launch_msd(const void *x, const void *wp, const void *scale, void *y,
     return hipGetLastError();
 }
 
+hipError_t launch_msd(const void *x, const void *wp, const void *scale, void *y, int64_t M, int64_t K,
+                      int64_t N, void *workspace, hipStream_t stream) {
+    return launch_msd_plan(msd_plan(M, K, N), x, wp, scale, y, M, K, N, workspace, stream);
+}
+
+
+// ---- the MSD call without a caller workspace ---------------------------------
+// For callers that cannot allocate device memory: the workspace lives in a
+// file-scope device array of kMsdScratchBytes that every GPU the library runs
+// on holds until the process ends.  In host code `scratch` is only a host-side
+// stand-in for that array; its device address is taken once per device, with
+// that device current, through hipGetSymbolAddress, and only that address is
+// ever handed to kernels.  Nothing in the workspace needs to start at zero
+// (every byte a kernel reads was written earlier in the same call), so no
+// clearing is done.  All calls on one GPU share the array: calls that overlap
+// in time on one GPU (different streams without ordering) race.
+static __device__ __align__(256) uint8_t scratch[kMsdScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kScratchDevices];
+}  // namespace
+
+static hipError_t msd_scratch_ptr(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    ScratchSlot &sl = g_scratch[dev];
+    std::call_once(sl.once, [&] { sl.err = hipGetSymbolAddress(&sl.ptr, HIP_SYMBOL(scratch)); });
+    if (sl.err != hipSuccess) return sl.err;
+    if (!sl.ptr) return hipErrorInvalidSymbol;
+    *out = sl.ptr;
+    return hipSuccess;
+}
+
+size_t msd_noalloc_bytes(int64_t M, int64_t K, int64_t N) { return msd_plan(M, K, N).total; }
+
+hipError_t launch_msd_noalloc(const void *x, const void *wp, const void *scale, void *y, int64_t M, int64_t K,
+                              int64_t N, hipStream_t stream) {
+    const MsdPlan p = msd_plan(M, K, N);     // the plan that runs: its own workspace size is checked
+    if (p.total > kMsdScratchBytes) return hipErrorInvalidValue;
+    void *ws = nullptr;
+    const hipError_t e = msd_scratch_ptr(&ws);
+    if (e != hipSuccess) return e;
+    return launch_msd_plan(p, x, wp, scale, y, M, K, N, ws, stream);
+}
 
 size_t msd_basic_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     return align_up(msd_workspace_bytes(M, K, N), 256) + sizeof(int32_t) * (size_t)(K / kGroup) * 3 * (size_t)M * (size_t)N;

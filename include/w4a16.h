@@ -6,8 +6,8 @@
  *   X     fp16 or bf16 activations,
  *   W     int4 weights, one scale (same dtype as X) and optionally one uint4
  *         zero point per group of `group_size` consecutive K rows and per
- *         column (group_size a multiple of 128; group_size == K gives one
- *         scale per column),
+ *         column (group_size 32, 64 or a multiple of 128; group_size == K
+ *         gives one scale per column),
  *   dequant(W)[k][n] = (q[k][n] - z[k/gs][n]) * s[k/gs][n], gs = group_size,
  *   fp32 accumulation, Y rounded to the dtype of X.
  * Sources: "Humming: open-source library for quantized inference" (vLLM /
@@ -30,10 +30,11 @@
  *    `zero` is given the weights are unsigned in [0, 15] (prepacked with
  *    is_signed = 0) and zero[G][N/2] holds uint4 zero points packed like w.
  *  - Shape rules: K > 0, K % 128 == 0, N > 0, N % 64 == 0, M (or R) >= 0,
- *    E >= 1.  group_size: a multiple of 128 dividing K for w4a16_gemm and
- *    w4a16_grouped_gemm (else W4A16_ERR_UNSUPPORTED, or W4A16_ERR_SHAPE when
- *    it does not divide K); exactly 128 for the MSD path (whose page fixes
- *    the group at 128 rows) and the MoE chain.  M == 0 (or an expert without rows) is a
+ *    E >= 1.  group_size: 32, 64, or a multiple of 128 dividing K for
+ *    w4a16_gemm and w4a16_grouped_gemm (else W4A16_ERR_UNSUPPORTED, or
+ *    W4A16_ERR_SHAPE when it does not divide K); 32 and 64 need weights
+ *    prepacked by w4a16_prepack_g with that group size; exactly 128 for the
+ *    MSD path (whose page fixes the group at 128 rows) and the MoE chain.  M == 0 (or an expert without rows) is a
  *    no-op that returns W4A16_OK.
  *  - Alignment: x, w_packed, workspace 16 bytes; scale, y 2 bytes.
  *  - Errors: every argument is checked on the host before anything is
@@ -92,6 +93,23 @@ w4a16_status w4a16_prepack(const void *w, void *w_packed, int64_t E, int64_t K, 
                            int is_signed, void *stream);
 
 /*
+ * Weight repack for a given scale group size (Humming article: the
+ * quantization descriptor keeps the scale granularity as its own parameter).
+ * group_size a multiple of 128 gives exactly w4a16_prepack's layout.
+ * group_size 32 or 64 gives the group-aligned layout that w4a16_gemm,
+ * w4a16_grouped_gemm and w4a16_gemm_desc require for those group sizes: the
+ * same tiles and slots with the roles of the slot's 32-row chunk and word
+ * exchanged (word t of slot L holds rows 128*g + 32*t + 8*(L/16) + i, code
+ * of row i at bit 4*(i/2) + 16*(i%2)), so each 16x16x32 and each pair of
+ * 32x32x16 matrix-core steps takes the rows of one 32-row block, which lies
+ * in one scale group.  Same sizes, pointers and errors as w4a16_prepack
+ * (W4A16_ERR_UNSUPPORTED for another group_size, W4A16_ERR_SHAPE when it
+ * does not divide K).
+ */
+w4a16_status w4a16_prepack_g(const void *w, void *w_packed, int64_t E, int64_t K, int64_t N,
+                             int is_signed, int64_t group_size, void *stream);
+
+/*
  * Dense W4A16 GEMM: y[M][N] = x[M][K] . dequant(W).
  *   x        [M][K] fp16/bf16 (dtype dt)
  *   w_packed prepacked weights (E = 1)
@@ -101,7 +119,9 @@ w4a16_status w4a16_prepack(const void *w, void *w_packed, int64_t E, int64_t K, 
  * M <= 16 (K <= 8192), and 16 < M <= 64 with K <= 4096 (two 16-row tiles
  * per workgroup, 32-row groups on the grid), run a split-K matrix-core kernel
  * whose waves reduce through LDS; larger M runs an LDS-staged tile kernel
- * whose tile shape follows M.
+ * whose tile shape follows M.  With group_size 32 or 64 (weights from
+ * w4a16_prepack_g) the split-K kernel covers M <= 16 with K <= 4096 and the
+ * tile kernel the rest, each running one accumulation chain per scale group.
  */
 w4a16_status w4a16_gemm(const void *x, const void *w_packed, const void *scale,
                         const void *zero, void *y, int64_t M, int64_t K, int64_t N,

@@ -77,6 +77,8 @@ def lib():
             "oracle_w4a8_mxfp4": ([_p, _p, _p, _p, _i64, _i64, _i64, C.c_int, _p, _p], None),
             "oracle_prepack": ([_p, _p, _i64, _i64, _i64, C.c_int], None),
             "oracle_unpack": ([_p, _p, _i64, _i64, _i64, C.c_int], None),
+            "oracle_prepack_layout": ([_p, _p, _i64, _i64, _i64, C.c_int, C.c_int], None),
+            "oracle_unpack_layout": ([_p, _p, _i64, _i64, _i64, C.c_int, C.c_int], None),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -311,17 +313,19 @@ def w4a8_mxfp4(qx, sx, w, sw, M, K, N, dtype):
     return y64, y
 
 
-def prepack(w, E, K, N, is_signed):
+def prepack(w, E, K, N, is_signed, layout=0):
+    """layout 0: the standard tile layout; 1: the group-aligned layout used for
+    scale groups of 32 or 64 rows."""
     out = np.empty(E * K * N // 2, dtype=np.uint8)
     wc = np.ascontiguousarray(w, np.uint8)
-    lib().oracle_prepack(_ptr(wc), _ptr(out), E, K, N, int(is_signed))
+    lib().oracle_prepack_layout(_ptr(wc), _ptr(out), E, K, N, int(is_signed), int(layout))
     return out
 
 
-def unpack(packed, E, K, N, is_signed):
+def unpack(packed, E, K, N, is_signed, layout=0):
     out = np.empty(E * K * N // 2, dtype=np.uint8)
     pc = np.ascontiguousarray(packed, np.uint8)
-    lib().oracle_unpack(_ptr(pc), _ptr(out), E, K, N, int(is_signed))
+    lib().oracle_unpack_layout(_ptr(pc), _ptr(out), E, K, N, int(is_signed), int(layout))
     return out
 
 

@@ -359,11 +359,24 @@ void oracle_msd(const uint16_t *x, const uint8_t *w, const uint16_t *scale, int6
  * little-endian uint32 at byte 4t of the slot) holds r = 8t + i, i = 0..7, with
  * the 4-bit code of row r at bit 4*(i / 2) + 16*(i % 2).  The code is the
  * unsigned value u (unsigned weights) or q + 8 (signed weights q in [-8, 7]).
+ *
+ * Group-aligned layout (layout 1, for scale groups of 32 or 64 rows): the
+ * same tiles, slots, words and bit positions, with the roles of the slot's
+ * chunk c = L / 16 and the word t exchanged: word t of slot L holds the rows
+ * k = 128*g + 32*t + 8*c + i, i = 0..7.  (Layout 0 above is the case
+ * k = 128*g + 32*c + 8*t + i.)
  */
-static int64_t packed_bit_index(int64_t K, int64_t N, int64_t e, int64_t k, int64_t n) {
+static int64_t packed_bit_index(int64_t K, int64_t N, int64_t e, int64_t k, int64_t n, int layout) {
     int64_t G = K / 128, NB = N / 16;
     int64_t nb = n / 16, j = n % 16, g = k / 128, kk = k % 128;
-    int64_t c = kk / 32, r = kk % 32, t = r / 8, i = r % 8;
+    int64_t c, t, i = kk % 8;
+    if (layout == 1) {
+        t = kk / 32;
+        c = (kk % 32) / 8;
+    } else {
+        c = kk / 32;
+        t = (kk % 32) / 8;
+    }
     int64_t tile = (e * NB + nb) * G + g;
     int64_t slot = c * 16 + j;
     int64_t byte = tile * 1024 + slot * 16 + t * 4;
@@ -371,14 +384,15 @@ static int64_t packed_bit_index(int64_t K, int64_t N, int64_t e, int64_t k, int6
     return byte * 8 + bit;      /* bit offset inside a little-endian word */
 }
 
-void oracle_prepack(const uint8_t *w, uint8_t *packed, int64_t E, int64_t K, int64_t N, int is_signed) {
+void oracle_prepack_layout(const uint8_t *w, uint8_t *packed, int64_t E, int64_t K, int64_t N, int is_signed,
+                           int layout) {
     memset(packed, 0, (size_t)(E * K * N / 2));
     for (int64_t e = 0; e < E; ++e)
         for (int64_t k = 0; k < K; ++k)
             for (int64_t n = 0; n < N; ++n) {
                 int code = nibble(w + e * K * (N / 2), N, k, n);
                 if (is_signed) code ^= 0x8;   /* (q + 8) mod 16 for two's complement q */
-                int64_t b = packed_bit_index(K, N, e, k, n);
+                int64_t b = packed_bit_index(K, N, e, k, n, layout);
                 /* word-relative bit b%32 of the word at byte (b/32)*4: little endian */
                 int64_t word_byte = (b / 32) * 4;
                 int64_t wb = b % 32;
@@ -386,12 +400,13 @@ void oracle_prepack(const uint8_t *w, uint8_t *packed, int64_t E, int64_t K, int
             }
 }
 
-void oracle_unpack(const uint8_t *packed, uint8_t *w, int64_t E, int64_t K, int64_t N, int is_signed) {
+void oracle_unpack_layout(const uint8_t *packed, uint8_t *w, int64_t E, int64_t K, int64_t N, int is_signed,
+                          int layout) {
     memset(w, 0, (size_t)(E * K * N / 2));
     for (int64_t e = 0; e < E; ++e)
         for (int64_t k = 0; k < K; ++k)
             for (int64_t n = 0; n < N; ++n) {
-                int64_t b = packed_bit_index(K, N, e, k, n);
+                int64_t b = packed_bit_index(K, N, e, k, n, layout);
                 int64_t word_byte = (b / 32) * 4;
                 int64_t wb = b % 32;
                 int code = (packed[word_byte + wb / 8] >> (wb % 8)) & 0xF;
@@ -399,6 +414,14 @@ void oracle_unpack(const uint8_t *packed, uint8_t *w, int64_t E, int64_t K, int6
                 uint8_t *dst = w + e * K * (N / 2) + k * (N / 2) + n / 2;
                 *dst |= (uint8_t)((n & 1) ? (code << 4) : code);
             }
+}
+
+void oracle_prepack(const uint8_t *w, uint8_t *packed, int64_t E, int64_t K, int64_t N, int is_signed) {
+    oracle_prepack_layout(w, packed, E, K, N, is_signed, 0);
+}
+
+void oracle_unpack(const uint8_t *packed, uint8_t *w, int64_t E, int64_t K, int64_t N, int is_signed) {
+    oracle_unpack_layout(packed, w, E, K, N, is_signed, 0);
 }
 
 /* ------------------------------------------------------------------------- */

@@ -81,6 +81,13 @@ void oracle_msd(const uint16_t *x, const uint8_t *w, const uint16_t *scale, int6
  * in words in the design notes) and its inverse.  w/out sizes E*K*N/2. */
 void oracle_prepack(const uint8_t *w, uint8_t *packed, int64_t E, int64_t K, int64_t N, int is_signed);
 void oracle_unpack(const uint8_t *packed, uint8_t *w, int64_t E, int64_t K, int64_t N, int is_signed);
+/* The same with a layout selector: 0 as above, 1 the group-aligned layout for
+ * scale groups of 32 or 64 rows (word t of slot L holds rows
+ * 128*g + 32*t + 8*(L/16) + i). */
+void oracle_prepack_layout(const uint8_t *w, uint8_t *packed, int64_t E, int64_t K, int64_t N, int is_signed,
+                           int layout);
+void oracle_unpack_layout(const uint8_t *packed, uint8_t *w, int64_t E, int64_t K, int64_t N, int is_signed,
+                          int layout);
 
 /* ---- MoE fused-experts chain (pwwt.cn notes, §5: fused_experts_impl runs
  * moe_gemm -> fuse_silu_mul -> moe_gemm; FlagGems-vLLM operator list, MoE and

@@ -24,9 +24,14 @@ def to_host_u16(t: torch.Tensor) -> np.ndarray:
 
 
 def prepack(p: synth.Problem) -> torch.Tensor:
+    """Prepacked weights of p: the group-aligned layout for scale groups of 32
+    or 64 rows, the standard one otherwise."""
     w = to_dev(p.w.reshape(-1))
     out = torch.empty(w4.w4a16_prepacked_bytes(p.E, p.K, p.N), dtype=torch.uint8, device=DEV)
-    w4.w4a16_prepack(w, out, p.E, p.K, p.N, int(p.signed))
+    if p.group < 128:
+        w4.w4a16_prepack_g(w, out, p.E, p.K, p.N, int(p.signed), p.group)
+    else:
+        w4.w4a16_prepack(w, out, p.E, p.K, p.N, int(p.signed))
     return out
 
 

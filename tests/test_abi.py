@@ -53,7 +53,8 @@ FAKE = 1 << 40          # never dereferenced: validation fails first
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(group_size=64), 3),
+    (dict(group_size=48), 3),             # below 128: only 32 and 64
+    (dict(group_size=16), 3),
     (dict(group_size=192), 3),            # not a multiple of 128
     (dict(group_size=512), 2),            # does not divide K = 256
     (dict(dt=7), 3),
@@ -111,7 +112,7 @@ def test_grouped_and_prepack_validation():
 
 def test_binding_raises_on_error():
     with pytest.raises(w4.W4A16Error) as ei:
-        w4.w4a16_gemm(FAKE, FAKE, FAKE, None, FAKE, 4, 256, 256, group_size=32, dt=0, stream=0)
+        w4.w4a16_gemm(FAKE, FAKE, FAKE, None, FAKE, 4, 256, 256, group_size=48, dt=0, stream=0)
     assert ei.value.status == 3
 
 
@@ -252,3 +253,16 @@ def test_msd_noalloc_validation():
     assert L.w4a16_msd_gemm_noalloc(FAKE, FAKE, FAKE, FAKE, 64, 8000, 8192, 128, None) == 2
     assert L.w4a16_msd_gemm_noalloc(FAKE + 8, FAKE, FAKE, FAKE, 64, 8192, 8192, 128, None) == 4
     assert L.w4a16_msd_gemm_noalloc(FAKE, FAKE, FAKE, FAKE, 0, 8192, 8192, 128, None) == 0
+
+
+def test_prepack_g_validation():
+    L = w4.lib()
+    assert L.w4a16_prepack_g(FAKE, FAKE, 1, 256, 64, 1, 48, None) == 3       # unsupported group
+    assert L.w4a16_prepack_g(FAKE, FAKE, 1, 256, 64, 1, 512, None) == 2      # does not divide K
+    assert L.w4a16_prepack_g(FAKE, FAKE, 1, 200, 64, 1, 32, None) == 2       # K % 128 != 0
+    assert L.w4a16_prepack_g(None, FAKE, 1, 256, 64, 1, 32, None) == 1
+    assert L.w4a16_prepack_g(FAKE + 4, FAKE, 1, 256, 64, 1, 64, None) == 4
+    # 32/64-row groups in the descriptor: 4-bit weights with integer zero points only
+    for bits, zf in ((8, 0), (4, 1)):
+        d = w4.WeightDesc(weight_bits=bits, group_size=32, scale=FAKE, zero=FAKE, zero_format=zf)
+        assert L.w4a16_gemm_desc(FAKE, FAKE, C.byref(d), FAKE, 4, 256, 64, 0, None, 0, None) == 3

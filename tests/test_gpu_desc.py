@@ -121,3 +121,24 @@ def test_float_zero_points_many_groups(orc, dtype):
     w4.w4a16_gemm_desc(x, wp, y, M, K, N, sc, zd, None, weight_bits=4, group_size=group, dt=dtype, zero_format=1,
                        workspace=ws, workspace_bytes=nb)
     check_tol(to_host_u16(y), ref, dtype, label="fzero_many_groups")
+
+
+@pytest.mark.parametrize("group,signed,M,dtype", [(32, True, 1, synth.BF16), (64, False, 16, synth.F16),
+                                                  (32, False, 100, synth.BF16), (64, True, 40, synth.F16)])
+def test_gemm_desc_small_scale_groups(orc, group, signed, M, dtype):
+    """The descriptor with 32/64-row scale groups (4-bit weights prepacked by
+    w4a16_prepack_g) and a per-column secondary scale, both kernel families."""
+    import weight_only_quantized_amd as w4
+    from gpu_helpers import check_tol, prepack, to_dev, to_host_u16
+    K, N = 1024, 320
+    print(f"[case] desc group={group} signed={signed} M={M} dtype={dtype}", flush=True)
+    t = np.random.default_rng(M + group).uniform(0.25, 4.0, N).astype(np.float32)
+    p = synth.make_dense(M, K, N, dtype, signed=signed, seed=M + group, group=group)
+    wp = prepack(p)
+    zero = to_dev(p.zero) if p.zero is not None else None
+    y64, _ = orc.w4a16(p.x, p.w, p.scale, p.zero, M, K, N, dtype, group=group)
+    y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    w4.w4a16_gemm_desc(to_dev(p.x), wp, y, M, K, N, to_dev(p.scale), zero, torch.from_numpy(t).to(DEV),
+                       weight_bits=4, group_size=group, dt=dtype)
+    _, ref = orc.channel_scaled(y64, t, dtype)
+    check_tol(to_host_u16(y), ref, dtype, label=f"desc_group{group}_m{M}")

@@ -144,7 +144,7 @@ def test_m_zero_and_errors_leave_y_untouched():
     d = Dev(p)
     y = d.new_y(fill=0x1234)
     w4.w4a16_gemm(d.x, d.wp, d.scale, None, y, 0, p.K, p.N, 128, p.dtype)
-    for kwargs, status in [(dict(group_size=64), 3), (dict(N=100), 2)]:
+    for kwargs, status in [(dict(group_size=48), 3), (dict(N=100), 2)]:
         args = dict(group_size=128, N=p.N)
         args.update(kwargs)
         with pytest.raises(w4.W4A16Error) as ei:
@@ -190,3 +190,32 @@ def test_group_sizes(orc, M, K, N, dt, signed, group, variant):
     column): both kernel families against the oracle at the same group."""
     p = synth.make_dense(M, K, N, dt, signed=signed, seed=M + group, group=group)
     _run_and_check(orc, p, f"group{group}_{M}x{K}x{N}", variant=variant)
+
+
+@pytest.mark.parametrize("M,K,N,dt,signed,group,variant", [
+    (1, 128, 64, synth.BF16, True, 32, 0),     # one 128-row tile, split-K kernel
+    (4, 512, 256, synth.F16, False, 32, 0),
+    (16, 4096, 320, synth.BF16, False, 64, 0),
+    (7, 1024, 192, synth.F16, True, 64, 0),
+    (3, 8192, 128, synth.BF16, False, 32, 0),  # K past the split-K kernel's 32/64-group reach: tile kernel
+    (5, 512, 256, synth.BF16, True, 32, 2),    # small M forced onto the tile kernel
+    (16, 768, 128, synth.F16, False, 64, 2),
+    (17, 256, 64, synth.BF16, True, 32, 0),    # tile kernel, ragged row tile
+    (100, 1024, 576, synth.BF16, False, 32, 0),
+    (130, 512, 320, synth.F16, True, 64, 0),
+    (300, 768, 1024, synth.BF16, True, 64, 0),
+    (1000, 384, 4096, synth.F16, False, 32, 0),  # 32 x 256 tiles (many workgroups)
+])
+def test_small_scale_groups(orc, M, K, N, dt, signed, group, variant):
+    """Scale groups of 32 and 64 rows (weights in the group-aligned layout):
+    the split-K and tile kernels against the oracle at the same group."""
+    p = synth.make_dense(M, K, N, dt, signed=signed, seed=M + group + K, group=group)
+    _run_and_check(orc, p, f"group{group}_{M}x{K}x{N}", variant=variant)
+
+
+@pytest.mark.parametrize("M,group", [(1, 32), (16, 64), (64, 32)])
+def test_small_scale_groups_decode_shape(orc, M, group):
+    """The decode shape (K = 4096, N = 14336, bf16, zero points) with 32/64-row
+    scale groups, every output compared."""
+    p = synth.make_dense(M, 4096, 14336, synth.BF16, signed=False, seed=M, group=group)
+    _run_and_check(orc, p, f"decode_group{group}_m{M}")

@@ -79,3 +79,17 @@ def test_grouped_group_sizes(orc, group, dt, signed):
     p = synth.make_grouped(len(counts), sum(counts), 1, 1024, 320, dt, signed=signed, counts=counts,
                            seed=group, group=group)
     _check(orc, p, f"grouped_group{group}")
+
+
+@pytest.mark.parametrize("group,dt,signed,counts", [
+    (32, synth.BF16, True, [5, 0, 70, 33, 1, 129]),
+    (64, synth.F16, False, [200, 3, 0, 97]),
+    (32, synth.F16, False, [40] * 9),
+    (64, synth.BF16, True, [0, 0, 17]),
+])
+def test_grouped_small_scale_groups(orc, group, dt, signed, counts):
+    """Grouped GEMM with scale groups of 32 and 64 rows (group-aligned
+    weights): ragged experts, experts without rows, both tile shapes."""
+    p = synth.make_grouped(len(counts), sum(counts), 1, 1024, 320, dt, signed=signed, counts=counts,
+                           seed=group + len(counts), group=group)
+    _check(orc, p, f"grouped_group{group}_{counts[:4]}")

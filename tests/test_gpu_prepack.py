@@ -36,3 +36,23 @@ def test_prepack_full_size(orc, name):
     got = prepack(p).cpu().numpy()
     ref = orc.prepack(p.w.reshape(-1), p.E, p.K, p.N, p.signed)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("E,K,N,signed,group", [(1, 128, 64, True, 32), (2, 384, 192, False, 64),
+                                                (3, 256, 128, True, 64), (1, 4096, 14336, False, 32)])
+def test_prepack_group_aligned_bytes(orc, E, K, N, signed, group):
+    """w4a16_prepack_g with 32/64-row groups writes the group-aligned layout:
+    bytes equal to the oracle's statement of it; with a 128-multiple group
+    it writes the standard layout."""
+    import weight_only_quantized_amd as w4
+    from gpu_helpers import to_dev
+    print(f"[case] prepack_g E={E} K={K} N={N} signed={signed} group={group}", flush=True)
+    rng = np.random.default_rng(K + N + group)
+    w = rng.integers(0, 256, size=(E, K, N // 2), dtype=np.uint8)
+    out = torch.empty(E * K * N // 2, dtype=torch.uint8, device="cuda:0")
+    w4.w4a16_prepack_g(to_dev(w.reshape(-1)), out, E, K, N, int(signed), group)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), orc.prepack(w, E, K, N, signed, layout=1))
+    w4.w4a16_prepack_g(to_dev(w.reshape(-1)), out, E, K, N, int(signed), 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), orc.prepack(w, E, K, N, signed, layout=0))

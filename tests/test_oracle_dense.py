@@ -10,6 +10,10 @@
   integer activations with unit scales equal an int64 matmul; a unit row of x
   picks one dequantised weight row (pins nibble order, group index, scale and
   zero indexing); signed weights equal the unsigned encoding q+8 with zero 8.
+* Scale groups of 32, 64 and 256 rows (Humming article: the descriptor keeps
+  the scale granularity as a parameter): the unit-row probe at the group
+  edges, and integer activations with power-of-two scales per group equal an
+  int64 reduction (per-group int64 matmuls, each scaled exactly).
 """
 import numpy as np
 import pytest
@@ -155,3 +159,56 @@ def test_moe_routing_shape():
     assert p.M == 512 * 8 and p.offsets[-1] == p.M and p.E == 64
     counts = np.diff(p.offsets)
     assert counts.min() >= 0 and counts.max() > 4 * np.median(counts)   # skewed
+
+
+@pytest.mark.parametrize("group", [32, 64, 256])
+@pytest.mark.parametrize("signed", [False, True])
+def test_unit_row_probe_small_groups(orc, group, signed):
+    p = synth.make_dense(1, 512, 64, synth.F16, signed=signed, seed=11 + group, group=group)
+    K, N = p.K, p.N
+    s = synth.bits_to_f32(p.scale, p.dtype).astype(np.float64)
+    z = synth.unpack_nibbles(p.zero).astype(np.int64) if p.zero is not None else np.zeros((K // group, N), np.int64)
+    for k in sorted({0, 1, group - 1, group, group + 1, 2 * group - 1, 255, 256, 511}):
+        xk = np.zeros((1, K), np.float32)
+        xk[0, k] = 1.0
+        y64, _ = orc.w4a16(synth.to_bits(xk, p.dtype), p.w, p.scale, p.zero, 1, K, N, p.dtype, group=group)
+        g = k // group
+        expect = (p.q[k].astype(np.int64) - z[g]) * s[g]
+        assert np.array_equal(y64[0], expect), (group, k)
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_small_groups_integer_reduction(orc, group):
+    """Integer x, zero points, scales 2^e (e in [-3, 3]) per (group, column):
+    8 * y equals sum_g x_g . ((q - z)_g * 2^(e_g + 3)) in int64."""
+    M, K, N = 6, 384, 128
+    rng = np.random.default_rng(group)
+    G = K // group
+    xi = rng.integers(-30, 31, size=(M, K))
+    u = rng.integers(0, 16, size=(K, N))
+    zq = rng.integers(0, 16, size=(G, N))
+    e = rng.integers(-3, 4, size=(G, N))
+    for dt in (orc.F16, orc.BF16):
+        x = synth.to_bits(xi.astype(np.float32), dt)
+        s = synth.to_bits(np.exp2(e).astype(np.float32), dt)
+        y64, _ = orc.w4a16(x, synth.pack_nibbles(u.astype(np.uint8)), s, synth.pack_nibbles(zq.astype(np.uint8)),
+                           M, K, N, dt, group=group)
+        acc = np.zeros((M, N), np.int64)
+        for g in range(G):
+            rows = slice(g * group, (g + 1) * group)
+            wg = (u[rows] - zq[g]) * (2 ** (e[g] + 3))
+            acc += xi[:, rows].astype(np.int64) @ wg.astype(np.int64)
+        assert np.array_equal(y64 * 8, acc.astype(np.float64)), dt
+
+
+def test_grouped_small_groups_reduce_to_dense(orc):
+    counts = [7, 0, 33, 2]
+    p = synth.make_grouped(len(counts), 20, 2, 256, 128, synth.F16, counts=counts, seed=12, group=32)
+    y64, _ = orc.grouped(p.x, p.offsets, p.w, p.scale, None, p.E, p.M, p.K, p.N, p.dtype, group=32)
+    for ex, c in enumerate(counts):
+        r0, r1 = p.offsets[ex], p.offsets[ex + 1]
+        if c == 0:
+            continue
+        ye, _ = orc.w4a16(np.ascontiguousarray(p.x[r0:r1]), np.ascontiguousarray(p.w[ex]),
+                          np.ascontiguousarray(p.scale[ex]), None, c, p.K, p.N, p.dtype, group=32)
+        assert np.array_equal(y64[r0:r1], ye)

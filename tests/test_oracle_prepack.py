@@ -10,7 +10,12 @@ of the slot holds r = 8t + i with the code of row r at bit 4*(i//2) + 16*(i%2);
 codes are u (unsigned) or q+8 (signed).
 
 Pins: spot positions taken from that statement; a bijection over all bits;
-the round trip over every byte value at every position.
+the round trip over every byte value at every position.  The group-aligned
+layout (scale groups of 32 or 64 rows) exchanges the roles of the chunk
+c = L // 16 and the word t: word t of slot L holds rows 128*g + 32*t +
+8*(L//16) + i.  Its pins: its own spot positions, the round trip, and the
+statement that it is layout 0 with rows permuted inside each 32x32 block of
+(chunk, word) positions.
 """
 import numpy as np
 import pytest
@@ -88,3 +93,49 @@ def test_round_trip_all_byte_values(orc, signed):
         p = orc.prepack(w, E, K, N, signed)
         back = orc.unpack(p, E, K, N, signed)
         assert np.array_equal(back, w.reshape(-1))
+
+
+@pytest.mark.parametrize("k,n,byte,shift", [
+    (0, 0, 0, 0),        # slot 0, word 0, i=0
+    (1, 0, 2, 0),        # i=1 -> bit 16
+    (7, 0, 3, 4),        # i=7 -> bit 28
+    (8, 0, 256, 0),      # rows 8..15 of the 32-row block: chunk 1 -> slot 16, word 0
+    (16, 0, 512, 0),     # chunk 2 -> slot 32
+    (24, 0, 768, 0),     # chunk 3 -> slot 48
+    (32, 0, 4, 0),       # next 32-row block: word 1 of slot 0
+    (96, 0, 12, 0),      # word 3
+    (127, 15, 768 + 15 * 16 + 12 + 3, 4),  # chunk 3, column 15, word 3, i=7
+    (128, 0, 1024, 0),   # next 128-row block: next tile
+    (0, 16, 2 * 1024, 0),
+])
+def test_group_aligned_spot_positions(orc, k, n, byte, shift):
+    K, N = 256, 64
+    p = orc.prepack(_single(K, N, k, n, 0x5), 1, K, N, is_signed=False, layout=1)
+    nz = np.nonzero(p)[0]
+    assert list(nz) == [byte]
+    assert p[byte] == (0x5 << shift)
+
+
+@pytest.mark.parametrize("signed", [False, True])
+def test_group_aligned_round_trip(orc, signed):
+    E, K, N = 2, 384, 128
+    base = (np.arange(E * K * N // 2) % 251).astype(np.uint8)
+    w = base.reshape(E, K, N // 2)
+    p = orc.prepack(w, E, K, N, signed, layout=1)
+    assert np.array_equal(orc.unpack(p, E, K, N, signed, layout=1), w.reshape(-1))
+
+
+def test_group_aligned_is_a_row_permutation_of_layout0(orc):
+    """Layout 1 of W equals layout 0 of W with the rows of every 128-row block
+    permuted by k = 32t + 8c + i -> 32c + 8t + i."""
+    E, K, N = 1, 256, 64
+    codes = np.random.default_rng(4).integers(0, 16, size=(K, N)).astype(np.uint8)
+    perm = np.empty(K, np.int64)
+    for g in range(K // 128):
+        for t in range(4):
+            for c in range(4):
+                for i in range(8):
+                    perm[128 * g + 32 * c + 8 * t + i] = 128 * g + 32 * t + 8 * c + i
+    p1 = orc.prepack(synth.pack_nibbles(codes), E, K, N, False, layout=1)
+    p0 = orc.prepack(synth.pack_nibbles(codes[perm]), E, K, N, False, layout=0)
+    assert np.array_equal(p1, p0)

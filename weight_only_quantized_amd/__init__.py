@@ -44,6 +44,7 @@ _SIGS = {
     "w4a16_status_str": ([C.c_int], C.c_char_p),
     "w4a16_prepacked_bytes": ([_i64, _i64, _i64], C.c_size_t),
     "w4a16_prepack": ([_p, _p, _i64, _i64, _i64, C.c_int, _p], C.c_int),
+    "w4a16_prepack_g": ([_p, _p, _i64, _i64, _i64, C.c_int, _i64, _p], C.c_int),
     "w4a16_gemm": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, C.c_int, _p], C.c_int),
     "w4a16_msd_workspace_bytes": ([_i64, _i64, _i64, _i64], C.c_size_t),
     "w4a16_msd_gemm": ([_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, C.c_size_t, _p], C.c_int),
@@ -136,6 +137,11 @@ def w4a16_prepacked_bytes(E: int, K: int, N: int) -> int:
 
 def w4a16_prepack(w, w_packed, E, K, N, is_signed, stream=None):
     _check(lib().w4a16_prepack(_ptr(w), _ptr(w_packed), E, K, N, int(is_signed), _stream(stream)), "w4a16_prepack")
+
+
+def w4a16_prepack_g(w, w_packed, E, K, N, is_signed, group_size, stream=None):
+    _check(lib().w4a16_prepack_g(_ptr(w), _ptr(w_packed), E, K, N, int(is_signed), group_size, _stream(stream)),
+           "w4a16_prepack_g")
 
 
 def w4a16_gemm(x, w_packed, scale, zero, y, M, K, N, group_size=GROUP_SIZE, dt=W4A16_BF16, stream=None):

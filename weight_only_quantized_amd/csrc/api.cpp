@@ -63,6 +63,16 @@ w4a16_status check_kn_groups(int64_t K, int64_t N, int64_t group_size, int *gm) 
     return W4A16_OK;
 }
 
+// Scale groups of 32 or 64 rows (the group-aligned weight layout): *gr is the
+// group size; W4A16_ERR_UNSUPPORTED for other sizes below 128.
+w4a16_status check_kn_small_groups(int64_t K, int64_t N, int64_t group_size, int *gr) {
+    if (group_size != 32 && group_size != 64) return W4A16_ERR_UNSUPPORTED;
+    w4a16_status st = check_kn(K, N, 128);
+    if (st != W4A16_OK) return st;
+    *gr = (int)group_size;
+    return W4A16_OK;
+}
+
 // W4A8-MXFP4 shapes: K a multiple of 128 up to the small kernel's K limit,
 // N a multiple of 64.
 // The packed weights of one expert are addressed with 32-bit byte offsets.
@@ -115,7 +125,7 @@ const char *w4a16_status_str(int status) {
         case W4A16_OK: return "W4A16_OK";
         case W4A16_ERR_NULL: return "W4A16_ERR_NULL: a required pointer is NULL";
         case W4A16_ERR_SHAPE: return "W4A16_ERR_SHAPE: sizes violate K>0, K%128==0, N>0, N%64==0, M>=0, E>=1";
-        case W4A16_ERR_UNSUPPORTED: return "W4A16_ERR_UNSUPPORTED: group_size must be a multiple of 128 (MSD and the MoE chain: 128), dtype F16 or BF16 (MSD: F16)";
+        case W4A16_ERR_UNSUPPORTED: return "W4A16_ERR_UNSUPPORTED: group_size must be 32, 64 or a multiple of 128 (MSD and the MoE chain: 128; W8A16 and floating-point zero points: a multiple of 128), dtype F16 or BF16 (MSD: F16)";
         case W4A16_ERR_ALIGN: return "W4A16_ERR_ALIGN: x, w_packed, workspace need 16-byte, scale and y 2-byte alignment";
         case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE: MSD workspace is NULL or smaller than w4a16_msd_workspace_bytes()";
         case W4A16_ERR_DEVICE: return "W4A16_ERR_DEVICE: current device is not gfx950 or a launch failed";
@@ -142,11 +152,36 @@ w4a16_status w4a16_prepack(const void *w, void *w_packed, int64_t E, int64_t K, 
     return map_err(w4::launch_prepack(w, w_packed, E, K, N, is_signed ? 1 : 0, (hipStream_t)stream));
 }
 
+w4a16_status w4a16_prepack_g(const void *w, void *w_packed, int64_t E, int64_t K, int64_t N, int is_signed,
+                             int64_t group_size, void *stream) {
+    if (!w || !w_packed) return W4A16_ERR_NULL;
+    if (E < 1) return W4A16_ERR_SHAPE;
+    int layout = 0, gx = 1;
+    w4a16_status st = group_size < 128 ? check_kn_small_groups(K, N, group_size, &gx)
+                                       : check_kn_groups(K, N, group_size, &gx);
+    if (st != W4A16_OK) return st;
+    if (group_size < 128) layout = 1;
+    if (!aligned(w, 16) || !aligned(w_packed, 16)) return W4A16_ERR_ALIGN;
+    if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    return map_err(w4::launch_prepack(w, w_packed, E, K, N, is_signed ? 1 : 0, (hipStream_t)stream, layout));
+}
+
+// Dense call with 32- or 64-row scale groups (group-aligned weights).
+static w4a16_status gemm_small_groups(const void *x, const void *w_packed, const void *scale, const void *zero,
+                                      void *y, int64_t M, int64_t K, int64_t N, int gr, int dt, hipStream_t s,
+                                      const float *cs) {
+    const int forced = g_force_variant.load(std::memory_order_relaxed);
+    if (forced != 2 && M <= 16 && K <= w4::small_gs_max_k())
+        return map_err(w4::launch_gemm_small_gs(x, w_packed, scale, zero, y, M, K, N, dt, gr, s, cs));
+    return map_err(w4::launch_gemm_tile_gs(x, nullptr, w_packed, scale, zero, y, M, K, N, 1, dt, gr, s, cs));
+}
+
 w4a16_status w4a16_gemm(const void *x, const void *w_packed, const void *scale, const void *zero, void *y,
                         int64_t M, int64_t K, int64_t N, int64_t group_size, int dt, void *stream) {
     if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
-    int gm = 1;
-    w4a16_status st = check_kn_groups(K, N, group_size, &gm);
+    int gm = 1, gr = 0;
+    w4a16_status st = group_size < 128 ? check_kn_small_groups(K, N, group_size, &gr)
+                                       : check_kn_groups(K, N, group_size, &gm);
     if (st != W4A16_OK) return st;
     if (M < 0 || M > (int64_t(1) << 31) - 1) return W4A16_ERR_SHAPE;
     if (M == 0) return W4A16_OK;
@@ -155,6 +190,7 @@ w4a16_status w4a16_gemm(const void *x, const void *w_packed, const void *scale, 
         return W4A16_ERR_ALIGN;
     if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
     hipStream_t s = (hipStream_t)stream;
+    if (gr) return gemm_small_groups(x, w_packed, scale, zero, y, M, K, N, gr, dt, s, nullptr);
     if (pick_variant(M, K) == 1)
         return map_err(w4::launch_gemm_small(x, w_packed, scale, zero, y, M, K, N, dt, s, gm));
     return map_err(w4::launch_gemm_tile(x, nullptr, w_packed, scale, zero, y, M, K, N, 1, dt, s, nullptr, gm));
@@ -200,8 +236,9 @@ w4a16_status w4a16_grouped_gemm(const void *x, const int32_t *expert_offsets, co
                                 const void *scale, const void *zero, void *y, int64_t E, int64_t R, int64_t K,
                                 int64_t N, int64_t group_size, int dt, void *stream) {
     if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
-    int gm = 1;
-    w4a16_status st = check_kn_groups(K, N, group_size, &gm);
+    int gm = 1, gr = 0;
+    w4a16_status st = group_size < 128 ? check_kn_small_groups(K, N, group_size, &gr)
+                                       : check_kn_groups(K, N, group_size, &gm);
     if (st != W4A16_OK) return st;
     if (E < 1 || E > (int64_t(1) << 20) || R < 0 || R > (int64_t(1) << 31) - 1) return W4A16_ERR_SHAPE;
     if (R == 0) return W4A16_OK;
@@ -210,6 +247,9 @@ w4a16_status w4a16_grouped_gemm(const void *x, const int32_t *expert_offsets, co
         !aligned(expert_offsets, 4))
         return W4A16_ERR_ALIGN;
     if (current_device_ok() != 1) return W4A16_ERR_DEVICE;
+    if (gr)
+        return map_err(w4::launch_gemm_tile_gs(x, expert_offsets, w_packed, scale, zero, y, R, K, N, E, dt, gr,
+                                               (hipStream_t)stream));
     return map_err(w4::launch_gemm_tile(x, expert_offsets, w_packed, scale, zero, y, R, K, N, E, dt,
                                         (hipStream_t)stream, nullptr, gm));
 }
@@ -472,8 +512,11 @@ w4a16_status w4a16_gemm_desc(const void *x, const void *w_packed, const w4a16_we
     if ((desc->weight_bits != 4 && desc->weight_bits != 8) || (desc->zero_format != 0 && desc->zero_format != 1))
         return W4A16_ERR_UNSUPPORTED;
     if (dt != W4A16_F16 && dt != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
-    int gm = 1;
-    w4a16_status st = check_kn_groups(K, N, desc->group_size, &gm);
+    int gm = 1, gr = 0;
+    // 32/64-row scale groups: 4-bit weights with integer zero points (or none)
+    if (desc->group_size < 128 && (desc->weight_bits != 4 || desc->zero_format != 0)) return W4A16_ERR_UNSUPPORTED;
+    w4a16_status st = desc->group_size < 128 ? check_kn_small_groups(K, N, desc->group_size, &gr)
+                                             : check_kn_groups(K, N, desc->group_size, &gm);
     if (st != W4A16_OK) return st;
     if (M < 0 || M > (int64_t(1) << 31) - 1) return W4A16_ERR_SHAPE;
     if (M == 0) return W4A16_OK;
@@ -504,6 +547,7 @@ w4a16_status w4a16_gemm_desc(const void *x, const void *w_packed, const w4a16_we
         const bool small = forced != 2 && M <= kW8SmallMaxM && K <= w4::w8_small_max_k();
         return map_err(w4::launch_w8_gemm(x, w_packed, desc->scale, zero, y, M, K, N, dt, gm, small, s, cs, cz));
     }
+    if (gr) return gemm_small_groups(x, w_packed, desc->scale, zero, y, M, K, N, gr, dt, s, cs);
     if (pick_variant(M, K) == 1)
         return map_err(w4::launch_gemm_small(x, w_packed, desc->scale, zero, y, M, K, N, dt, s, gm, cs, cz));
     return map_err(w4::launch_gemm_tile(x, nullptr, w_packed, desc->scale, zero, y, M, K, N, 1, dt, s, nullptr,

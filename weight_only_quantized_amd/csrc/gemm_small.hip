@@ -39,6 +39,13 @@
 // wave then issues a single memory instruction, the 128-bit weight load, as
 // a buffer load whose tile offset is a scalar register (no per-load address
 // arithmetic in the vector ALU).
+//
+// Scale groups of 32 or 64 rows (GS = 32 or 64; weights in the group-aligned
+// layout, word t of slot L holding rows 32*t + 8*(L/16) + i): step t of a
+// tile then multiplies the 32 consecutive rows 32t .. 32t + 31, which lie in
+// one scale group, so each scale group's steps form their own chain and its
+// scale (and zero point) applies to that chain's fp32 sum.  Lane l's A operand
+// for step t is x[row][32t + 8*(l/16) + 0..7] accordingly.
 #include <atomic>
 
 #include "common.hpp"
@@ -52,7 +59,7 @@ constexpr int kSmallMaxWaves = 16;
 constexpr int kSmallMaxWaves2 = 8;
 
 // MT 16-row tiles of x share every dequantized weight operand.
-template <int DT, bool ZERO, int NB, int SG, int D, int MT = 1>
+template <int DT, bool ZERO, int NB, int SG, int D, int MT = 1, int GS = 0>
 __global__ void __launch_bounds__((MT == 1 ? kSmallMaxWaves : kSmallMaxWaves2) * 64)
 gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp,
                   const uint16_t *__restrict__ scale, const uint8_t *__restrict__ zero,
@@ -60,6 +67,9 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
                   const float *__restrict__ cz) {
     static_assert(NB == 1 || NB == 2 || NB == 4, "one 64-lane load covers the scales of <= 4 blocks");
     static_assert(MT == 1 || MT == 2, "one or two 16-row tiles");
+    static_assert(GS == 0 || GS == 32 || GS == 64, "standard layout, or 32/64-row scale groups");
+    constexpr int NSUB = GS ? kGroup / GS : 1;    // scale groups per 128-row tile
+    constexpr int TSUB = 4 / NSUB;                // matrix-core steps per scale group
     constexpr int T = NB * SG;                    // tiles per wave, ordered block-major
     const int G = (int)(K / kGroup);
     const int W = blockDim.x >> 6;
@@ -81,7 +91,7 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int jrow = m0 + 16 * mt + j < M ? m0 + 16 * mt + j : M - 1;
-        xoff[mt] = (uint32_t)((int64_t)jrow * K + 32 * kc) * 2u;
+        xoff[mt] = (uint32_t)((int64_t)jrow * K + (GS ? 8 : 32) * kc) * 2u;
     }
     // buffer resource over this workgroup's NB * G weight tiles (raw, 32-bit
     // data format; every offset below is in range)
@@ -97,7 +107,8 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) xa[i][mt][t] = ld128(xbase + (int64_t)g * (kGroup * 2) + xoff[mt] + 16 * t);
+            for (int t = 0; t < 4; ++t)
+                xa[i][mt][t] = ld128(xbase + (int64_t)g * (kGroup * 2) + xoff[mt] + (GS ? 64 : 16) * t);
     }
 
     // ---- scales and zero points: one load per group for all NB blocks -------
@@ -107,20 +118,23 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     // past the end of K (G not a multiple of SG) gets scale 0: its clamped,
     // finite tile then contributes nothing.
     constexpr uint32_t kBiasBase = DT == DT_BF16 ? 128u : 0u;
-    uint32_t sz[SG];
+    uint32_t sz[SG][NSUB];
     {
         const int cl = lane & (16 * NB - 1);
         const int64_t col = nb0 * 16 + cl;
 #pragma unroll
-        for (int i = 0; i < SG; ++i) {
-            const bool live = g0 + i < G;
-            const int g = live ? g0 + i : G - 1;
-            const int64_t gs = g / gm;                 // scale group (gm 128-row groups each)
-            const uint32_t sbits = scale[gs * N + col];
-            uint32_t zb = 8u;
-            if constexpr (ZERO) zb = __builtin_amdgcn_ubfe(zero[(gs * N + col) >> 1], (uint32_t)(cl & 1) * 4u, 4);
-            sz[i] = (live ? sbits : 0u) | (kBiasBase + zb) << 16;
-        }
+        for (int i = 0; i < SG; ++i)
+#pragma unroll
+            for (int h = 0; h < NSUB; ++h) {
+                const bool live = g0 + i < G;
+                const int g = live ? g0 + i : G - 1;
+                // scale group: gm 128-row tiles each, or NSUB per tile
+                const int64_t gs = GS ? (int64_t)g * NSUB + h : g / gm;
+                const uint32_t sbits = scale[gs * N + col];
+                uint32_t zb = 8u;
+                if constexpr (ZERO) zb = __builtin_amdgcn_ubfe(zero[(gs * N + col) >> 1], (uint32_t)(cl & 1) * 4u, 4);
+                sz[i][h] = (live ? sbits : 0u) | (kBiasBase + zb) << 16;
+            }
     }
 
     // ---- weight tile stream ---------------------------------------------------
@@ -137,18 +151,22 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
     // the same for every block, used as accumulator input) or, with zero
     // points, the row sums of x (B = 1.0 in every slot) that each tile scales
     // by its column's -(128 + z).
-    f32x4_t corr[SG][MT];
+    // (per scale group of the tile: one chain of TSUB steps each)
+    f32x4_t corr[SG][MT][NSUB];
     if constexpr (DT == DT_BF16) {
         const uint32_t c2 = ZERO ? 0x3F803F80u : bf16_negbias(8) * 0x10001u;
         const u32x4_t bc = {c2, c2, c2, c2};
 #pragma unroll
         for (int i = 0; i < SG; ++i)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                corr[i][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) corr[i][mt] = mfma16x16x32<DT>(xa[i][mt][t], bc, corr[i][mt]);
-            }
+                for (int h = 0; h < NSUB; ++h) {
+                    corr[i][mt][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = h * TSUB; t < (h + 1) * TSUB; ++t)
+                        corr[i][mt][h] = mfma16x16x32<DT>(xa[i][mt][t], bc, corr[i][mt][h]);
+                }
     }
 
     float yacc[NB][MT][4];
@@ -165,34 +183,37 @@ gemm_small_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp
         if (q + D < T) issue(q + D);
         __builtin_amdgcn_sched_barrier(0);
         const int b = q / SG, i = q % SG;
-        const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * b + j) << 2, (int)sz[i]);
-        f32x4_t acc[MT];
-        uint32_t nb2 = 0;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            if constexpr (DT == DT_BF16 && !ZERO) acc[mt] = corr[i][mt];
-            else acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        if constexpr (DT == DT_F16) nb2 = ZERO ? f16_negbias2(v >> 16) : f16_negbias2(8u);
+        for (int h = 0; h < NSUB; ++h) {
+            const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * b + j) << 2, (int)sz[i][h]);
+            f32x4_t acc[MT];
+            uint32_t nb2 = 0;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const u32x4_t wq = dequant_word<DT>(raw[q][t], nb2);
+            for (int mt = 0; mt < MT; ++mt) {
+                if constexpr (DT == DT_BF16 && !ZERO) acc[mt] = corr[i][mt][h];
+                else acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            if constexpr (DT == DT_F16) nb2 = ZERO ? f16_negbias2(v >> 16) : f16_negbias2(8u);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x32<DT>(xa[i][mt][t], wq, acc[mt]);
-        }
-        if constexpr (DT == DT_BF16 && ZERO) {
-            // 128 + z sits in byte 2: one byte-to-float conversion
-            const float nbias = -(float)((v >> 16) & 0xFFu);
+            for (int t = h * TSUB; t < (h + 1) * TSUB; ++t) {
+                const u32x4_t wq = dequant_word<DT>(raw[q][t], nb2);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x32<DT>(xa[i][mt][t], wq, acc[mt]);
+            }
+            if constexpr (DT == DT_BF16 && ZERO) {
+                // 128 + z sits in byte 2: one byte-to-float conversion
+                const float nbias = -(float)((v >> 16) & 0xFFu);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(nbias, corr[i][mt][h][r], acc[mt][r]);
+            }
+            const float sv = h2f<DT>((uint16_t)(v & 0xFFFFu));
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(nbias, corr[i][mt][r], acc[mt][r]);
+                for (int r = 0; r < 4; ++r) yacc[b][mt][r] += sv * acc[mt][r];
         }
-        const float sv = h2f<DT>((uint16_t)(v & 0xFFFFu));
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) yacc[b][mt][r] += sv * acc[mt][r];
     }
 
     // ---- reduce the waves' partial sums ---------------------------------------
@@ -229,14 +250,14 @@ int small_config_count() { return (int)(sizeof(kSmallCfgs) / sizeof(kSmallCfgs[0
 void set_small_config(int idx) { g_small_cfg.store(idx, std::memory_order_relaxed); }
 int64_t small_max_k() { return (int64_t)kSmallMaxWaves * 4 * kGroup; }
 
-template <int DT, bool ZERO, int NB, int SG, int D, int MT = 1>
+template <int DT, bool ZERO, int NB, int SG, int D, int MT = 1, int GS = 0>
 static hipError_t small_launch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
                                int64_t M, int64_t K, int64_t N, int gm, const float *cs, const float *cz,
                                hipStream_t stream) {
     const int64_t G = K / kGroup;
     const int64_t waves = (G + SG - 1) / SG;
     const dim3 grid((unsigned)(N / (16 * NB)), MT == 1 ? 1u : (unsigned)((M + 16 * MT - 1) / (16 * MT)));
-    hipLaunchKernelGGL((gemm_small_kernel<DT, ZERO, NB, SG, D, MT>), grid, dim3((unsigned)(waves * 64)), 0, stream,
+    hipLaunchKernelGGL((gemm_small_kernel<DT, ZERO, NB, SG, D, MT, GS>), grid, dim3((unsigned)(waves * 64)), 0, stream,
                        (const uint16_t *)x, (const uint8_t *)wp, (const uint16_t *)scale,
                        (const uint8_t *)zero, (uint16_t *)y, (int)M, K, N, gm, cs, cz);
     return hipGetLastError();
@@ -291,6 +312,41 @@ static hipError_t small2_dispatch(const void *x, const void *wp, const void *sca
     W4_SMALL2(4, 4, 8) W4_SMALL2(2, 4, 8) W4_SMALL2(4, 2, 8) W4_SMALL2(4, 1, 4) W4_SMALL2(1, 4, 4) W4_SMALL2(2, 2, 4)
     W4_SMALL2(1, 2, 2) W4_SMALL2(2, 1, 2) W4_SMALL2(1, 1, 1)
 #undef W4_SMALL2
+    return hipErrorInvalidValue;
+}
+
+// Scale groups of 32 or 64 rows (group-aligned weights): one 16-row tile,
+// K <= small_gs_max_k() (two groups per wave: with per-scale-group
+// correction sums the x slice, tiles and sums of a wave stay within the 128
+// registers a 16-wave workgroup allows), the default (NB, SG, D) by M; the
+// tuning hook does not apply.
+int64_t small_gs_max_k() { return (int64_t)kSmallMaxWaves * 2 * kGroup; }
+
+template <int DT, bool ZERO, int GS>
+static hipError_t small_gs_dispatch(const void *x, const void *wp, const void *scale, const void *zero, void *y,
+                                    int64_t M, int64_t K, int64_t N, const float *cs, const float *cz,
+                                    hipStream_t stream) {
+    if (M > 16 || K > small_gs_max_k()) return hipErrorInvalidValue;
+    if (M > 4) return small_launch<DT, ZERO, 4, 2, 8, 1, GS>(x, wp, scale, zero, y, M, K, N, 1, cs, cz, stream);
+    return small_launch<DT, ZERO, 4, 2, 4, 1, GS>(x, wp, scale, zero, y, M, K, N, 1, cs, cz, stream);
+}
+
+template <int GS>
+static hipError_t small_gs_dispatch_dt(const void *x, const void *wp, const void *scale, const void *zero, void *y,
+                                       int64_t M, int64_t K, int64_t N, int dt, const float *cs, const float *cz,
+                                       hipStream_t stream) {
+    if (dt == DT_BF16)
+        return zero ? small_gs_dispatch<DT_BF16, true, GS>(x, wp, scale, zero, y, M, K, N, cs, cz, stream)
+                    : small_gs_dispatch<DT_BF16, false, GS>(x, wp, scale, zero, y, M, K, N, cs, cz, stream);
+    return zero ? small_gs_dispatch<DT_F16, true, GS>(x, wp, scale, zero, y, M, K, N, cs, cz, stream)
+                : small_gs_dispatch<DT_F16, false, GS>(x, wp, scale, zero, y, M, K, N, cs, cz, stream);
+}
+
+hipError_t launch_gemm_small_gs(const void *x, const void *wp, const void *scale, const void *zero, void *y,
+                                int64_t M, int64_t K, int64_t N, int dt, int group_size, hipStream_t stream,
+                                const float *cs, const float *cz) {
+    if (group_size == 32) return small_gs_dispatch_dt<32>(x, wp, scale, zero, y, M, K, N, dt, cs, cz, stream);
+    if (group_size == 64) return small_gs_dispatch_dt<64>(x, wp, scale, zero, y, M, K, N, dt, cs, cz, stream);
     return hipErrorInvalidValue;
 }
 

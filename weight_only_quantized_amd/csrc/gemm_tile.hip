@@ -31,6 +31,14 @@
 // and k-block l / 32 (64 rows of the group: chunks 2*(l/32) and 2*(l/32)+1 of
 // the prepacked slot layout); result register r of lane l is row
 // 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+//  * Scale groups of 32 or 64 rows (GR = 32 or 64, weights in the
+//    group-aligned layout: word t of slot L holds rows 32*t + 8*(L/16) + i):
+//    step s (0..7) takes word s/2 of the lane's slot 2*(l/32) + s%2, i.e. rows
+//    32*(s/2) + 16*(l/32) + 8*(s%2) + i, so steps 2h and 2h+1 cover exactly the
+//    32 rows of block h.  Each scale group's steps form their own chain, whose
+//    fp32 sum takes that group's scale; for bf16 each chain starts from its
+//    own correction step, whose A operand holds the three bf16 limbs of every
+//    32/64-row block's row sum (limbs v of block h in k-slot 3h + v).
 #include <atomic>
 
 #include "common.hpp"
@@ -50,7 +58,7 @@ constexpr int kXcds = 8;
 // columns, and the epilogue stores a = silu(gate) * up with each input first
 // rounded to the activation dtype (as if the projection were stored and read
 // back), so the result equals that of the separate SiLU-and-multiply kernel.
-template <int DT, bool ZERO, int BM, int BN, int WM, int WN, bool GROUPED, bool SILU = false>
+template <int DT, bool ZERO, int BM, int BN, int WM, int WN, bool GROUPED, bool SILU = false, int GR = 0>
 __global__ void __launch_bounds__(WM * WN * 64, 2)
 gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
                  const int32_t *__restrict__ row_src, const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
@@ -67,6 +75,11 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     static_assert((BM * 16) % NT == 0, "x staging must divide evenly");
     static_assert(XP <= 16, "one row-sum split per lane");
     static_assert(!SILU || (GROUPED && CT == 2), "SiLU epilogue: grouped, gate and up tile per wave");
+    static_assert(GR == 0 || GR == 32 || GR == 64, "standard layout, or 32/64-row scale groups");
+    static_assert(GR == 0 || !SILU, "the fused-experts chain keeps 128-row groups");
+    constexpr int NSUB = GR ? kGroup / GR : 1;   // scale groups per 128-row tile
+    constexpr int SPS = 8 / NSUB;                // 32x32x16 steps per scale group
+    constexpr int CPS = GR / 8;                  // 16-byte x chunks per scale group (GR > 0)
     constexpr int BNO = SILU ? BN / 2 : BN;   // output columns per workgroup
     constexpr int TNO = SILU ? 32 : TN;       // output columns per wave
 
@@ -179,8 +192,9 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     const bool wave_cols = n0 + (int64_t)wn * TNO < NOUT;
     const int64_t wcol0 = wave_cols ? n0 + (int64_t)wn * TNO : NOUT - TNO;
 
-    // one scale (and zero) row per gm consecutive 128-row groups
-    const int64_t GS = G / gm;
+    // one scale (and zero) row per gm consecutive 128-row groups, or NSUB per
+    // 128-row group
+    const int64_t GS = GR ? (int64_t)G * NSUB : G / gm;
     const uint16_t *sc = scale + e * GS * N;
     const uint8_t *zp = ZERO ? zero + e * GS * (N / 2) : nullptr;
     const uint8_t *we = wp + e * NBLK * (int64_t)G * kTileBytes;
@@ -231,10 +245,18 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     v = __builtin_amdgcn_fdot2_f32_bf16(as<bf16x2_t>(xr[p][q]), ones, v, false);
-                ps[p] = row16_sum(v);
+                if constexpr (GR == 0) {
+                    ps[p] = row16_sum(v);
+                } else {
+                    // sum over the CPS lanes (chunks) of one 32/64-row block
+                    v += __shfl_xor(v, 1);
+                    v += __shfl_xor(v, 2);
+                    if constexpr (CPS == 8) v += __shfl_xor(v, 4);
+                    ps[p] = v;
+                }
             }
         }
-        if constexpr (CORR) {
+        if constexpr (CORR && GR == 0) {
             const int c16 = tid & 15;
             float mine = ps[0];
 #pragma unroll
@@ -246,10 +268,36 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
                 *reinterpret_cast<u32x4_t *>(base + r * ROWB + 256) = u32x4_t{hi | (mid << 16), lo, 0, 0};
             }
         }
+        if constexpr (CORR && GR != 0) {
+            // the first lane of each block stores its block's limbs: k-slots
+            // 3h, 3h + 1, 3h + 2 (bytes 256 + 6h ..)
+            const int c16 = tid & 15;
+            if (c16 % CPS == 0) {
+                const int h = c16 / CPS;
+#pragma unroll
+                for (int p = 0; p < XP; ++p) {
+                    const int r = (p * NT + tid) >> 4;
+                    uint32_t hi, mid, lo;
+                    split3_bf16(ps[p], hi, mid, lo);
+                    uint16_t *lp = reinterpret_cast<uint16_t *>(base + r * ROWB + 256 + 6 * h);
+                    lp[0] = (uint16_t)hi;
+                    lp[1] = (uint16_t)mid;
+                    lp[2] = (uint16_t)lo;
+                }
+            }
+        }
     };
     if constexpr (CORR) {
-        for (int r = tid; r < 2 * BM; r += NT)
-            *reinterpret_cast<u32x4_t *>(lds + r * ROWB + 272) = u32x4_t{0, 0, 0, 0};
+        // k-slots past the limbs read as zero: bytes 272.. (one sum) or
+        // 256 + 6 * NSUB .. 287 (per-block sums), written once
+        for (int r = tid; r < 2 * BM; r += NT) {
+            if constexpr (GR == 0) {
+                *reinterpret_cast<u32x4_t *>(lds + r * ROWB + 272) = u32x4_t{0, 0, 0, 0};
+            } else {
+                uint16_t *lp = reinterpret_cast<uint16_t *>(lds + r * ROWB + 256);
+                for (int k = 3 * NSUB; k < 16; ++k) lp[k] = 0;
+            }
+        }
     }
 
     // ---- weight fragments, scales and zero points -----------------------------
@@ -267,9 +315,9 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     // scales and zero points stay in their loaded 16/8-bit types: a mask of
     // the loaded value would be a use of the load, and the compiler may place
     // it right after the prefetch (forcing a wait for every load in flight)
-    uint16_t sraw[CT], snext[CT];
-    uint8_t zraw[CT], znext[CT];
-    auto load_b = [&](int g, u32x4_t (&dst)[CT][2], uint16_t (&sdst)[CT], uint8_t (&zdst)[CT]) {
+    uint16_t sraw[CT][NSUB], snext[CT][NSUB];
+    uint8_t zraw[CT][NSUB], znext[CT][NSUB];
+    auto load_b = [&](int g, u32x4_t (&dst)[CT][2], uint16_t (&sdst)[CT][NSUB], uint8_t (&zdst)[CT][NSUB]) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             const uint8_t *p = we + boff[ct] + (int64_t)g * kTileBytes;
@@ -279,9 +327,12 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             const int64_t n = wcol(ct);
-            const int64_t gs = g / gm;
-            sdst[ct] = sc[gs * N + n];
-            zdst[ct] = ZERO ? zp[(gs * N + n) >> 1] : (uint8_t)0;
+#pragma unroll
+            for (int h = 0; h < NSUB; ++h) {
+                const int64_t gs = GR ? (int64_t)g * NSUB + h : g / gm;
+                sdst[ct][h] = sc[gs * N + n];
+                zdst[ct][h] = ZERO ? zp[(gs * N + n) >> 1] : (uint8_t)0;
+            }
         }
     };
 
@@ -307,76 +358,107 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     // it (a register copy would wait for it at once).
     const int arow = wm * TM + lj;             // LDS row of this lane's A operand (row tile 0)
     constexpr int kStageStep = 4;              // k-step after which the next x slice is staged
-    auto step = [&](int g, const u32x4_t (&bw)[CT][2], const uint16_t (&sw)[CT], const uint8_t (&zw)[CT],
-                    u32x4_t (&bn)[CT][2], uint16_t (&sn)[CT], uint8_t (&zn)[CT]) {
+    auto step = [&](int g, const u32x4_t (&bw)[CT][2], const uint16_t (&sw)[CT][NSUB],
+                    const uint8_t (&zw)[CT][NSUB], u32x4_t (&bn)[CT][2], uint16_t (&sn)[CT][NSUB],
+                    uint8_t (&zn)[CT][NSUB]) {
         const int buf = g & 1;
         const int gn = g + 1 < G ? g + 1 : g;
         load_x(gn);
         load_b(gn, bn, sn, zn);
-        float s[CT];
-        uint32_t nb2[CT];
-        u32x4_t bcorr[CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            const int64_t n = wcol(ct);
-            s[ct] = h2f<DT>(sw[ct]);
-            uint32_t z = 8;
-            if constexpr (ZERO) z = __builtin_amdgcn_ubfe((uint32_t)zw[ct], (uint32_t)(n & 1) * 4u, 4);
-            if constexpr (CORR) {
-                const uint32_t c = bf16_negbias(z);
-                bcorr[ct] = kg == 0 ? u32x4_t{c | (c << 16), c, 0, 0} : u32x4_t{0, 0, 0, 0};
-                nb2[ct] = 0;
-            } else {
-                nb2[ct] = f16_negbias2(z);
-            }
-        }
-        const uint8_t *abase = lds + buf * BM * ROWB + arow * ROWB + kg * 128;
-        // accumulator inputs of the first step: the bias correction (bf16; one
-        // per row tile when every column has z = 8, else one per column tile)
-        // or zero.  Passing it as the matrix-core C input avoids copying one
-        // correction into several accumulators.
-        f32x16_t cin[RT][ZERO ? CT : 1];
+        const uint8_t *abase = lds + buf * BM * ROWB + arow * ROWB + (GR ? kg * 32 : kg * 128);
+        // A operand of the correction steps: the bf16 limbs of the rows' sums
+        u32x4_t alimb[RT];
         if constexpr (CORR) {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const u32x4_t a = *reinterpret_cast<const u32x4_t *>(
-                    lds + buf * BM * ROWB + (arow + rt * 32) * ROWB + 256 + kg * 16);
-#pragma unroll
-                for (int ci = 0; ci < (ZERO ? CT : 1); ++ci) cin[rt][ci] = mfma32x32x16<DT>(a, bcorr[ci], f32x16_t{});
-            }
+            for (int rt = 0; rt < RT; ++rt)
+                alimb[rt] = *reinterpret_cast<const u32x4_t *>(lds + buf * BM * ROWB + (arow + rt * 32) * ROWB + 256 +
+                                                               kg * 16);
         }
-        f32x16_t acc[RT][CT];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            u32x4_t a[RT], bq[CT];
+        for (int h = 0; h < NSUB; ++h) {
+            float s[CT];
+            uint32_t nb2[CT];
+            u32x4_t bcorr[CT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                a[rt] = *reinterpret_cast<const u32x4_t *>(abase + rt * 32 * ROWB + t * 16);
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) bq[ct] = dequant_word<DT>(bw[ct][t >> 2][t & 3], nb2[ct]);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    if (t == 0) {
-                        if constexpr (CORR) acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], cin[rt][ZERO ? ct : 0]);
-                        else acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], f32x16_t{});
+            for (int ct = 0; ct < CT; ++ct) {
+                const int64_t n = wcol(ct);
+                s[ct] = h2f<DT>(sw[ct][h]);
+                uint32_t z = 8;
+                if constexpr (ZERO) z = __builtin_amdgcn_ubfe((uint32_t)zw[ct][h], (uint32_t)(n & 1) * 4u, 4);
+                if constexpr (CORR) {
+                    const uint32_t c = bf16_negbias(z);
+                    if constexpr (GR == 0) {
+                        bcorr[ct] = kg == 0 ? u32x4_t{c | (c << 16), c, 0, 0} : u32x4_t{0, 0, 0, 0};
                     } else {
-                        acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], acc[rt][ct]);
+                        // c in k-slots 3h .. 3h + 2 only; this lane holds slots
+                        // 8*kg .. 8*kg + 7, two per word
+                        const uint32_t cc = c | (c << 16);
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            constexpr uint32_t lo16 = 0x0000FFFFu, hi16 = 0xFFFF0000u;
+                            auto msk = [&](int slot) -> uint32_t {
+                                return (slot >= 3 * h && slot < 3 * h + 3) ? ((slot & 1) ? hi16 : lo16) : 0u;
+                            };
+                            const uint32_t m0 = msk(2 * w) | msk(2 * w + 1);
+                            const uint32_t m1 = msk(8 + 2 * w) | msk(8 + 2 * w + 1);
+                            bcorr[ct][w] = cc & (kg == 0 ? m0 : m1);
+                        }
                     }
+                    nb2[ct] = 0;
+                } else {
+                    nb2[ct] = f16_negbias2(z);
                 }
-            // stage the next group's x slice halfway through the products: its
-            // vector work (row sums, limb split) then overlaps matrix-core
-            // steps.  The buffer written was last read in the previous step,
-            // before that step's barrier.
-            if (t == kStageStep) store_x(buf ^ 1);
+            }
+            // accumulator inputs of the first step: the bias correction (bf16; one
+            // per row tile when every column has z = 8, else one per column tile)
+            // or zero.  Passing it as the matrix-core C input avoids copying one
+            // correction into several accumulators.
+            f32x16_t cin[RT][ZERO ? CT : 1];
+            if constexpr (CORR) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int ci = 0; ci < (ZERO ? CT : 1); ++ci)
+                        cin[rt][ci] = mfma32x32x16<DT>(alimb[rt], bcorr[ci], f32x16_t{});
+            }
+            f32x16_t acc[RT][CT];
+#pragma unroll
+            for (int t = h * SPS; t < (h + 1) * SPS; ++t) {
+                u32x4_t a[RT], bq[CT];
+                // k offset of this step's operands: 8t (standard layout) or
+                // 32*(t/2) + 16*kg + 8*(t%2) (group-aligned; kg part in abase)
+                const int aoff = GR ? (t >> 1) * 64 + (t & 1) * 16 : t * 16;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    a[rt] = *reinterpret_cast<const u32x4_t *>(abase + rt * 32 * ROWB + aoff);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    bq[ct] = GR ? dequant_word<DT>(bw[ct][t & 1][t >> 1], nb2[ct])
+                                : dequant_word<DT>(bw[ct][t >> 2][t & 3], nb2[ct]);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        if (t == h * SPS) {
+                            if constexpr (CORR) acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], cin[rt][ZERO ? ct : 0]);
+                            else acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], f32x16_t{});
+                        } else {
+                            acc[rt][ct] = mfma32x32x16<DT>(a[rt], bq[ct], acc[rt][ct]);
+                        }
+                    }
+                // stage the next group's x slice halfway through the products: its
+                // vector work (row sums, limb split) then overlaps matrix-core
+                // steps.  The buffer written was last read in the previous step,
+                // before that step's barrier.
+                if (t == kStageStep) store_x(buf ^ 1);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) yacc[rt][ct][r] += s[ct] * acc[rt][ct][r];
         }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) yacc[rt][ct][r] += s[ct] * acc[rt][ct][r];
         __syncthreads();
     };
     for (int g = 0; g < G; g += 2) {
@@ -439,7 +521,7 @@ static std::atomic<int> g_tile_cfg{-1};      // -1: automatic
 int tile_config_count() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0])); }
 void set_tile_config(int idx) { g_tile_cfg.store(idx, std::memory_order_relaxed); }
 
-template <int DT, bool ZERO, bool GROUPED, int BM, int BN, int WM, int WN, bool SILU = false>
+template <int DT, bool ZERO, bool GROUPED, int BM, int BN, int WM, int WN, bool SILU = false, int GR = 0>
 static hipError_t tile_launch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
                               const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
                               int64_t E, int gm, const float *cs, const float *cz, hipStream_t stream) {
@@ -450,7 +532,7 @@ static hipError_t tile_launch(const void *x, const int32_t *offsets, const int32
     const int64_t slots = (mtiles * ncb + kXcds - 1) / kXcds * kXcds;
     if (GROUPED && slots > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid = GROUPED ? dim3((unsigned)slots) : dim3((unsigned)mtiles, (unsigned)ncb);
-    hipLaunchKernelGGL((gemm_tile_kernel<DT, ZERO, BM, BN, WM, WN, GROUPED, SILU>), grid, dim3(WM * WN * 64), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<DT, ZERO, BM, BN, WM, WN, GROUPED, SILU, GR>), grid, dim3(WM * WN * 64), 0,
                        stream, (const uint16_t *)x, offsets, row_src, (const uint8_t *)wp, (const uint16_t *)scale,
                        (const uint8_t *)zero, (uint16_t *)y, M, K, N, (int)E, gm, cs, cz);
     return hipGetLastError();
@@ -531,6 +613,47 @@ hipError_t launch_gemm_tile_silu(const void *x, const int32_t *offsets, const in
                     : tile_silu_dispatch<DT_BF16, false>(x, offsets, row_src, wp, scale, zero, a, M, K, N, E, stream);
     return zero ? tile_silu_dispatch<DT_F16, true>(x, offsets, row_src, wp, scale, zero, a, M, K, N, E, stream)
                 : tile_silu_dispatch<DT_F16, false>(x, offsets, row_src, wp, scale, zero, a, M, K, N, E, stream);
+}
+
+// Scale groups of 32 or 64 rows (group-aligned weights): 32-row wave tiles
+// (the per-scale-group chains and scales of 64-row wave tiles do not fit in
+// 256 registers), 32 x 128 while that gives at most 672 workgroups (or, for
+// grouped calls, experts average <= 96 rows), else 32 x 256; the tuning hook
+// does not apply.
+template <int DT, bool ZERO, bool GROUPED, int GR>
+static hipError_t tile_gs_dispatch(const void *x, const int32_t *offsets, const void *wp, const void *scale,
+                                   const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
+                                   const float *cs, const float *cz, hipStream_t stream) {
+    const bool narrow = GROUPED ? M / E <= 96 : (M + 31) / 32 * ((N + 127) / 128) <= 672;
+    if (narrow)
+        return tile_launch<DT, ZERO, GROUPED, 32, 128, 1, 4, false, GR>(x, offsets, nullptr, wp, scale, zero, y, M, K,
+                                                                        N, E, 1, cs, cz, stream);
+    return tile_launch<DT, ZERO, GROUPED, 32, 256, 1, 4, false, GR>(x, offsets, nullptr, wp, scale, zero, y, M, K, N,
+                                                                    E, 1, cs, cz, stream);
+}
+
+template <bool GROUPED, int GR>
+static hipError_t tile_gs_dispatch_dt(const void *x, const int32_t *offsets, const void *wp, const void *scale,
+                                      const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E, int dt,
+                                      const float *cs, const float *cz, hipStream_t stream) {
+    if (dt == DT_BF16)
+        return zero ? tile_gs_dispatch<DT_BF16, true, GROUPED, GR>(x, offsets, wp, scale, zero, y, M, K, N, E, cs, cz, stream)
+                    : tile_gs_dispatch<DT_BF16, false, GROUPED, GR>(x, offsets, wp, scale, zero, y, M, K, N, E, cs, cz, stream);
+    return zero ? tile_gs_dispatch<DT_F16, true, GROUPED, GR>(x, offsets, wp, scale, zero, y, M, K, N, E, cs, cz, stream)
+                : tile_gs_dispatch<DT_F16, false, GROUPED, GR>(x, offsets, wp, scale, zero, y, M, K, N, E, cs, cz, stream);
+}
+
+hipError_t launch_gemm_tile_gs(const void *x, const int32_t *offsets, const void *wp, const void *scale,
+                               const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E, int dt,
+                               int group_size, hipStream_t stream, const float *cs, const float *cz) {
+    if (offsets) {
+        if (group_size == 32) return tile_gs_dispatch_dt<true, 32>(x, offsets, wp, scale, zero, y, M, K, N, E, dt, cs, cz, stream);
+        if (group_size == 64) return tile_gs_dispatch_dt<true, 64>(x, offsets, wp, scale, zero, y, M, K, N, E, dt, cs, cz, stream);
+    } else {
+        if (group_size == 32) return tile_gs_dispatch_dt<false, 32>(x, nullptr, wp, scale, zero, y, M, K, N, 1, dt, cs, cz, stream);
+        if (group_size == 64) return tile_gs_dispatch_dt<false, 64>(x, nullptr, wp, scale, zero, y, M, K, N, 1, dt, cs, cz, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *wp, const void *scale,

@@ -9,10 +9,12 @@
 
 namespace w4 {
 
+// layout 0: the standard tile layout; 1: the group-aligned layout (scale
+// groups of 32 or 64 rows; see prepack.hip)
 hipError_t launch_prepack(const void *w, void *out, int64_t E, int64_t K, int64_t N, int is_signed,
-                          hipStream_t stream);
+                          hipStream_t stream, int layout = 0);
 hipError_t launch_unpack(const void *in, void *w, int64_t E, int64_t K, int64_t N, int is_signed,
-                         hipStream_t stream);
+                         hipStream_t stream, int layout = 0);
 
 // Small-M split-K kernel (M <= 16, K <= small_max_k()).
 int small_config_count();
@@ -27,6 +29,13 @@ hipError_t launch_gemm_small(const void *x, const void *wp, const void *scale, c
                              int64_t M, int64_t K, int64_t N, int dt, hipStream_t stream, int gm = 1,
                              const float *cs = nullptr, const float *cz = nullptr);
 
+// Scale groups of 32 or 64 rows (weights prepacked in the group-aligned
+// layout): M <= 16 and K <= small_gs_max_k().
+int64_t small_gs_max_k();
+hipError_t launch_gemm_small_gs(const void *x, const void *wp, const void *scale, const void *zero, void *y,
+                                int64_t M, int64_t K, int64_t N, int dt, int group_size, hipStream_t stream,
+                                const float *cs = nullptr, const float *cz = nullptr);
+
 // LDS-staged tile kernel; grouped when offsets != nullptr (then M = R rows).
 // With row_src, row r of the product reads x row row_src[r] (gathered load).
 int tile_config_count();
@@ -35,6 +44,11 @@ hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *w
                             const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
                             int dt, hipStream_t stream, const int32_t *row_src = nullptr, int gm = 1,
                             const float *cs = nullptr, const float *cz = nullptr);
+// The tile kernel for scale groups of 32 or 64 rows (group-aligned weights).
+hipError_t launch_gemm_tile_gs(const void *x, const int32_t *offsets, const void *wp, const void *scale,
+                               const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E, int dt,
+                               int group_size, hipStream_t stream, const float *cs = nullptr,
+                               const float *cz = nullptr);
 // Grouped gate/up projection (N = 2 * I weight columns) with the
 // SiLU-and-multiply epilogue, a [M][I]; hipErrorNotSupported for tile shapes
 // without a gate/up pair per wave.

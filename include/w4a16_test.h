@@ -67,6 +67,16 @@ int w4a16_test_small_config(int idx);
 int w4a16_test_tile_config(int idx);
 
 /*
+ * Half items of the grouped tile kernel (32-row tiles of four waves): with
+ * enable = 0, subsequent grouped calls run every item over the whole K range
+ * in one wave per column tile, so every output is accumulated in the same
+ * order under every tile configuration; enable = 1 restores the default
+ * (the item plan may split an item's K range between two wave pairs).
+ * Tuning and tests only; not thread-safe.  Returns the previous setting.
+ */
+int w4a16_test_tile_halves(int enable);
+
+/*
  * Select the configuration (row tiles per workgroup, column blocks per wave,
  * waves) of the MSD product kernel for subsequent calls: idx in [0, count), or
  * -1 for the default.  w4a16_msd_workspace_bytes() covers every configuration.

@@ -23,6 +23,32 @@ def test_moe_full(orc):
     _check(orc, synth.moe(), "moe")
 
 
+@pytest.mark.parametrize("halves", [0, 1])
+def test_moe_full_half_items_on_off(orc, halves):
+    """The MoE workload with the grouped kernel's half items (K range split
+    between two wave pairs) turned off and on."""
+    import weight_only_quantized_amd as w4
+    prev = w4.w4a16_test_tile_halves(halves)
+    try:
+        _check(orc, synth.moe(), f"moe halves={halves}")
+    finally:
+        w4.w4a16_test_tile_halves(prev)
+
+
+@pytest.mark.parametrize("counts,K,N", [
+    ([3, 0, 40, 1, 65], 384, 320),     # odd group count: the second half runs one empty step
+    ([64] * 3 + [0, 7], 128, 192),     # one group: the second half has no groups
+    ([33, 31, 2], 1408, 1408),         # the MoE down projection's K and N
+])
+def test_half_items_shapes(orc, counts, K, N):
+    """Few items: the plan turns whole items into half items (every item fits
+    in one round as halves), with odd and single group counts and natural
+    half column blocks."""
+    p = synth.make_grouped(len(counts), sum(counts), 1, K, N, synth.BF16, signed=True, counts=counts,
+                           seed=K + N)
+    _check(orc, p, f"grouped_half_{counts[:4]}_{K}_{N}")
+
+
 @pytest.mark.parametrize("counts,dt,signed", [
     ([5, 0, 17, 1, 0, 9], synth.BF16, True),
     ([0, 0, 0, 40], synth.BF16, False),

@@ -208,14 +208,16 @@ def test_silu_epilogue_equals_separate_kernel(cfg):
     configurations 0 and 2: a gate and an up tile per wave) against the same
     chain through the stored projection and the separate kernel
     (configuration 4, one column tile per wave): bit for bit, since both round
-    the projection to the dtype before the same fp32 SiLU and product, and every
-    tile configuration accumulates each output in the same order."""
+    the projection to the dtype before the same fp32 SiLU and product, and with
+    half items off every tile configuration accumulates each output in the same
+    order."""
     import weight_only_quantized_amd as w4
     from gpu_helpers import to_host_u16
     k = dict(CHAINS[4])
     c = synth.make_moe_chain(seed=9, **k)
     print(f"[case] silu epilogue cfg={cfg} vs separate kernel {CHAINS[4]}", flush=True)
     d = DevChain(c)
+    prev = w4.w4a16_test_tile_halves(0)
     try:
         w4.w4a16_test_tile_config(cfg)
         fused = to_host_u16(d.run())
@@ -223,4 +225,23 @@ def test_silu_epilogue_equals_separate_kernel(cfg):
         separate = to_host_u16(d.run())
     finally:
         w4.w4a16_test_tile_config(-1)
+        w4.w4a16_test_tile_halves(prev)
     assert np.array_equal(fused, separate)
+
+
+@pytest.mark.parametrize("halves", [0, 1])
+def test_fused_moe_full_half_items(orc, halves):
+    """The benchmark-size chain with half items on and off: both within the
+    bar against the oracle's steps (the gate/up projection's plan splits some
+    items' K range between two wave pairs when they are on)."""
+    import weight_only_quantized_amd as w4
+    from gpu_helpers import check_tol, to_host_u16
+    c = synth.moe_chain()
+    print(f"[case] fused_moe full halves={halves}", flush=True)
+    prev = w4.w4a16_test_tile_halves(halves)
+    try:
+        out = to_host_u16(DevChain(c).run())
+        torch.cuda.synchronize()
+    finally:
+        w4.w4a16_test_tile_halves(prev)
+    check_tol(out, orc.fused_moe_steps(c), c.dtype, label=f"fused_moe_full halves={halves}")

@@ -79,6 +79,7 @@ _SIGS = {
     "w4a16_test_variant_name": ([_i64, _i64, _i64, C.c_int, C.c_int], C.c_char_p),
     "w4a16_test_small_config": ([C.c_int], C.c_int),
     "w4a16_test_tile_config": ([C.c_int], C.c_int),
+    "w4a16_test_tile_halves": ([C.c_int], C.c_int),
     "w4a16_test_msd_config": ([C.c_int], C.c_int),
     "w4a16_test_mx_small_config": ([C.c_int], C.c_int),
     "w4a16_test_mx_tile_config": ([C.c_int], C.c_int),
@@ -311,6 +312,10 @@ def w4a16_test_small_config(idx: int) -> int:
 
 def w4a16_test_tile_config(idx: int) -> int:
     return lib().w4a16_test_tile_config(int(idx))
+
+
+def w4a16_test_tile_halves(enable: int) -> int:
+    return lib().w4a16_test_tile_halves(int(enable))
 
 
 def w4a16_test_msd_config(idx: int) -> int:

@@ -419,6 +419,8 @@ int w4a16_test_tile_config(int idx) {
     return w4::tile_config_count();
 }
 
+int w4a16_test_tile_halves(int enable) { return w4::set_tile_halves(enable); }
+
 int w4a16_test_msd_config(int idx) {
     w4::set_msd_config(idx);
     return w4::msd_config_count();

@@ -49,143 +49,55 @@ namespace w4 {
 // XCDs of an MI355X; workgroups are dispatched to them round-robin.
 constexpr int kXcds = 8;
 
-// At least two waves per SIMD: two resident workgroups of four waves (or one
-// of eight) per compute unit, each wave within 256 registers.
-//
-// SILU (grouped, two 32-column tiles per wave): the weights hold 2 * NOUT
-// columns, gate then up (the fused-experts gate/up projection); a wave's two
-// tiles are gate columns c and up columns NOUT + c of the same 32 output
-// columns, and the epilogue stores a = silu(gate) * up with each input first
-// rounded to the activation dtype (as if the projection were stored and read
-// back), so the result equals that of the separate SiLU-and-multiply kernel.
-template <int DT, bool ZERO, int BM, int BN, int WM, int WN, bool GROUPED, bool SILU = false, int GR = 0>
-__global__ void __launch_bounds__(WM * WN * 64, 2)
-gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
-                 const int32_t *__restrict__ row_src, const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
-                 const uint8_t *__restrict__ zero, uint16_t *__restrict__ y,
-                 int64_t M, int64_t K, int64_t N, int E, int gm, const float *__restrict__ cs,
-                 const float *__restrict__ cz) {
+// LDS row stride (bytes) of the staged x slice
+constexpr int tile_rowb(int dt) { return (kGroup + (dt == DT_BF16 ? 16 : 0)) * 2 + 16; }
+
+// The work of one workgroup item: a BM x BN tile (BM x BN/2 outputs with the
+// SiLU epilogue) over the K groups of this wave's share.  KS = 1: the four (or
+// WM x WN) waves split the columns and run every group.  KS = 2 (a "half
+// item"): waves 0-1 and 2-3 are two sub-workgroups over the same BN/2 columns,
+// each over one half of the groups with its own x buffers; the halves meet at
+// every barrier (the shorter half runs one empty step when the group count is
+// odd) and their sums are added in LDS at the end.
+template <int DT, bool ZERO, int BM, int BN, int WM, int WN, bool GROUPED, bool SILU, int GR, int KS>
+__device__ __forceinline__ void tile_body(const uint16_t *__restrict__ x, const int32_t *__restrict__ row_src,
+                                          const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
+                                          const uint8_t *__restrict__ zero, uint16_t *__restrict__ y, int64_t K,
+                                          int64_t N, int gm, const float *__restrict__ cs,
+                                          const float *__restrict__ cz, uint8_t *lds_all, int64_t row0,
+                                          int64_t row_end, int64_t n0, int64_t e, int wm, int wn, int kh) {
     constexpr int NT = WM * WN * 64;
+    constexpr int NTS = NT / KS;                                // threads staging one x slice
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int RT = TM / 32, CT = TN / 32;
     constexpr bool CORR = DT == DT_BF16;
-    constexpr int ROWB = (kGroup + (CORR ? 16 : 0)) * 2 + 16;   // LDS row stride (bytes)
-    constexpr int XP = BM * 16 / NT;                            // 16-byte x chunks per thread
+    constexpr int ROWB = tile_rowb(DT);                         // LDS row stride (bytes)
+    constexpr int XP = BM * 16 / NTS;                           // 16-byte x chunks per thread
+    static_assert(KS == 1 || KS == 2, "whole items or K halves");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-    static_assert((BM * 16) % NT == 0, "x staging must divide evenly");
+    static_assert((BM * 16) % NTS == 0, "x staging must divide evenly");
     static_assert(XP <= 16, "one row-sum split per lane");
     static_assert(!SILU || (GROUPED && CT == 2), "SiLU epilogue: grouped, gate and up tile per wave");
     static_assert(GR == 0 || GR == 32 || GR == 64, "standard layout, or 32/64-row scale groups");
     static_assert(GR == 0 || !SILU, "the fused-experts chain keeps 128-row groups");
+    static_assert(KS == 1 || GR == 0, "K halves use the standard layout");
     constexpr int NSUB = GR ? kGroup / GR : 1;   // scale groups per 128-row tile
     constexpr int SPS = 8 / NSUB;                // 32x32x16 steps per scale group
     constexpr int CPS = GR / 8;                  // 16-byte x chunks per scale group (GR > 0)
-    constexpr int BNO = SILU ? BN / 2 : BN;   // output columns per workgroup
-    constexpr int TNO = SILU ? 32 : TN;       // output columns per wave
+    constexpr int TNO = SILU ? 32 : TN;          // output columns per wave
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BM * ROWB];
-
-    // the wave index is uniform (readfirstlane: values derived from it stay
-    // in scalar registers)
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
+    const int stid = tid % NTS;                  // thread index within this sub-workgroup
+    uint8_t *lds = lds_all + kh * 2 * BM * ROWB;
     const int G = (int)(K / kGroup);
     const int64_t NBLK = N / 16;
-    const int64_t NOUT = SILU ? N / 2 : N;    // output columns (row stride of y)
-
-    int64_t row0, row_end, n0;
-    int64_t e = 0;
-    if constexpr (GROUPED) {
-        __shared__ int s_info[3];
-        __shared__ int scan[NT];
-        auto tiles_of = [&](int ee) {
-            const int cnt = ee < E ? offsets[ee + 1] - offsets[ee] : 0;
-            return cnt > 0 ? (cnt + BM - 1) / BM : 0;
-        };
-        // this workgroup's item: slot bid / 8 of XCD bid % 8's contiguous range
-        // of (row tile, column block) items
-        const int64_t ncb = (NOUT + BNO - 1) / BNO;
-        const int64_t bid = blockIdx.x, xcd = bid % kXcds;
-        int64_t item, last;
-        if (E <= 64) {
-            // one wave: inclusive scan of the experts' row tiles over its
-            // lanes, then the expert holding this item's row tile
-            if (wave == 0) {
-                const int tl = tiles_of(lane);
-                int incl = tl;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const int v = __shfl_up(incl, off);
-                    if (lane >= off) incl += v;
-                }
-                const int64_t total = __shfl(incl, 63);
-                const int64_t items = total * ncb;
-                const int64_t it = items * xcd / kXcds + bid / kXcds;
-                const int tile = (int)(it / ncb);
-                if (lane == 0) {
-                    s_info[0] = -1;
-                    s_info[2] = (int)total;
-                }
-                if (it < items * (xcd + 1) / kXcds && lane < E && tile >= incl - tl && tile < incl) {
-                    s_info[0] = lane;
-                    s_info[1] = tile - (incl - tl);
-                }
-            }
-            __syncthreads();
-            const int64_t items = (int64_t)s_info[2] * ncb;
-            item = items * xcd / kXcds + bid / kXcds;
-            last = items * (xcd + 1) / kXcds;
-            if (item >= last) return;   // uniform: surplus workgroup
-        } else {
-        // total row tiles over all experts
-        if (tid == 0) {
-            s_info[0] = -1;
-            s_info[2] = 0;
-        }
-        __syncthreads();
-        int part = 0;
-        for (int ee = tid; ee < E; ee += NT) part += tiles_of(ee);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
-        if (lane == 0) atomicAdd(&s_info[2], part);
-        __syncthreads();
-        const int64_t items = (int64_t)s_info[2] * ncb;
-        item = items * xcd / kXcds + bid / kXcds;
-        last = items * (xcd + 1) / kXcds;
-        if (item >= last) return;   // uniform: surplus workgroup
-        const int tile = (int)(item / ncb);
-        // expert and row tile within it (block-wide inclusive scan per chunk)
-        int carry = 0;
-        for (int base = 0; base < E; base += NT) {
-            const int ee = base + tid;
-            const int tl = tiles_of(ee);
-            scan[tid] = tl;
-            __syncthreads();
-            for (int off = 1; off < NT; off <<= 1) {
-                const int v = tid >= off ? scan[tid - off] : 0;
-                __syncthreads();
-                scan[tid] += v;
-                __syncthreads();
-            }
-            const int incl = scan[tid] + carry, excl = incl - tl;
-            if (ee < E && tile >= excl && tile < incl) {
-                s_info[0] = ee;
-                s_info[1] = tile - excl;
-            }
-            carry += scan[NT - 1];
-            __syncthreads();
-        }
-        }
-        n0 = (item % ncb) * BNO;
-        e = s_info[0];   // always found: tile < total row tiles
-        row0 = offsets[e] + (int64_t)s_info[1] * BM;
-        row_end = offsets[e + 1] < M ? offsets[e + 1] : M;   // offsets[E] == R by contract
-    } else {
-        row0 = (int64_t)blockIdx.x * BM;
-        row_end = M;
-        n0 = (int64_t)blockIdx.y * BN;
-    }
+    const int64_t NOUT = SILU ? N / 2 : N;       // output columns (row stride of y)
+    // this wave's groups: [gb, ge), nsteps steps (equal for both K halves)
+    const int nsteps = KS == 1 ? G : (G + 1) / 2;
+    const int gb = kh * nsteps, ge = gb + nsteps < G ? gb + nsteps : G;
+    // any group index past the share re-reads its last group (or, for an empty
+    // share, the last group of K): loads stay in bounds and unconditional
+    auto gclamp = [&](int g) { return g < ge ? g : (ge > gb ? ge - 1 : G - 1); };
     // A wave whose columns lie past N (N % 64 == 0, so a wave's columns are all
     // in or all out) still runs the loop on the last columns, with every load
     // in bounds, and stores nothing: no branch around any load in the loop.
@@ -209,7 +121,7 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     const uint16_t *xrow[XP];
 #pragma unroll
     for (int p = 0; p < XP; ++p) {
-        const int id = p * NT + tid, r = id >> 4, c16 = id & 15;
+        const int id = p * NTS + stid, r = id >> 4, c16 = id & 15;
         const int64_t grow = row0 + r < row_end ? row0 + r : row_end - 1;
         const int64_t src = row_src ? (int64_t)row_src[grow] : grow;
         xrow[p] = x + src * K + c16 * 8;
@@ -237,7 +149,7 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
         float ps[XP];
 #pragma unroll
         for (int p = 0; p < XP; ++p) {
-            const int id = p * NT + tid, r = id >> 4, c16 = id & 15;
+            const int id = p * NTS + stid, r = id >> 4, c16 = id & 15;
             *reinterpret_cast<u32x4_t *>(base + r * ROWB + c16 * 16) = xr[p];
             if constexpr (CORR) {
                 const bf16x2_t ones = as<bf16x2_t>(0x3F803F80u);
@@ -257,26 +169,26 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
             }
         }
         if constexpr (CORR && GR == 0) {
-            const int c16 = tid & 15;
+            const int c16 = stid & 15;
             float mine = ps[0];
 #pragma unroll
             for (int p = 1; p < XP; ++p) mine = c16 == p ? ps[p] : mine;
             uint32_t hi, mid, lo;
             split3_bf16(mine, hi, mid, lo);
             if (c16 < XP) {
-                const int r = (c16 * NT + tid) >> 4;
+                const int r = (c16 * NTS + stid) >> 4;
                 *reinterpret_cast<u32x4_t *>(base + r * ROWB + 256) = u32x4_t{hi | (mid << 16), lo, 0, 0};
             }
         }
         if constexpr (CORR && GR != 0) {
             // the first lane of each block stores its block's limbs: k-slots
             // 3h, 3h + 1, 3h + 2 (bytes 256 + 6h ..)
-            const int c16 = tid & 15;
+            const int c16 = stid & 15;
             if (c16 % CPS == 0) {
                 const int h = c16 / CPS;
 #pragma unroll
                 for (int p = 0; p < XP; ++p) {
-                    const int r = (p * NT + tid) >> 4;
+                    const int r = (p * NTS + stid) >> 4;
                     uint32_t hi, mid, lo;
                     split3_bf16(ps[p], hi, mid, lo);
                     uint16_t *lp = reinterpret_cast<uint16_t *>(base + r * ROWB + 256 + 6 * h);
@@ -290,7 +202,7 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     if constexpr (CORR) {
         // k-slots past the limbs read as zero: bytes 272.. (one sum) or
         // 256 + 6 * NSUB .. 287 (per-block sums), written once
-        for (int r = tid; r < 2 * BM; r += NT) {
+        for (int r = stid; r < 2 * BM; r += NTS) {
             if constexpr (GR == 0) {
                 *reinterpret_cast<u32x4_t *>(lds + r * ROWB + 272) = u32x4_t{0, 0, 0, 0};
             } else {
@@ -344,8 +256,8 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
 #pragma unroll
             for (int r = 0; r < 16; ++r) yacc[rt][ct][r] = 0.f;
 
-    load_x(0);
-    load_b(0, braw, sraw, zraw);
+    load_x(gclamp(gb));
+    load_b(gclamp(gb), braw, sraw, zraw);
     store_x(0);
     __syncthreads();
 
@@ -358,11 +270,12 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     // it (a register copy would wait for it at once).
     const int arow = wm * TM + lj;             // LDS row of this lane's A operand (row tile 0)
     constexpr int kStageStep = 4;              // k-step after which the next x slice is staged
-    auto step = [&](int g, const u32x4_t (&bw)[CT][2], const uint16_t (&sw)[CT][NSUB],
+    auto step = [&](int gi, const u32x4_t (&bw)[CT][2], const uint16_t (&sw)[CT][NSUB],
                     const uint8_t (&zw)[CT][NSUB], u32x4_t (&bn)[CT][2], uint16_t (&sn)[CT][NSUB],
                     uint8_t (&zn)[CT][NSUB]) {
-        const int buf = g & 1;
-        const int gn = g + 1 < G ? g + 1 : g;
+        const int buf = gi & 1;
+        const bool valid = gb + gi < ge;           // uniform: the shorter K half's last step is empty
+        const int gn = gclamp(gb + gi + 1);
         load_x(gn);
         load_b(gn, bn, sn, zn);
         const uint8_t *abase = lds + buf * BM * ROWB + arow * ROWB + (GR ? kg * 32 : kg * 128);
@@ -452,18 +365,52 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
                 // before that step's barrier.
                 if (t == kStageStep) store_x(buf ^ 1);
             }
+            if (valid) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) yacc[rt][ct][r] += s[ct] * acc[rt][ct][r];
+            }
+        }
+        __syncthreads();
+    };
+    for (int gi = 0; gi < nsteps; gi += 2) {
+        step(gi, braw, sraw, zraw, bnext, snext, znext);
+        if (gi + 1 < nsteps) step(gi + 1, bnext, snext, znext, braw, sraw, zraw);
+    }
+
+    if constexpr (KS == 2) {
+        // sum of the two K halves, in LDS (the x buffers are free: every wave
+        // has passed the barrier after its last read of them): the second
+        // half's waves store their sums, the first half's waves add them in
+        // a fixed order and run the epilogue
+        float *red = reinterpret_cast<float *>(lds_all);
+        auto slot = [&](int rt, int ct, int q) { return red + ((((wn * RT + rt) * CT + ct) * 4 + q) * 64 + lane) * 4; };
+        if (kh == 1) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) yacc[rt][ct][r] += s[ct] * acc[rt][ct][r];
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<f32x4_t *>(slot(rt, ct, q)) =
+                            f32x4_t{yacc[rt][ct][4 * q], yacc[rt][ct][4 * q + 1], yacc[rt][ct][4 * q + 2],
+                                    yacc[rt][ct][4 * q + 3]};
         }
         __syncthreads();
-    };
-    for (int g = 0; g < G; g += 2) {
-        step(g, braw, sraw, zraw, bnext, snext, znext);
-        if (g + 1 < G) step(g + 1, bnext, snext, znext, braw, sraw, zraw);
+        if (kh == 1) return;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4_t v = *reinterpret_cast<const f32x4_t *>(slot(rt, ct, q));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) yacc[rt][ct][4 * q + i] += v[i];
+                }
     }
 
     if (!wave_cols) return;
@@ -502,6 +449,209 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
         }
 }
 
+// Half items (grouped 32 x 256 tiles, four waves of 32 x 64): the planner
+// below may split an item's K range between two wave pairs, each over half
+// the item's columns, so that a half item takes about half the time of a
+// whole one.  The hardware keeps a fixed number of workgroups resident (three
+// per compute unit for these tiles); when the whole items overrun a round by
+// a few, the rest of the machine would otherwise idle through a second round.
+template <int BM, int WM, int WN, bool GROUPED, int GR>
+constexpr bool tile_half_ok() {
+    return GROUPED && GR == 0 && BM == 32 && WM == 1 && WN == 4;
+}
+
+// Finishing time, in half-item durations, of F whole and H half items
+// dispatched in that order onto S slots (each whole item two units).
+__device__ __forceinline__ int64_t tile_makespan(int64_t F, int64_t H, int64_t S) {
+    const int64_t q = F / S, r = F % S;
+    if (r == 0) return 2 * q + (H + S - 1) / S;
+    const int64_t rem = H - 2 * (S - r);       // halves the partly used round cannot take
+    return 2 * q + 2 + (rem > 0 ? (rem + S - 1) / S : 0);
+}
+
+struct TileItem {
+    int64_t tile, ncol;   // global row tile, first output column
+    int half, valid;
+};
+
+// Item k (dispatch order) of XCD xcd.  XCD x owns the contiguous row tiles
+// [T*x/8, T*(x+1)/8) with all their column blocks, so an expert's row tiles
+// share one L2 (two where the boundary splits it).  Its list holds the whole
+// items first, in (row tile, column block) order, then the half items: the
+// two halves of each of the last c whole items (c chosen to shorten the
+// finishing time on S resident slots per XCD, else 0), then the last column
+// block of every row tile when it spans at most half a block.  Every output
+// column of every row tile is covered exactly once.
+__device__ __forceinline__ TileItem tile_plan(int64_t T, int64_t xcd, int64_t k, int64_t ncb, int64_t bno,
+                                              int64_t nout, int64_t S, bool halfok) {
+    TileItem it{0, 0, 0, 0};
+    const int64_t t0 = T * xcd / kXcds, t1 = T * (xcd + 1) / kXcds, nt = t1 - t0;
+    const int64_t lastw = nout - (ncb - 1) * bno;
+    halfok = halfok && S > 0;
+    const int64_t nh = (halfok && 2 * lastw <= bno) ? 1 : 0, nfb = ncb - nh;
+    const int64_t F0 = nt * nfb, H0 = nt * nh;
+    int64_t c = 0;
+    if (halfok) {
+        const int64_t r = F0 % S;
+        if (r > 0 && tile_makespan(F0 - r, H0 + 2 * r, S) < tile_makespan(F0, H0, S)) c = r;
+    }
+    const int64_t F = F0 - c, H = H0 + 2 * c;
+    if (k < F) {
+        it.tile = t0 + k / nfb;
+        it.ncol = (k % nfb) * bno;
+        it.valid = 1;
+    } else if (k < F + H) {
+        const int64_t j = k - F;
+        if (j < 2 * c) {
+            const int64_t fi = F + j / 2;
+            it.tile = t0 + fi / nfb;
+            it.ncol = (fi % nfb) * bno + (j & 1) * (bno / 2);
+        } else {
+            it.tile = t0 + (j - 2 * c);
+            it.ncol = (ncb - 1) * bno;
+        }
+        it.half = 1;
+        it.valid = 1;
+    }
+    return it;
+}
+
+// At least two waves per SIMD: two resident workgroups of four waves (or one
+// of eight) per compute unit, each wave within 256 registers.
+//
+// SILU (grouped, two 32-column tiles per wave): the weights hold 2 * NOUT
+// columns, gate then up (the fused-experts gate/up projection); a wave's two
+// tiles are gate columns c and up columns NOUT + c of the same 32 output
+// columns, and the epilogue stores a = silu(gate) * up with each input first
+// rounded to the activation dtype (as if the projection were stored and read
+// back), so the result equals that of the separate SiLU-and-multiply kernel.
+// slots: resident workgroups per XCD, for the item plan (any value >= 1 gives
+// results within the same bound; 0 plans no half items).
+template <int DT, bool ZERO, int BM, int BN, int WM, int WN, bool GROUPED, bool SILU = false, int GR = 0>
+__global__ void __launch_bounds__(WM * WN * 64, 2)
+gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
+                 const int32_t *__restrict__ row_src, const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
+                 const uint8_t *__restrict__ zero, uint16_t *__restrict__ y,
+                 int64_t M, int64_t K, int64_t N, int E, int gm, const float *__restrict__ cs,
+                 const float *__restrict__ cz, int slots) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int ROWB = tile_rowb(DT);
+    constexpr bool HALF = tile_half_ok<BM, WM, WN, GROUPED, GR>();
+    constexpr int BNO = SILU ? BN / 2 : BN;   // output columns per workgroup
+    __shared__ __attribute__((aligned(16))) uint8_t lds[(HALF ? 2 : 1) * 2 * BM * ROWB];
+
+    // the wave index is uniform (readfirstlane: values derived from it stay
+    // in scalar registers)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t NOUT = SILU ? N / 2 : N;
+
+    int64_t row0, row_end, n0;
+    int64_t e = 0;
+    bool half = false;
+    if constexpr (GROUPED) {
+        __shared__ int s_info[4];              // expert, row tile within it, first column, half
+        __shared__ int s_total;
+        __shared__ int scan[NT];
+        auto tiles_of = [&](int ee) {
+            const int cnt = ee < E ? offsets[ee + 1] - offsets[ee] : 0;
+            return cnt > 0 ? (cnt + BM - 1) / BM : 0;
+        };
+        const int64_t ncb = (NOUT + BNO - 1) / BNO;
+        const int64_t bid = blockIdx.x, xcd = bid % kXcds, k = bid / kXcds;
+        if (E <= 64) {
+            // one wave: inclusive scan of the experts' row tiles over its
+            // lanes, the plan, then the expert holding this item's row tile
+            if (wave == 0) {
+                const int tl = tiles_of(lane);
+                int incl = tl;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int v = __shfl_up(incl, off);
+                    if (lane >= off) incl += v;
+                }
+                const int64_t total = __shfl(incl, 63);
+                const TileItem it = tile_plan(total, xcd, k, ncb, BNO, NOUT, slots, HALF);
+                if (lane == 0) {
+                    s_info[0] = -1;
+                    s_info[2] = (int)it.ncol;
+                    s_info[3] = it.half;
+                }
+                if (it.valid && lane < E && it.tile >= incl - tl && it.tile < incl) {
+                    s_info[0] = lane;
+                    s_info[1] = (int)(it.tile - (incl - tl));
+                }
+            }
+            __syncthreads();
+        } else {
+        // total row tiles over all experts
+        if (tid == 0) {
+            s_info[0] = -1;
+            s_total = 0;
+        }
+        __syncthreads();
+        int part = 0;
+        for (int ee = tid; ee < E; ee += NT) part += tiles_of(ee);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+        if (lane == 0) atomicAdd(&s_total, part);
+        __syncthreads();
+        const TileItem it = tile_plan(s_total, xcd, k, ncb, BNO, NOUT, slots, HALF);
+        if (!it.valid) return;   // uniform: surplus workgroup
+        if (tid == 0) {
+            s_info[2] = (int)it.ncol;
+            s_info[3] = it.half;
+        }
+        const int tile = (int)it.tile;
+        // expert and row tile within it (block-wide inclusive scan per chunk)
+        int carry = 0;
+        for (int base = 0; base < E; base += NT) {
+            const int ee = base + tid;
+            const int tl = tiles_of(ee);
+            scan[tid] = tl;
+            __syncthreads();
+            for (int off = 1; off < NT; off <<= 1) {
+                const int v = tid >= off ? scan[tid - off] : 0;
+                __syncthreads();
+                scan[tid] += v;
+                __syncthreads();
+            }
+            const int incl = scan[tid] + carry, excl = incl - tl;
+            if (ee < E && tile >= excl && tile < incl) {
+                s_info[0] = ee;
+                s_info[1] = tile - excl;
+            }
+            carry += scan[NT - 1];
+            __syncthreads();
+        }
+        }
+        const int es = __builtin_amdgcn_readfirstlane(s_info[0]);
+        if (es < 0) return;      // uniform: surplus workgroup
+        e = es;
+        const int64_t tin = __builtin_amdgcn_readfirstlane(s_info[1]);
+        n0 = __builtin_amdgcn_readfirstlane(s_info[2]);
+        half = __builtin_amdgcn_readfirstlane(s_info[3]) != 0;
+        const int64_t oe = __builtin_amdgcn_readfirstlane(offsets[e]);
+        const int64_t oe1 = __builtin_amdgcn_readfirstlane(offsets[e + 1]);
+        row0 = oe + tin * BM;
+        row_end = oe1 < M ? oe1 : M;   // offsets[E] == R by contract
+    } else {
+        row0 = (int64_t)blockIdx.x * BM;
+        row_end = M;
+        n0 = (int64_t)blockIdx.y * BN;
+    }
+    if constexpr (HALF) {
+        if (half) {
+            tile_body<DT, ZERO, BM, BN, WM, WN, GROUPED, SILU, GR, 2>(x, row_src, wp, scale, zero, y, K, N, gm, cs, cz,
+                                                                      lds, row0, row_end, n0, e, 0, wave & 1,
+                                                                      wave >> 1);
+            return;
+        }
+    }
+    tile_body<DT, ZERO, BM, BN, WM, WN, GROUPED, SILU, GR, 1>(x, row_src, wp, scale, zero, y, K, N, gm, cs, cz, lds,
+                                                              row0, row_end, n0, e, wave / WN, wave % WN, 0);
+}
+
 // Workgroup tile configurations (BM x BN rows x columns, WM x WN waves).
 // Index 0 is the dense default for large M: 64 x 64 wave tiles in workgroups
 // of four waves, two resident per compute unit, so that one workgroup's
@@ -517,6 +667,8 @@ static constexpr TileCfg kTileCfgs[] = {{64, 256, 1, 4}, {64, 256, 2, 4}, {32, 2
                                         {64, 128, 2, 2}, {32, 128, 1, 4}, {128, 128, 2, 2},
                                         {128, 256, 2, 4}, {64, 128, 1, 2}};
 static std::atomic<int> g_tile_cfg{-1};      // -1: automatic
+static std::atomic<int> g_tile_halves{1};    // half items allowed (test hook)
+int set_tile_halves(int enable) { return g_tile_halves.exchange(enable ? 1 : 0, std::memory_order_relaxed); }
 
 int tile_config_count() { return (int)(sizeof(kTileCfgs) / sizeof(kTileCfgs[0])); }
 void set_tile_config(int idx) { g_tile_cfg.store(idx, std::memory_order_relaxed); }
@@ -525,16 +677,42 @@ template <int DT, bool ZERO, bool GROUPED, int BM, int BN, int WM, int WN, bool 
 static hipError_t tile_launch(const void *x, const int32_t *offsets, const int32_t *row_src, const void *wp,
                               const void *scale, const void *zero, void *y, int64_t M, int64_t K, int64_t N,
                               int64_t E, int gm, const float *cs, const float *cz, hipStream_t stream) {
-    // grouped: every expert may end in a partial row tile, hence + E; the
-    // items go on a 1-D grid rounded up to whole rounds over the XCDs
+    constexpr bool HALF = tile_half_ok<BM, WM, WN, GROUPED, GR>();
+    auto kern = gemm_tile_kernel<DT, ZERO, BM, BN, WM, WN, GROUPED, SILU, GR>;
     const int64_t ncb = SILU ? (N / 2 + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
     const int64_t mtiles = GROUPED ? (M + BM - 1) / BM + E : (M + BM - 1) / BM;
-    const int64_t slots = (mtiles * ncb + kXcds - 1) / kXcds * kXcds;
+    int sx = 1;
+    if (GROUPED && HALF && !g_tile_halves.load(std::memory_order_relaxed)) {
+        sx = 0;                          // no half items
+    } else if constexpr (GROUPED) {
+        // resident workgroups per XCD, for the item plan (queried once; a
+        // failed query only makes the plan less balanced)
+        static std::atomic<int> cached{0};
+        sx = cached.load(std::memory_order_relaxed);
+        if (sx <= 0) {
+            int dev = 0, cus = 0, blocks = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+                cus = 256;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void *>(kern),
+                                                             WM * WN * 64, 0) != hipSuccess || blocks < 1)
+                blocks = 1;
+            (void)hipGetLastError();
+            sx = cus * blocks / kXcds > 0 ? cus * blocks / kXcds : 1;
+            cached.store(sx, std::memory_order_relaxed);
+        }
+    }
+    // grouped: every expert may end in a partial row tile, hence + E; each XCD
+    // takes at most ceil(mtiles / 8) row tiles with all their column blocks,
+    // plus fewer than sx extra half items; the grid holds that many slots per
+    // XCD (surplus workgroups exit at once)
+    const int64_t per_xcd = (mtiles + kXcds - 1) / kXcds * ncb + (HALF && sx > 0 ? sx : 0);
+    const int64_t slots = per_xcd * kXcds;
     if (GROUPED && slots > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid = GROUPED ? dim3((unsigned)slots) : dim3((unsigned)mtiles, (unsigned)ncb);
-    hipLaunchKernelGGL((gemm_tile_kernel<DT, ZERO, BM, BN, WM, WN, GROUPED, SILU, GR>), grid, dim3(WM * WN * 64), 0,
-                       stream, (const uint16_t *)x, offsets, row_src, (const uint8_t *)wp, (const uint16_t *)scale,
-                       (const uint8_t *)zero, (uint16_t *)y, M, K, N, (int)E, gm, cs, cz);
+    hipLaunchKernelGGL(kern, grid, dim3(WM * WN * 64), 0, stream, (const uint16_t *)x, offsets, row_src,
+                       (const uint8_t *)wp, (const uint16_t *)scale, (const uint8_t *)zero, (uint16_t *)y, M, K, N,
+                       (int)E, gm, cs, cz, sx);
     return hipGetLastError();
 }
 

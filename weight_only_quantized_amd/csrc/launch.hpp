@@ -40,6 +40,7 @@ hipError_t launch_gemm_small_gs(const void *x, const void *wp, const void *scale
 // With row_src, row r of the product reads x row row_src[r] (gathered load).
 int tile_config_count();
 void set_tile_config(int idx);
+int set_tile_halves(int enable);     // returns the previous setting
 hipError_t launch_gemm_tile(const void *x, const int32_t *offsets, const void *wp, const void *scale,
                             const void *zero, void *y, int64_t M, int64_t K, int64_t N, int64_t E,
                             int dt, hipStream_t stream, const int32_t *row_src = nullptr, int gm = 1,

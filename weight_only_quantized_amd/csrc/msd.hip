@@ -210,17 +210,21 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
     // ---- layers and coefficients of the slice into LDS ------------------------
     // chunk c: layer l, row, 16-byte piece p of the slice's gps*128 bytes
     {
-        // every thread issues all of its layer loads before its first LDS
-        // store (one memory round trip), after the first two groups' weights
-        load_w(0, wr[0], sr[0]);
-        load_w(1, wr[1], sr[1]);
+        // every thread issues all of its layer and coefficient loads, then the
+        // first two groups' weights, then stores the layers and coefficients:
+        // the load counter is in order, so the stores (and the barrier) wait
+        // for one round trip of the slice only, not for the weights, which
+        // stay in flight into the first steps
         // every group slot of the slice is filled: slots past a short final
         // slice copy its last group (finite bytes, multiplied by zero
         // coefficients), so the chunk count and its divisions are static
         constexpr int PIECES = GPS * 8;                            // 16-byte pieces per row
         constexpr int CMAX = 3 * ROWS * PIECES;
         constexpr int CPT = (CMAX + NT - 1) / NT;
+        constexpr int CN = GPS * 4 * ROWS;                         // coefficients of the slice
+        constexpr int CFT = (CN + NT - 1) / NT;
         u32x4_t v[CPT];
+        float cv[CFT];
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
             const int c1 = u * NT + tid, c = c1 < CMAX ? c1 : CMAX - 1;
@@ -230,6 +234,15 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
             v[u] = ld128(layers + (l * Mpad + m0 + row) * K + (g_begin + gl) * kGroup + (pc % 8) * 16);
         }
 #pragma unroll
+        for (int u = 0; u < CFT; ++u) {
+            const int i1 = u * NT + tid, i = i1 < CN ? i1 : CN - 1;
+            const int gl = i / (4 * ROWS), lr = i % (4 * ROWS);
+            const int gc = gl < ng ? gl : ng - 1;                  // in bounds; zeroed below
+            cv[u] = coef[((g_begin + gc) * 4 + lr / ROWS) * Mpad + m0 + lr % ROWS];
+        }
+        load_w(0, wr[0], sr[0]);
+        load_w(1, wr[1], sr[1]);
+#pragma unroll
         for (int u = 0; u < CPT; ++u) {
             const int c = u * NT + tid;
             if (CMAX % NT == 0 || c < CMAX) {
@@ -237,9 +250,10 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
                 *reinterpret_cast<u32x4_t *>(&sA[lr * AROW + pc * 16]) = v[u];
             }
         }
-        for (int i = tid; i < GPS * 4 * ROWS; i += NT) {
-            const int gl = i / (4 * ROWS), lr = i % (4 * ROWS);
-            sC[i] = gl < ng ? coef[((g_begin + gl) * 4 + lr / ROWS) * Mpad + m0 + lr % ROWS] : 0.f;
+#pragma unroll
+        for (int u = 0; u < CFT; ++u) {
+            const int i = u * NT + tid;
+            if (CN % NT == 0 || i < CN) sC[i] = i / (4 * ROWS) < ng ? cv[u] : 0.f;
         }
     }
     __syncthreads();

@@ -22,11 +22,14 @@
 //    numbered over all experts from the expert offsets (prefix sum of
 //    ceil(rows_e / BM)), computed on the device so the host never reads the
 //    offsets.  The hardware hands workgroup i to XCD i % 8, and each XCD has
-//    its own L2; XCD x therefore takes an equal, contiguous range of the items
-//    in (row tile, column block) order, so the row tiles of one expert and the
+//    its own L2; XCD x therefore takes a contiguous range of the row tiles
+//    with all their column blocks, so the row tiles of one expert and the
 //    expert's weights stay in one L2 (two where a range boundary splits an
-//    expert).  With another XCD count the map is still a bijection, only the
-//    locality changes.  Surplus workgroups exit at once.
+//    expert).  With 32-row tiles some items are "half items" (tile_plan):
+//    two wave pairs split the item's K groups over half its columns, which
+//    fills the last round of resident workgroups.  With another XCD count
+//    the map still covers every output once, only the locality changes.
+//    Surplus workgroups exit at once.
 // Matrix-core mapping (v_mfma_f32_32x32x16_*): lane l feeds row/column l % 32
 // and k-block l / 32 (64 rows of the group: chunks 2*(l/32) and 2*(l/32)+1 of
 // the prepacked slot layout); result register r of lane l is row

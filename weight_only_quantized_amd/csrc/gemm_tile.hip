@@ -693,14 +693,21 @@ static hipError_t tile_launch(const void *x, const int32_t *offsets, const int32
         static std::atomic<int> cached{0};
         sx = cached.load(std::memory_order_relaxed);
         if (sx <= 0) {
+            // (an error of these queries is cleared so that it is not reported
+            // by the launch below; nothing else touches the error state)
             int dev = 0, cus = 0, blocks = 0;
             if (hipGetDevice(&dev) != hipSuccess ||
-                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+                (void)hipGetLastError();
                 cus = 256;
+            }
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void *>(kern),
-                                                             WM * WN * 64, 0) != hipSuccess || blocks < 1)
+                                                             WM * WN * 64, 0) != hipSuccess) {
+                (void)hipGetLastError();
                 blocks = 1;
-            (void)hipGetLastError();
+            }
+            if (cus < 1) cus = 256;
+            if (blocks < 1) blocks = 1;
             sx = cus * blocks / kXcds > 0 ? cus * blocks / kXcds : 1;
             cached.store(sx, std::memory_order_relaxed);
         }

@@ -243,9 +243,9 @@ w4a16_status w4a16_silu_and_mul(const void *h, const int32_t *row_count, int64_t
 w4a16_status w4a16_moe_sum(const void *o, const int32_t *row_of, const float *topk_w, int64_t T, int64_t topk,
                            int64_t N, void *out, int dt, void *stream);
 
-/* Workspace of w4a16_fused_moe: offsets, the permutation, the token of every
- * routed row and the intermediates h [T*topk][2I], a [T*topk][I],
- * o [T*topk][H].  0 for invalid sizes. */
+/* Workspace of w4a16_fused_moe: offsets, the row of every routing entry, the
+ * token of every routed row and the intermediates h [T*topk][2I],
+ * a [T*topk][I], o [T*topk][H].  0 for invalid sizes. */
 size_t w4a16_fused_moe_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I);
 
 /*

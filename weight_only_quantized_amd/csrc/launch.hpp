@@ -94,7 +94,7 @@ hipError_t launch_msd_intermediates(const void *x, const void *wp, int64_t M, in
 // sum, and the whole chain around two grouped GEMMs.
 constexpr int kMoeMaxExperts = 1024;
 struct MoePlan {
-    size_t off_offsets, off_sorted, off_row_of, off_tok, off_h, off_a, off_o, total;
+    size_t off_offsets, off_row_of, off_tok, off_h, off_a, off_o, total;
 };
 MoePlan moe_plan(int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I);
 hipError_t launch_moe_align(const int32_t *ids, int64_t T, int64_t topk, int64_t E, int32_t *offsets,

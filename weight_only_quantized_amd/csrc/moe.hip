@@ -7,8 +7,9 @@
 // expert topk_ids[i] with weight topk_w[i]; ids outside [0, E) are not routed.
 //
 //   moe_align_kernel      routed entries ordered by (expert, i): offsets,
-//                         sorted entry of every row, row of every entry,
-//                         token of every row
+//                         row of every entry, token of every row (the
+//                         standalone entry point writes the sorted entry of
+//                         every row instead of its token)
 //   gemm_tile_kernel      gate/up projection  h = x[token of row] . W13_e
 //                         (grouped; the gather is folded into its x loads)
 //                         with a = silu(h[:, :I]) * h[:, I:] in its epilogue
@@ -33,14 +34,106 @@ namespace w4 {
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignCache = 8192;                     // routing ids kept in LDS between the passes
 
+constexpr int kAlignMaskExperts = 256;               // lane-mask matching up to this many experts
+
+// Stable placement, J * 1024 entries per chunk: wave w takes the contiguous
+// entries c0 + 64 J w .. + 64 J - 1 in J sub-steps of 64 (J grows with the
+// entry count, so that a small count still spreads over all the waves).
+// In a sub-step the lanes holding the same expert e are found either through
+// a per-wave LDS word (every lane ORs its bit into lmask[w][e] and reads the
+// word back; E <= kAlignMaskExperts) or with one ballot per bit of the expert
+// id; a lane's rank is the count of such lanes below it plus the running
+// count of e over the wave's earlier sub-steps, wcnt[w][e] (read by every
+// lane of the expert, then advanced by its first lane, which also clears the
+// mask word: one wave's LDS accesses complete in order).  After the chunk one
+// pass per expert turns wcnt[.][e] into each wave's first position (the
+// expert's running base plus the counts of the waves before it), so a lane's
+// position is one LDS read; each wave then clears its own row.
+template <int J, bool MASK, bool CACHED>
+__device__ __forceinline__ void align_place(int64_t cb, int64_t ce, const int *idc, const int32_t *__restrict__ ids,
+                                            int64_t n, int E,
+                                            int topk, int *base, int (*wcnt)[kMoeMaxExperts],
+                                            unsigned long long (*lmask)[kAlignMaskExperts], int nbits,
+                                            int32_t *__restrict__ sorted, int32_t *__restrict__ row_of,
+                                            int32_t *__restrict__ tok_of_row) {
+    constexpr int NW = kAlignThreads / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int64_t c0 = cb; c0 < ce; c0 += (int64_t)J * kAlignThreads) {
+        int ev[J], rk[J];
+        // every id of the chunk is requested before the first is used
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int64_t i = c0 + wave * (64 * J) + j * 64 + lane;
+            if constexpr (CACHED) ev[j] = i < n ? idc[i] : -1;
+            else ev[j] = i < n ? ids[i] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int e = ev[j];
+            const bool valid = e >= 0 && e < E;
+            uint64_t same = 0;
+            int prior = 0;
+            if constexpr (MASK) {
+                if (valid) {
+                    atomicOr(&lmask[wave][e], 1ull << lane);
+                    same = lmask[wave][e];
+                    prior = wcnt[wave][e];
+                }
+            } else {
+                same = __ballot(valid);
+                for (int b = 0; b < nbits; ++b) {
+                    const bool bit = (e >> b) & 1;
+                    const uint64_t ones = __ballot(valid && bit);
+                    same &= bit ? ones : ~ones;
+                }
+                if (valid) prior = wcnt[wave][e];
+            }
+            const int rank = __popcll(same & below);
+            if (valid && rank == 0) {
+                wcnt[wave][e] = prior + __popcll(same);
+                if constexpr (MASK) lmask[wave][e] = 0ull;
+            }
+            ev[j] = valid ? e : -1;
+            rk[j] = prior + rank;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += kAlignThreads) {
+            int t[NW];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) t[w] = wcnt[w][ee];
+            int s = base[ee];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                wcnt[w][ee] = s;
+                s += t[w];
+            }
+            base[ee] = s;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int64_t i = c0 + wave * (64 * J) + j * 64 + lane;
+            const int e = ev[j];
+            if (e >= 0) {
+                const int pos = wcnt[wave][e] + rk[j];
+                if (sorted) sorted[pos] = (int32_t)i;
+                row_of[i] = pos;
+                if (tok_of_row) tok_of_row[pos] = (int32_t)((uint32_t)i / (uint32_t)topk);   // n < 2^31
+            } else if (i < n) {
+                row_of[i] = -1;
+            }
+        }
+        // this wave's row is read only by this wave until the next chunk's
+        // pass over the experts, which follows a barrier
+        for (int ee = lane; ee < E; ee += 64) wcnt[wave][ee] = 0;
+    }
+}
+
 // One workgroup: per-expert counts (LDS atomics), an exclusive scan over the
-// experts, then a stable placement of 1024 entries at a time.  The first
-// kAlignCache ids are read from memory once (every load issued before the
-// first is used) and kept in LDS for the placement pass; with E <= 64 one
-// wave scans the counts.  Inside a wave the lanes holding the same expert are found with one
-// ballot per bit of the expert id; a lane's rank among them is the count of
-// such lanes below it, and the waves' per-expert counts (in LDS) order the
-// waves.
+// experts, then the stable placement above.  The first kAlignCache ids are
+// read from memory once (every load issued before the first is used) and kept
+// in LDS for the placement pass; with E <= 64 one wave scans the counts.
 __global__ void __launch_bounds__(kAlignThreads)
 moe_align_kernel(const int32_t *__restrict__ ids, int64_t n, int E, int topk, int32_t *__restrict__ offsets,
                  int32_t *__restrict__ sorted, int32_t *__restrict__ row_of, int32_t *__restrict__ tok_of_row) {
@@ -49,22 +142,24 @@ moe_align_kernel(const int32_t *__restrict__ ids, int64_t n, int E, int topk, in
     __shared__ int base[kMoeMaxExperts];              // counts, then the running position per expert
     __shared__ int wcnt[NW][kMoeMaxExperts];          // per-wave counts of the current chunk
     __shared__ int scan[kAlignThreads];
+    __shared__ unsigned long long lmask[NW][kAlignMaskExperts];   // lane masks per wave and expert (zero between uses)
     constexpr int PT = kAlignCache / kAlignThreads;     // cached ids per thread (entry tid + 1024 j)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+    int ev[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        const int64_t i = tid + (int64_t)j * kAlignThreads;
+        ev[j] = i < n ? ids[i] : -1;
+    }
     for (int e = tid; e < E; e += kAlignThreads) {
         base[e] = 0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) wcnt[w][e] = 0;
     }
+    for (int k = tid; k < NW * kAlignMaskExperts; k += kAlignThreads) (&lmask[0][0])[k] = 0ull;
     __syncthreads();
-    int ev[PT];
     {
-#pragma unroll
-        for (int j = 0; j < PT; ++j) {
-            const int64_t i = tid + (int64_t)j * kAlignThreads;
-            ev[j] = i < n ? ids[i] : -1;
-        }
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
             const int64_t i = tid + (int64_t)j * kAlignThreads;
@@ -74,9 +169,15 @@ moe_align_kernel(const int32_t *__restrict__ ids, int64_t n, int E, int topk, in
             }
         }
     }
-    for (int64_t i = kAlignCache + tid; i < n; i += kAlignThreads) {
-        const int e = ids[i];
-        if (e >= 0 && e < E) atomicAdd(&base[e], 1);
+    for (int64_t c = kAlignCache; c < n; c += (int64_t)PT * kAlignThreads) {
+#pragma unroll
+        for (int j = 0; j < PT; ++j) {
+            const int64_t i = c + tid + (int64_t)j * kAlignThreads;
+            ev[j] = i < n ? ids[i] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < PT; ++j)
+            if (ev[j] >= 0 && ev[j] < E) atomicAdd(&base[ev[j]], 1);
     }
     __syncthreads();
     // exclusive scan over the experts
@@ -116,41 +217,26 @@ moe_align_kernel(const int32_t *__restrict__ ids, int64_t n, int E, int topk, in
 
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    const uint64_t below = (1ull << lane) - 1ull;
-    for (int64_t c0 = 0; c0 < n; c0 += kAlignThreads) {
-        const int64_t i = c0 + tid;
-        const int e = i < n ? (i < kAlignCache ? idc[i] : ids[i]) : -1;
-        const bool valid = e >= 0 && e < E;
-        uint64_t same = __ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t ones = __ballot(valid && bit);
-            same &= bit ? ones : ~ones;
-        }
-        const int rank = __popcll(same & below);
-        if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
-        __syncthreads();
-        if (valid) {
-            int pos = base[e] + rank;
-            for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
-            sorted[pos] = (int32_t)i;
-            row_of[i] = pos;
-            if (tok_of_row) tok_of_row[pos] = (int32_t)(i / topk);
-        } else if (i < n) {
-            row_of[i] = -1;
-        }
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += kAlignThreads) {
-            int s = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                s += wcnt[w][ee];
-                wcnt[w][ee] = 0;
-            }
-            base[ee] += s;
-        }
-        __syncthreads();
+#define W4_ALIGN_PLACE(JV, MV, CV, B, EN)                                                                     \
+    align_place<JV, MV, CV>(B, EN, idc, ids, n, E, topk, base, wcnt, lmask, nbits, sorted, row_of, tok_of_row)
+    // chunks within the cached ids load from LDS only (their waits then never
+    // cover earlier chunks' stores); the rest (J = 4, chunk-aligned at
+    // kAlignCache) load from memory
+    const int J = n <= kAlignThreads ? 1 : (n <= 2 * kAlignThreads ? 2 : 4);
+    const int64_t nc = n < kAlignCache ? n : kAlignCache;
+    static_assert(kAlignCache % (4 * kAlignThreads) == 0, "cached range must end on a chunk boundary");
+    if (E <= kAlignMaskExperts) {
+        if (J == 1) W4_ALIGN_PLACE(1, true, true, 0, nc);
+        else if (J == 2) W4_ALIGN_PLACE(2, true, true, 0, nc);
+        else W4_ALIGN_PLACE(4, true, true, 0, nc);
+        if (n > kAlignCache) W4_ALIGN_PLACE(4, true, false, kAlignCache, n);
+    } else {
+        if (J == 1) W4_ALIGN_PLACE(1, false, true, 0, nc);
+        else if (J == 2) W4_ALIGN_PLACE(2, false, true, 0, nc);
+        else W4_ALIGN_PLACE(4, false, true, 0, nc);
+        if (n > kAlignCache) W4_ALIGN_PLACE(4, false, false, kAlignCache, n);
     }
+#undef W4_ALIGN_PLACE
 }
 
 // x_sorted[r] = x[sorted[r] / topk] for the routed rows r < offsets[E]; one
@@ -297,8 +383,7 @@ MoePlan moe_plan(int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I) {
     MoePlan p{};
     const size_t n = (size_t)(T * topk);
     p.off_offsets = 0;
-    p.off_sorted = align256(p.off_offsets + sizeof(int32_t) * (size_t)(E + 1));
-    p.off_row_of = align256(p.off_sorted + sizeof(int32_t) * n);
+    p.off_row_of = align256(p.off_offsets + sizeof(int32_t) * (size_t)(E + 1));
     p.off_tok = align256(p.off_row_of + sizeof(int32_t) * n);
     p.off_h = align256(p.off_tok + sizeof(int32_t) * n);
     p.off_a = align256(p.off_h + 2 * n * (size_t)(2 * I));
@@ -314,12 +399,13 @@ hipError_t launch_fused_moe(const void *x, const int32_t *ids, const float *topk
     const MoePlan p = moe_plan(T, topk, E, H, I);
     uint8_t *ws = (uint8_t *)workspace;
     int32_t *offsets = (int32_t *)(ws + p.off_offsets);
-    int32_t *sorted = (int32_t *)(ws + p.off_sorted);
     int32_t *row_of = (int32_t *)(ws + p.off_row_of);
     int32_t *tok = (int32_t *)(ws + p.off_tok);
     void *h = ws + p.off_h, *a = ws + p.off_a, *o = ws + p.off_o;
     const int64_t n = T * topk;                       // upper bound of the routed rows
-    hipError_t err = launch_moe_align(ids, T, topk, E, offsets, sorted, row_of, stream, tok);
+    // the chain reads the token of each row and the row of each entry, never
+    // the sorted entry indices: those are not written
+    hipError_t err = launch_moe_align(ids, T, topk, E, offsets, nullptr, row_of, stream, tok);
     // the grouped kernel takes its row tiles from the offsets (offsets[E] <= n)
     // and reads row r of its x operand from token tok[r]
     if (err == hipSuccess) {

@@ -42,7 +42,8 @@ def _routing(T, topk, E, invalid, seed):
 
 @pytest.mark.parametrize("T,topk,E,invalid", [(1, 1, 1, False), (37, 4, 5, True), (700, 3, 64, True),
                                               (512, 8, 64, False), (64, 2, 1024, True), (300, 8, 7, False),
-                                              (1100, 8, 16, True), (200, 8, 33, True), (128, 8, 64, False)])
+                                              (1100, 8, 16, True), (200, 8, 33, True), (128, 8, 64, False),
+                                              (1100, 8, 300, True), (300, 8, 256, False), (150, 8, 257, True)])
 def test_align_bit_exact(orc, T, topk, E, invalid):
     import weight_only_quantized_amd as w4
     print(f"[case] align T={T} topk={topk} E={E} invalid={invalid}", flush=True)

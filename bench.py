@@ -483,22 +483,33 @@ def run_steps(calls, steps, warmup):
     return wall, a.elapsed_time(b) * 1e-3
 
 
-def per_launch_ms(calls, steps, warmup):
+def per_launch_ms(calls, steps, warmup, warm_s=0.1, reps=3):
     """Average duration of each call: a graph of `steps` back-to-back launches of
-    that one call (rotating buffer sets), replayed once to warm up and once
-    between two HIP events on the replay stream (torch's current stream)."""
+    that one call (rotating buffer sets), replayed until >= `warm_s` seconds of
+    the same work have run (at least twice: under a long matrix-core load the
+    clocks settle only after ~50 ms), then `reps` more times, each
+    between two HIP events on the replay stream (torch's current stream); the
+    mean over those replays."""
     import torch
     out = []
     for c in calls:
         g = _capture([c], warmup, steps)
-        g.replay()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        out.append(a.elapsed_time(b) / steps)
+        t0 = time.perf_counter()
+        n = 0
+        while n < 2 or time.perf_counter() - t0 < warm_s:
+            g.replay()
+            torch.cuda.synchronize()
+            n += 1
+        ms = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b) / steps)
+        out.append(sum(ms) / len(ms))
     return out
 
 

@@ -134,7 +134,9 @@ w4a16_status w4a16_gemm(const void *x, const void *w_packed, const void *scale,
  * 7.49, 14.98, 14.98 (round half to even); the layers are multiplied with the
  * int4 weights by int8 matrix-core instructions with int32 accumulation, then
  * merged as ((Y1/7.49 + Y2/(7.49*14.98) + Y3/(7.49*14.98^2)) * A_max) * scale
- * and accumulated over groups in fp32.
+ * and accumulated over groups in fp32.  A single row (M = 1) runs as one
+ * launch that decomposes x itself and uses no workspace; larger M runs the
+ * decomposition, the product kernel over K slices and their sum.
  *   x                [M][K] fp16
  *   w_packed         prepacked signed weights (is_signed = 1)
  *   antiquant_scale  [K/128][N] fp16
@@ -160,8 +162,8 @@ w4a16_status w4a16_msd_gemm(const void *x, const void *w_packed, const void *ant
  * the process ends.  A problem whose workspace (that of the kernel
  * configuration the call runs, at most w4a16_msd_workspace_bytes()) exceeds
  * it returns W4A16_ERR_SCRATCH before anything is enqueued; the shapes of the
- * MSD page fit (M = 64, K = N = 8192 needs about 19 MB; M = 1, K = 8192,
- * N = 12288 about 1 MB).  Calls no allocating routine.  Every call on one GPU shares that GPU's array: calls
+ * MSD page fit (M = 64, K = N = 8192 needs about 19 MB; a single row needs
+ * none).  Calls no allocating routine.  Every call on one GPU shares that GPU's array: calls
  * that may overlap in time on one GPU (different streams without ordering,
  * other threads) race and must be serialized by the caller.
  */

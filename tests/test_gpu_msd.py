@@ -28,7 +28,8 @@ def _intermediates(p):
 
 
 @pytest.mark.parametrize("M,K,N,seed", [(1, 128, 64, 0), (5, 384, 128, 1), (17, 256, 64, 2), (64, 512, 192, 3),
-                                        (70, 256, 128, 4)])
+                                        (70, 256, 128, 4), (1, 2176, 128, 5), (1, 3072, 192, 6),
+                                        (1, 8192, 12288, 7)])
 def test_intermediates_bit_exact(orc, M, K, N, seed):
     print(f"[case] msd intermediates M={M} K={K} N={N}", flush=True)
     p = synth.msd(M=M, K=K, N=N, seed=seed)
@@ -81,7 +82,8 @@ def test_msd_page_example(orc):
     _check_msd(orc, synth.msd_page_example(), "msd_page")
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 128, 64), (3, 1024, 320), (33, 2048, 192), (100, 512, 128)])
+@pytest.mark.parametrize("M,K,N", [(1, 128, 64), (3, 1024, 320), (33, 2048, 192), (100, 512, 128),
+                                   (1, 2176, 192), (1, 1920, 64)])
 def test_msd_shapes(orc, M, K, N):
     _check_msd(orc, synth.msd(M=M, K=K, N=N, seed=M), f"msd_{M}x{K}x{N}")
 
@@ -93,6 +95,21 @@ def test_msd_zero_rows(orc):
     xf[2, 128:256] = 0.0
     p.x = synth.to_bits(xf, synth.F16)
     mx, _ = _check_msd(orc, p, "msd_zero_rows")
+
+
+def test_msd_zero_groups_single_row(orc):
+    """One row (the one-launch kernel) with all-zero groups (A_max = 0: zero
+    layers and coefficients) next to ordinary ones."""
+    p = synth.msd(M=1, K=2048, N=192, seed=11)
+    xf = synth.bits_to_f32(p.x, synth.F16)
+    xf[0, 0:128] = 0.0
+    xf[0, 1024:1280] = 0.0
+    p.x = synth.to_bits(xf, synth.F16)
+    _check_msd(orc, p, "msd_zero_groups_1row")
+    amax, layers, yint = _intermediates(p)
+    ra = orc.msd_amax(p.x, 1, p.K)
+    rl = orc.msd_layers(p.x, ra, 1, p.K)
+    assert np.array_equal(yint, orc.msd_yint(rl, p.w, 1, p.K, p.N))
 
 
 def test_msd_workspace_errors():

@@ -376,6 +376,144 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
             }
 }
 
+// One-row MSD (M = 1, the shape of the page's worked example, §4.3): the
+// decomposition, the integer products and the merge in one launch.  A
+// workgroup owns NB 16-column blocks; its 16 waves split K (wave w takes the
+// groups [w*SG, (w+1)*SG)) and add their sums through LDS at the end, in wave
+// order, so no partial sums reach memory and no other launch is needed.  For
+// each of its groups a wave decomposes the row's 128 values itself (two per
+// lane, the fp32 steps of msd_decompose_kernel; A_max and the layer sums by
+// wave reductions), writes the layer bytes to its own LDS row in the order
+// the matrix-core operand takes (byte p of each 8-value chunk holds value
+// perm8(p)) and every lane reads its k-block of that row, so all 16 result
+// rows equal row 0 and no lane is masked.  The next group's weight tiles,
+// scales and x values are requested before the current group is used (two
+// register sets).  DUMP writes the per-group integer products Y_j - 8 S_j
+// ([G][3][1][N], as the product kernel's test hook) instead of y.
+template <int NB, bool DUMP>
+__global__ void __launch_bounds__(1024)
+msd_row_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
+               uint16_t *__restrict__ y, int32_t *__restrict__ yint, int64_t K, int64_t N) {
+    constexpr int NW = 16;
+    __shared__ __attribute__((aligned(16))) uint8_t sL[NW][3][kGroup];
+    __shared__ float red[NW][NB * 16];
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, kc = lane >> 4;
+    const int64_t G = K / kGroup;
+    const int64_t SG = (G + NW - 1) / NW;
+    const int64_t gb = (int64_t)wave * SG;
+    const int ns = (int)(gb < G ? (gb + SG < G ? SG : G - gb) : 0);     // this wave's groups
+    const int64_t nb0 = (int64_t)blockIdx.x * NB;
+    const uint8_t *wu = wp + nb0 * G * kTileBytes;                      // tile (b, g) at (b*G + g) KB
+    const uint32_t woff = (uint32_t)lane * 16u;
+
+    // group gl of the slice (clamped to the slice's last; a wave without
+    // groups reads group 0 and uses nothing): every load is unconditional
+    auto load = [&](int gl, u32x4_t (&wd)[NB], uint16_t (&sd)[NB], uint32_t &xd) {
+        const int64_t g = ns > 0 ? gb + (gl < ns ? gl : ns - 1) : 0;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) wd[b] = ld128(wu + ((int64_t)b * G + g) * kTileBytes + woff);
+        if constexpr (!DUMP) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) sd[b] = scale[g * N + (nb0 + b) * 16 + j];
+        }
+        xd = *reinterpret_cast<const uint32_t *>(x + g * kGroup + 2 * lane);
+    };
+    // byte positions of this lane's two values (2*lane, 2*lane + 1) in the
+    // operand order of their 8-value chunk
+    const int q0 = 2 * (lane & 3);
+    const int pos0 = (lane >> 2) * 8 + (q0 < 4 ? 2 * q0 : 2 * (q0 - 4) + 1);
+    const int pos1 = (lane >> 2) * 8 + (q0 + 1 < 4 ? 2 * (q0 + 1) : 2 * (q0 + 1 - 4) + 1);
+
+    float yacc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) yacc[b] = 0.f;
+
+    auto step = [&](int gl, const u32x4_t (&wc)[NB], const uint16_t (&sc)[NB], uint32_t xc, u32x4_t (&wn)[NB],
+                    uint16_t (&sn)[NB], uint32_t &xn) {
+        load(gl + 1, wn, sn, xn);
+        const int64_t g = gb + gl;
+        // eq.1-7 for the row's group g
+        const float a0 = h2f<DT_F16>((uint16_t)(xc & 0xFFFFu)), a1 = h2f<DT_F16>((uint16_t)(xc >> 16));
+        float am = fmaxf(fabsf(a0), fabsf(a1));
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
+        int l0[3], l1[3], ls[3];
+        msd_decompose(a0, am, l0[0], l0[1], l0[2]);
+        msd_decompose(a1, am, l1[0], l1[1], l1[2]);
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            int t = l0[q] + l1[q];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) t += __shfl_xor(t, off);
+            ls[q] = t;                                                   // exact in int32
+        }
+        const float c0 = am * kR0, c1 = am * kR1, c2 = am * kR2;
+        const float c3 = 8.f * __builtin_fmaf(c0, (float)ls[0], __builtin_fmaf(c1, (float)ls[1], c2 * (float)ls[2]));
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            sL[wave][q][pos0] = (uint8_t)(int8_t)l0[q];
+            sL[wave][q][pos1] = (uint8_t)(int8_t)l1[q];
+        }
+        // one wave's LDS accesses complete in order: the reads below see the
+        // writes above, and the next group's writes follow these reads
+        __builtin_amdgcn_wave_barrier();
+        u32x4_t a[3][2];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            a[q][0] = *reinterpret_cast<const u32x4_t *>(&sL[wave][q][32 * kc]);
+            a[q][1] = *reinterpret_cast<const u32x4_t *>(&sL[wave][q][32 * kc + 16]);
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const u32x4_t b0 = weight_u4(wc[b][0], wc[b][1]), b1 = weight_u4(wc[b][2], wc[b][3]);
+            i32x4_t Y[3];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                Y[q] = mfma_i8_16x16x64(a[q][0], b0, i32x4_t{0, 0, 0, 0});
+                Y[q] = mfma_i8_16x16x64(a[q][1], b1, Y[q]);
+            }
+            if constexpr (DUMP) {
+                if (kc == 0) {
+#pragma unroll
+                    for (int q = 0; q < 3; ++q) yint[(g * 3 + q) * N + (nb0 + b) * 16 + j] = Y[q][0] - 8 * ls[q];
+                }
+            } else {
+                float t = __builtin_fmaf((float)Y[0][0], c0, -c3);
+                t = __builtin_fmaf((float)Y[1][0], c1, t);
+                t = __builtin_fmaf((float)Y[2][0], c2, t);
+                yacc[b] += h2f<DT_F16>(sc[b]) * t;
+            }
+        }
+    };
+
+    u32x4_t wr0[NB], wr1[NB];
+    uint16_t sr0[NB], sr1[NB];
+    uint32_t xr0, xr1;
+    load(0, wr0, sr0, xr0);
+    int gl = 0;
+    for (; gl + 1 < ns; gl += 2) {
+        step(gl, wr0, sr0, xr0, wr1, sr1, xr1);
+        step(gl + 1, wr1, sr1, xr1, wr0, sr0, xr0);
+    }
+    if (gl < ns) step(gl, wr0, sr0, xr0, wr1, sr1, xr1);
+
+    if constexpr (DUMP) return;
+    if (kc == 0) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) red[wave][b * 16 + j] = yacc[b];
+    }
+    __syncthreads();
+    if (tid < NB * 16) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sum += red[w][tid];
+        y[nb0 * 16 + tid] = f2h<DT_F16>(sum);
+    }
+}
+
 // Sum of the K slices' partial sums (matrix-core result layout: per row chunk z,
 // 16-column block nb and 16-row tile mt, 64 lanes x 4 result registers) and
 // rounding to fp16.  One thread per lane and tile; slice stride `slice` floats.
@@ -575,8 +713,21 @@ static hipError_t launch_msd_plan(const MsdPlan &p, const void *x, const void *w
     return hipGetLastError();
 }
 
+// One row: the one-launch kernel above (N % 64 == 0 by contract, so the
+// grid covers the columns exactly); needs no workspace.
+constexpr int kMsdRowNb = 4;
+template <bool DUMP>
+static hipError_t launch_msd_row(const void *x, const void *wp, const void *scale, void *y, int32_t *yint,
+                                 int64_t K, int64_t N, hipStream_t stream) {
+    hipLaunchKernelGGL((msd_row_kernel<kMsdRowNb, DUMP>), dim3((unsigned)(N / (16 * kMsdRowNb))), dim3(1024), 0,
+                       stream, (const uint16_t *)x, (const uint8_t *)wp, (const uint16_t *)scale, (uint16_t *)y,
+                       yint, K, N);
+    return hipGetLastError();
+}
+
 hipError_t launch_msd(const void *x, const void *wp, const void *scale, void *y, int64_t M, int64_t K,
                       int64_t N, void *workspace, hipStream_t stream) {
+    if (M == 1) return launch_msd_row<false>(x, wp, scale, y, nullptr, K, N, stream);
     return launch_msd_plan(msd_plan(M, K, N), x, wp, scale, y, M, K, N, workspace, stream);
 }
 
@@ -616,10 +767,11 @@ static hipError_t msd_scratch_ptr(void **out) {
     return hipSuccess;
 }
 
-size_t msd_noalloc_bytes(int64_t M, int64_t K, int64_t N) { return msd_plan(M, K, N).total; }
+size_t msd_noalloc_bytes(int64_t M, int64_t K, int64_t N) { return M == 1 ? 0 : msd_plan(M, K, N).total; }
 
 hipError_t launch_msd_noalloc(const void *x, const void *wp, const void *scale, void *y, int64_t M, int64_t K,
                               int64_t N, hipStream_t stream) {
+    if (M == 1) return launch_msd_row<false>(x, wp, scale, y, nullptr, K, N, stream);     // no workspace
     const MsdPlan p = msd_plan(M, K, N);     // the plan that runs: its own workspace size is checked
     if (p.total > kMsdScratchBytes) return hipErrorInvalidValue;
     void *ws = nullptr;
@@ -666,7 +818,9 @@ hipError_t launch_msd_intermediates(const void *x, const void *wp, int64_t M, in
                        (const int8_t *)(ws + p.off_layers), layers, M, p.mpad, K);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // the products of every group are written separately
+    // the products of every group are written separately (one row: by the
+    // one-launch kernel, from its own decomposition)
+    if (M == 1) return launch_msd_row<true>(x, wp, nullptr, nullptr, yint, K, N, stream);
     return msd_gemm_launch<true>(p, (const int8_t *)(ws + p.off_layers), (const float *)(ws + p.off_coef),
                                  (const int32_t *)(ws + p.off_lsum), wp,
                                  nullptr, nullptr, nullptr, yint, M, K, N, p.ksplit, p.gps, stream);

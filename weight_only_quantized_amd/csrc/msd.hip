@@ -390,6 +390,32 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
 // scales and x values are requested before the current group is used (two
 // register sets).  DUMP writes the per-group integer products Y_j - 8 S_j
 // ([G][3][1][N], as the product kernel's test hook) instead of y.
+// Sum and maximum over the 64 lanes of a wave with DPP moves (quad
+// permutations, half-row and row mirrors, then the row broadcasts of lanes 15
+// and 31), read from lane 63: a wave-uniform result without LDS round trips.
+// Integer sums and maxima do not depend on the order of the operations; a
+// lane whose DPP source is disabled combines with `fill`.
+template <typename F>
+__device__ __forceinline__ int wave_reduce_dpp(int v, int fill, F op) {
+    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x140, 0xF, 0xF, false));   // row_mirror
+    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x142, 0xA, 0xF, false));   // row_bcast:15 into rows 1, 3
+    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x143, 0xC, 0xF, false));   // row_bcast:31 into rows 2, 3
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    return wave_reduce_dpp(v, 0, [](int a, int b) { return a + b; });
+}
+// maximum of non-negative floats with fmaxf, as in msd_decompose_kernel
+// (rows left out of a broadcast keep their value: fmaxf(v, 0) for v >= 0)
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    return __builtin_bit_cast(float, wave_reduce_dpp(__builtin_bit_cast(int, v), 0, [](int a, int b) {
+        return __builtin_bit_cast(int, fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+    }));
+}
+
 template <int NB, bool DUMP>
 __global__ void __launch_bounds__(1024)
 msd_row_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,
@@ -436,19 +462,12 @@ msd_row_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp, c
         const int64_t g = gb + gl;
         // eq.1-7 for the row's group g
         const float a0 = h2f<DT_F16>((uint16_t)(xc & 0xFFFFu)), a1 = h2f<DT_F16>((uint16_t)(xc >> 16));
-        float am = fmaxf(fabsf(a0), fabsf(a1));
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) am = fmaxf(am, __shfl_xor(am, off));
+        const float am = wave_max_nonneg(fmaxf(fabsf(a0), fabsf(a1)));
         int l0[3], l1[3], ls[3];
         msd_decompose(a0, am, l0[0], l0[1], l0[2]);
         msd_decompose(a1, am, l1[0], l1[1], l1[2]);
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            int t = l0[q] + l1[q];
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) t += __shfl_xor(t, off);
-            ls[q] = t;                                                   // exact in int32
-        }
+        for (int q = 0; q < 3; ++q) ls[q] = wave_sum_i32(l0[q] + l1[q]);   // exact in int32
         const float c0 = am * kR0, c1 = am * kR1, c2 = am * kR2;
         const float c3 = 8.f * __builtin_fmaf(c0, (float)ls[0], __builtin_fmaf(c1, (float)ls[1], c2 * (float)ls[2]));
 #pragma unroll

@@ -63,8 +63,50 @@ __device__ __forceinline__ void msd_decompose(float a, float amax, int &l1, int 
     l3 = (int)a3;
 }
 
-// One 256-thread workgroup handles 16 (row, group) pairs; 16 lanes per pair,
-// 8 elements per lane.
+// Sum and maximum over the 64 lanes of a wave with DPP moves (quad
+// permutations, half-row and row mirrors, then the row broadcasts of lanes 15
+// and 31), read from lane 63: a wave-uniform result without LDS round trips.
+// Integer sums and maxima do not depend on the order of the operations; a
+// lane whose DPP source is disabled combines with `fill`.
+// The first four steps leave every lane of a 16-lane row with the row's
+// result (row_reduce_dpp).
+template <typename F>
+__device__ __forceinline__ int row_reduce_dpp(int v, int fill, F op) {
+    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x140, 0xF, 0xF, false));   // row_mirror
+    return v;
+}
+template <typename F>
+__device__ __forceinline__ int wave_reduce_dpp(int v, int fill, F op) {
+    v = row_reduce_dpp(v, fill, op);
+    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x142, 0xA, 0xF, false));   // row_bcast:15 into rows 1, 3
+    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x143, 0xC, 0xF, false));   // row_bcast:31 into rows 2, 3
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    return wave_reduce_dpp(v, 0, [](int a, int b) { return a + b; });
+}
+// maximum of non-negative floats with fmaxf, as in msd_decompose_kernel
+// (rows left out of a broadcast keep their value: fmaxf(v, 0) for v >= 0)
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    return __builtin_bit_cast(float, wave_reduce_dpp(__builtin_bit_cast(int, v), 0, [](int a, int b) {
+        return __builtin_bit_cast(int, fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+    }));
+}
+
+__device__ __forceinline__ int row_sum_i32(int v) {
+    return row_reduce_dpp(v, 0, [](int a, int b) { return a + b; });
+}
+__device__ __forceinline__ float row_max_nonneg(float v) {
+    return __builtin_bit_cast(float, row_reduce_dpp(__builtin_bit_cast(int, v), 0, [](int a, int b) {
+        return __builtin_bit_cast(int, fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+    }));
+}
+
+// One 256-thread workgroup handles 16 (row, group) pairs; 16 lanes (one DPP
+// row) per pair, 8 elements per lane.
 __global__ void __launch_bounds__(256)
 msd_decompose_kernel(const uint16_t *__restrict__ x, float *__restrict__ coef, int32_t *__restrict__ lsum,
                      float *__restrict__ amax_out, int8_t *__restrict__ layers, int64_t M, int64_t Mpad,
@@ -87,10 +129,7 @@ msd_decompose_kernel(const uint16_t *__restrict__ x, float *__restrict__ coef, i
     float am = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(a[i]));
-    am = fmaxf(am, __shfl_xor(am, 1));
-    am = fmaxf(am, __shfl_xor(am, 2));
-    am = fmaxf(am, __shfl_xor(am, 4));
-    am = fmaxf(am, __shfl_xor(am, 8));          // eq.1: A_max of the (row, group)
+    am = row_max_nonneg(am);                    // eq.1: A_max of the (row, group)
     if (!valid) return;
 
     int l[3][8];
@@ -103,11 +142,7 @@ msd_decompose_kernel(const uint16_t *__restrict__ x, float *__restrict__ coef, i
         int t = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) t += l[j][i];
-        t += __shfl_xor(t, 1);
-        t += __shfl_xor(t, 2);
-        t += __shfl_xor(t, 4);
-        t += __shfl_xor(t, 8);
-        ls[j] = t;
+        ls[j] = row_sum_i32(t);
     }
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -390,32 +425,6 @@ msd_gemm_kernel(const int8_t *__restrict__ layers, const float *__restrict__ coe
 // scales and x values are requested before the current group is used (two
 // register sets).  DUMP writes the per-group integer products Y_j - 8 S_j
 // ([G][3][1][N], as the product kernel's test hook) instead of y.
-// Sum and maximum over the 64 lanes of a wave with DPP moves (quad
-// permutations, half-row and row mirrors, then the row broadcasts of lanes 15
-// and 31), read from lane 63: a wave-uniform result without LDS round trips.
-// Integer sums and maxima do not depend on the order of the operations; a
-// lane whose DPP source is disabled combines with `fill`.
-template <typename F>
-__device__ __forceinline__ int wave_reduce_dpp(int v, int fill, F op) {
-    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
-    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
-    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x141, 0xF, 0xF, false));   // row_half_mirror
-    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x140, 0xF, 0xF, false));   // row_mirror
-    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x142, 0xA, 0xF, false));   // row_bcast:15 into rows 1, 3
-    v = op(v, __builtin_amdgcn_update_dpp(fill, v, 0x143, 0xC, 0xF, false));   // row_bcast:31 into rows 2, 3
-    return __builtin_amdgcn_readlane(v, 63);
-}
-__device__ __forceinline__ int wave_sum_i32(int v) {
-    return wave_reduce_dpp(v, 0, [](int a, int b) { return a + b; });
-}
-// maximum of non-negative floats with fmaxf, as in msd_decompose_kernel
-// (rows left out of a broadcast keep their value: fmaxf(v, 0) for v >= 0)
-__device__ __forceinline__ float wave_max_nonneg(float v) {
-    return __builtin_bit_cast(float, wave_reduce_dpp(__builtin_bit_cast(int, v), 0, [](int a, int b) {
-        return __builtin_bit_cast(int, fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
-    }));
-}
-
 template <int NB, bool DUMP>
 __global__ void __launch_bounds__(1024)
 msd_row_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp, const uint16_t *__restrict__ scale,

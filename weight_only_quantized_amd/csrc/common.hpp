@@ -193,4 +193,18 @@ __device__ __forceinline__ u32x4_t ld128(const void *p) { return *reinterpret_ca
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active): DPP
+// shifts by 1, 2, 4 and 8 lanes within each 16-lane row (lanes shifted in
+// from outside the row add 0), then the rows' totals are added by the
+// broadcasts of lanes 15 and 31.  No LDS round trips.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+    return v;
+}
+
 }  // namespace w4

@@ -553,11 +553,14 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
     int64_t e = 0;
     bool half = false;
     if constexpr (GROUPED) {
-        __shared__ int s_info[4];              // expert, row tile within it, first column, half
+        __shared__ int s_info[6];              // expert, row tile within it, first column, half, its offsets
         __shared__ int s_total;
         __shared__ int scan[NT];
-        auto tiles_of = [&](int ee) {
-            const int cnt = ee < E ? offsets[ee + 1] - offsets[ee] : 0;
+        // row tiles of expert ee (0 past E); o0, o1 get its offsets
+        auto tiles_of = [&](int ee, int &o0, int &o1) {
+            o0 = ee < E ? offsets[ee] : 0;
+            o1 = ee < E ? offsets[ee + 1] : 0;
+            const int cnt = o1 - o0;
             return cnt > 0 ? (cnt + BM - 1) / BM : 0;
         };
         const int64_t ncb = (NOUT + BNO - 1) / BNO;
@@ -566,14 +569,10 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
             // one wave: inclusive scan of the experts' row tiles over its
             // lanes, the plan, then the expert holding this item's row tile
             if (wave == 0) {
-                const int tl = tiles_of(lane);
-                int incl = tl;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const int v = __shfl_up(incl, off);
-                    if (lane >= off) incl += v;
-                }
-                const int64_t total = __shfl(incl, 63);
+                int o0, o1;
+                const int tl = tiles_of(lane, o0, o1);
+                const int incl = wave_incl_scan(tl);
+                const int64_t total = __builtin_amdgcn_readlane(incl, 63);
                 const TileItem it = tile_plan(total, xcd, k, ncb, BNO, NOUT, slots, HALF);
                 if (lane == 0) {
                     s_info[0] = -1;
@@ -583,6 +582,8 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
                 if (it.valid && lane < E && it.tile >= incl - tl && it.tile < incl) {
                     s_info[0] = lane;
                     s_info[1] = (int)(it.tile - (incl - tl));
+                    s_info[4] = o0;
+                    s_info[5] = o1;
                 }
             }
             __syncthreads();
@@ -594,9 +595,11 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
         }
         __syncthreads();
         int part = 0;
-        for (int ee = tid; ee < E; ee += NT) part += tiles_of(ee);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+        for (int ee = tid; ee < E; ee += NT) {
+            int o0, o1;
+            part += tiles_of(ee, o0, o1);
+        }
+        part = __builtin_amdgcn_readlane(wave_incl_scan(part), 63);
         if (lane == 0) atomicAdd(&s_total, part);
         __syncthreads();
         const TileItem it = tile_plan(s_total, xcd, k, ncb, BNO, NOUT, slots, HALF);
@@ -610,7 +613,8 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
         int carry = 0;
         for (int base = 0; base < E; base += NT) {
             const int ee = base + tid;
-            const int tl = tiles_of(ee);
+            int o0, o1;
+            const int tl = tiles_of(ee, o0, o1);
             scan[tid] = tl;
             __syncthreads();
             for (int off = 1; off < NT; off <<= 1) {
@@ -623,6 +627,8 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
             if (ee < E && tile >= excl && tile < incl) {
                 s_info[0] = ee;
                 s_info[1] = tile - excl;
+                s_info[4] = o0;
+                s_info[5] = o1;
             }
             carry += scan[NT - 1];
             __syncthreads();
@@ -634,8 +640,9 @@ gemm_tile_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ off
         const int64_t tin = __builtin_amdgcn_readfirstlane(s_info[1]);
         n0 = __builtin_amdgcn_readfirstlane(s_info[2]);
         half = __builtin_amdgcn_readfirstlane(s_info[3]) != 0;
-        const int64_t oe = __builtin_amdgcn_readfirstlane(offsets[e]);
-        const int64_t oe1 = __builtin_amdgcn_readfirstlane(offsets[e + 1]);
+        // the expert's offsets as its scan lane read them (no second load)
+        const int64_t oe = __builtin_amdgcn_readfirstlane(s_info[4]);
+        const int64_t oe1 = __builtin_amdgcn_readfirstlane(s_info[5]);
         row0 = oe + tin * BM;
         row_end = oe1 < M ? oe1 : M;   // offsets[E] == R by contract
     } else {

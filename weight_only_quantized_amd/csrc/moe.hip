@@ -184,12 +184,7 @@ moe_align_kernel(const int32_t *__restrict__ ids, int64_t n, int E, int topk, in
     if (E <= 64) {
         if (wave == 0) {
             const int cnt = lane < E ? base[lane] : 0;
-            int incl = cnt;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int v = __shfl_up(incl, off);
-                if (lane >= off) incl += v;
-            }
+            const int incl = wave_incl_scan(cnt);
             if (lane < E) {
                 offsets[lane] = incl - cnt;
                 base[lane] = incl - cnt;

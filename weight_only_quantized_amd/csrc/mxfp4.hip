@@ -320,10 +320,13 @@ mx_tile_kernel(const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx, c
     const int G = (int)(K / kGroup);
     int64_t row0, row_end, n0, e = 0;
     if constexpr (GROUPED) {
-        __shared__ int s_info[3];
+        __shared__ int s_info[5];      // expert, row tile within it, total row tiles, the expert's offsets
         __shared__ int scan[NT];
-        auto tiles_of = [&](int ee) {
-            const int cnt = ee < E ? offsets[ee + 1] - offsets[ee] : 0;
+        // row tiles of expert ee (0 past E); o0, o1 get its offsets
+        auto tiles_of = [&](int ee, int &o0, int &o1) {
+            o0 = ee < E ? offsets[ee] : 0;
+            o1 = ee < E ? offsets[ee + 1] : 0;
+            const int cnt = o1 - o0;
             return cnt > 0 ? (cnt + BM - 1) / BM : 0;
         };
         // this workgroup's item: slot bid / 8 of XCD bid % 8's contiguous range
@@ -334,14 +337,10 @@ mx_tile_kernel(const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx, c
             // one wave: inclusive scan of the experts' row tiles over its
             // lanes, then the expert holding this item's row tile
             if (wave == 0) {
-                const int tl = tiles_of(lane);
-                int incl = tl;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const int v = __shfl_up(incl, off);
-                    if (lane >= off) incl += v;
-                }
-                const int64_t total = __shfl(incl, 63);
+                int o0, o1;
+                const int tl = tiles_of(lane, o0, o1);
+                const int incl = wave_incl_scan(tl);
+                const int64_t total = __builtin_amdgcn_readlane(incl, 63);
                 const int64_t items = total * ncb;
                 const int64_t it = items * xcd / kMxXcds + bid / kMxXcds;
                 const int tile = (int)(it / ncb);
@@ -352,6 +351,8 @@ mx_tile_kernel(const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx, c
                 if (it < items * (xcd + 1) / kMxXcds && lane < E && tile >= incl - tl && tile < incl) {
                     s_info[0] = lane;
                     s_info[1] = tile - (incl - tl);
+                    s_info[3] = o0;
+                    s_info[4] = o1;
                 }
             }
             __syncthreads();
@@ -368,9 +369,11 @@ mx_tile_kernel(const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx, c
         }
         __syncthreads();
         int part = 0;
-        for (int ee = tid; ee < E; ee += NT) part += tiles_of(ee);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+        for (int ee = tid; ee < E; ee += NT) {
+            int o0, o1;
+            part += tiles_of(ee, o0, o1);
+        }
+        part = __builtin_amdgcn_readlane(wave_incl_scan(part), 63);
         if (lane == 0) atomicAdd(&s_info[2], part);
         __syncthreads();
         const int64_t items = (int64_t)__builtin_amdgcn_readfirstlane(s_info[2]) * ncb;
@@ -380,7 +383,8 @@ mx_tile_kernel(const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx, c
         int carry = 0;
         for (int base = 0; base < E; base += NT) {
             const int ee = base + tid;
-            const int tl = tiles_of(ee);
+            int o0, o1;
+            const int tl = tiles_of(ee, o0, o1);
             scan[tid] = tl;
             __syncthreads();
             for (int off = 1; off < NT; off <<= 1) {
@@ -393,6 +397,8 @@ mx_tile_kernel(const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx, c
             if (ee < E && tile >= excl && tile < incl) {
                 s_info[0] = ee;
                 s_info[1] = tile - excl;
+                s_info[3] = o0;
+                s_info[4] = o1;
             }
             carry += scan[NT - 1];
             __syncthreads();
@@ -400,8 +406,10 @@ mx_tile_kernel(const uint8_t *__restrict__ qx, const uint8_t *__restrict__ sx, c
         }
         n0 = (item % ncb) * BN;
         e = __builtin_amdgcn_readfirstlane(s_info[0]);   // always found: tile < total row tiles
-        row0 = offsets[e] + (int64_t)__builtin_amdgcn_readfirstlane(s_info[1]) * BM;
-        row_end = offsets[e + 1] < M ? offsets[e + 1] : M;   // offsets[E] == R by contract
+        // the expert's offsets as its scan lane read them (no second load)
+        const int64_t oe = __builtin_amdgcn_readfirstlane(s_info[3]), oe1 = __builtin_amdgcn_readfirstlane(s_info[4]);
+        row0 = oe + (int64_t)__builtin_amdgcn_readfirstlane(s_info[1]) * BM;
+        row_end = oe1 < M ? oe1 : M;   // offsets[E] == R by contract
     } else {
         row0 = (int64_t)blockIdx.x * BM;
         row_end = M;

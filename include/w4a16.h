@@ -135,8 +135,9 @@ w4a16_status w4a16_gemm(const void *x, const void *w_packed, const void *scale,
  * int4 weights by int8 matrix-core instructions with int32 accumulation, then
  * merged as ((Y1/7.49 + Y2/(7.49*14.98) + Y3/(7.49*14.98^2)) * A_max) * scale
  * and accumulated over groups in fp32.  A single row (M = 1) runs as one
- * launch that decomposes x itself and uses no workspace; larger M runs the
- * decomposition, the product kernel over K slices and their sum.
+ * launch that decomposes x itself and leaves the workspace untouched (it is
+ * still required, as for any M); larger M runs the decomposition, the
+ * product kernel over K slices and their sum.
  *   x                [M][K] fp16
  *   w_packed         prepacked signed weights (is_signed = 1)
  *   antiquant_scale  [K/128][N] fp16
